@@ -1,0 +1,136 @@
+"""ctypes binding of libdspark.so: the C ABI of include/dspark.h, name for name.
+
+Pointer arguments accept an int (a device address), None (NULL) or any
+object with ``data_ptr()`` (a torch tensor); streams accept an int handle,
+None (the null stream) or an object with ``cuda_stream``.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+DSPARK_F32, DSPARK_BF16 = 0, 1
+DSPARK_SCHED_OFF, DSPARK_SCHED_EARLY_STOP, DSPARK_SCHED_FULL_SEARCH, DSPARK_SCHED_ASYNC_TOPK = range(4)
+STATUS_NAMES = ["DSPARK_OK", "DSPARK_ERR_NULL", "DSPARK_ERR_SHAPE", "DSPARK_ERR_DTYPE",
+                "DSPARK_ERR_VALUE", "DSPARK_ERR_WORKSPACE", "DSPARK_ERR_SPS_TABLE",
+                "DSPARK_ERR_MODE", "DSPARK_ERR_ALIGN", "DSPARK_ERR_HIP"]
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{where}: {name} ({dspark_status_string(status)})")
+
+
+_lib = None
+_vp, _sz, _i, _f, _u64 = C.c_void_p, C.c_size_t, C.c_int, C.c_float, C.c_uint64
+
+
+def library():
+    """Load libdspark.so.  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m draft_sampling_verification_03_amd.build` "
+                              "(there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        L.dspark_status_string.argtypes = [_i]
+        L.dspark_status_string.restype = C.c_char_p
+        L.dspark_draft_workspace.argtypes = [_i, _i, _i, _i, _i]
+        L.dspark_draft_workspace.restype = _sz
+        L.dspark_draft.argtypes = ([_i] * 5 + [_f] + [_vp] * 5 + [_i, _vp, _f, _u64, _u64]
+                                   + [_vp] * 5 + [_sz, _vp])
+        L.dspark_schedule_workspace.argtypes = [_i, _i]
+        L.dspark_schedule_workspace.restype = _sz
+        L.dspark_schedule.argtypes = [_i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 6 + [_sz, _vp]
+        L.dspark_verify_workspace.argtypes = [_i, _i, _i, _i]
+        L.dspark_verify_workspace.restype = _sz
+        L.dspark_verify.argtypes = ([_i] * 5 + [_f, _vp, _vp, _i] + [_vp] * 8 + [_u64, _u64]
+                                    + [_vp] * 4 + [_sz, _vp])
+        L.dspark_tv_overlap_workspace.argtypes = [_i, _i]
+        L.dspark_tv_overlap_workspace.restype = _sz
+        L.dspark_tv_overlap.argtypes = [_i, _i, _i, _f] + [_vp] * 6 + [_sz, _vp]
+        L.dspark_device_error.argtypes = [_vp, _vp, _vp]
+        L.dspark_clear_device_error.argtypes = [_vp, _vp]
+        for name in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_tv_overlap",
+                     "dspark_device_error", "dspark_clear_device_error"):
+            getattr(L, name).restype = _i
+        _lib = L
+    return _lib
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dspark_status_string(status):
+    return library().dspark_status_string(int(status)).decode()
+
+
+def dspark_draft_workspace(R, gamma, V, r, dt):
+    return library().dspark_draft_workspace(R, gamma, V, r, dt)
+
+
+def dspark_draft(R, gamma, V, r, dt, temp, U, W1, W2, x0, h, d, w_conf, b_conf, seed, round_,
+                 x, q_stats, q_x, c, ws, ws_bytes, stream):
+    return library().dspark_draft(R, gamma, V, r, dt, temp, _p(U), _p(W1), _p(W2), _p(x0), _p(h),
+                                  d, _p(w_conf), b_conf, seed, round_, _p(x), _p(q_stats), _p(q_x),
+                                  _p(c), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_schedule_workspace(R, gamma):
+    return library().dspark_schedule_workspace(R, gamma)
+
+
+def dspark_schedule(R, gamma, mode, c, c_prev2, SPS, B_max, ell, row_offset, a, n_admitted, theta,
+                    ws, ws_bytes, stream):
+    return library().dspark_schedule(R, gamma, mode, _p(c), _p(c_prev2), _p(SPS), B_max, _p(ell),
+                                     _p(row_offset), _p(a), _p(n_admitted), _p(theta), _p(ws),
+                                     ws_bytes, _s(stream))
+
+
+def dspark_verify_workspace(R, gamma, V, rows_capacity):
+    return library().dspark_verify_workspace(R, gamma, V, rows_capacity)
+
+
+def dspark_verify(R, gamma, V, r, dt, temp, ell, row_offset, rows_capacity, P, U, W1, W2, x0, x,
+                  q_stats, q_x, seed, round_, n_acc, y, c_star, ws, ws_bytes, stream):
+    return library().dspark_verify(R, gamma, V, r, dt, temp, _p(ell), _p(row_offset),
+                                   rows_capacity, _p(P), _p(U), _p(W1), _p(W2), _p(x0), _p(x),
+                                   _p(q_stats), _p(q_x), seed, round_, _p(n_acc), _p(y),
+                                   _p(c_star), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_tv_overlap_workspace(n_rows, V):
+    return library().dspark_tv_overlap_workspace(n_rows, V)
+
+
+def dspark_tv_overlap(n_rows, V, dt, temp, P, Q, p_stats, q_stats, c_star, ws, ws_bytes, stream):
+    return library().dspark_tv_overlap(n_rows, V, dt, temp, _p(P), _p(Q), _p(p_stats),
+                                       _p(q_stats), _p(c_star), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_device_error(ws, stream):
+    """Returns (status, code)."""
+    code = C.c_int32(0)
+    st = library().dspark_device_error(_p(ws), C.addressof(code), _s(stream))
+    return st, code.value
+
+
+def dspark_clear_device_error(ws, stream):
+    return library().dspark_clear_device_error(_p(ws), _s(stream))

@@ -1,0 +1,127 @@
+"""torch-facing wrappers over the C ABI: allocate outputs and workspaces with
+torch (device memory and streams only) and call the dspark_* entry points.
+No arithmetic of the method happens here."""
+import torch
+
+from . import _abi as A
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return A.DSPARK_BF16
+    if t.dtype == torch.float32:
+        return A.DSPARK_F32
+    raise TypeError(f"logits and weights must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(status, where):
+    if status != 0:
+        raise A.DSparkError(status, where)
+
+
+def _stream(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+class Workspace:
+    """Device scratch for one entry point, zeroed once at allocation (the sticky
+    error word lives in its first 256 bytes); grows on demand."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def error_code(self, stream=None):
+        st, code = A.dspark_device_error(self.buf, _stream(stream))
+        _check(st, "dspark_device_error")
+        return code
+
+    def clear_error(self, stream=None):
+        _check(A.dspark_clear_device_error(self.buf, _stream(stream)), "dspark_clear_device_error")
+
+
+def draft(U, W1, W2, x0, *, temp=1.0, seed=0, round=0, h=None, w_conf=None, b_conf=0.0,
+          ws=None, stream=None, out=None):
+    """U [R][gamma][V], W1 [V][r], W2 column-major ([V][r] storage), x0 [R] int32."""
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dt = _dt(U)
+    dev = U.device
+    if out is None:
+        out = dict(x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+                   q_stats=torch.empty((R, gamma, 2), dtype=torch.float32, device=dev),
+                   q_x=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   c=torch.empty((R, gamma), dtype=torch.float32, device=dev) if h is not None else None)
+    ws = ws or Workspace(dev)
+    nbytes = A.dspark_draft_workspace(R, gamma, V, r, dt)
+    buf = ws.get(nbytes)
+    d = 0 if h is None else h.shape[-1]
+    st = A.dspark_draft(R, gamma, V, r, dt, float(temp), U, W1, W2, x0, h, d, w_conf, float(b_conf),
+                        int(seed), int(round), out["x"], out["q_stats"], out["q_x"], out["c"], buf,
+                        buf.numel(), _stream(stream))
+    _check(st, "dspark_draft")
+    return out
+
+
+def schedule(c, SPS, mode, *, c_prev2=None, R=None, gamma=None, ws=None, stream=None, out=None,
+             want_a=True):
+    """c [R][gamma] fp32 (None in OFF mode with R, gamma given); SPS fp64 table."""
+    if c is not None:
+        R, gamma = c.shape
+        dev = c.device
+    else:
+        dev = SPS.device if SPS is not None else torch.device("cuda")
+    if out is None:
+        out = dict(ell=torch.empty(R, dtype=torch.int32, device=dev),
+                   row_offset=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                   a=torch.empty((R, gamma), dtype=torch.float32, device=dev)
+                   if (c is not None and want_a) else None,
+                   n_admitted=torch.empty(1, dtype=torch.int32, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(A.dspark_schedule_workspace(R, gamma))
+    B_max = 0 if SPS is None else SPS.numel() - 1
+    st = A.dspark_schedule(R, gamma, int(mode), c, c_prev2, SPS, B_max, out["ell"],
+                           out["row_offset"], out["a"], out["n_admitted"], out["theta"], buf,
+                           buf.numel(), _stream(stream))
+    _check(st, "dspark_schedule")
+    return out
+
+
+def verify(ell, row_offset, P, U, W1, W2, x0, x, q_stats, q_x, *, rows_capacity=None, temp=1.0,
+           seed=0, round=0, ws=None, stream=None, out=None):
+    """P [rows_capacity][V] flattened target rows; other inputs as for draft."""
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dt = _dt(U)
+    dev = U.device
+    rows_capacity = P.shape[0] if rows_capacity is None else rows_capacity
+    if out is None:
+        out = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                   y=torch.empty((R, gamma + 1), dtype=torch.int32, device=dev),
+                   c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(A.dspark_verify_workspace(R, gamma, V, rows_capacity))
+    st = A.dspark_verify(R, gamma, V, r, dt, float(temp), ell, row_offset, rows_capacity, P, U, W1,
+                         W2, x0, x, q_stats, q_x, int(seed), int(round), out["n_acc"], out["y"],
+                         out["c_star"], buf, buf.numel(), _stream(stream))
+    _check(st, "dspark_verify")
+    return out
+
+
+def tv_overlap(P, Q, *, p_stats=None, q_stats=None, temp=1.0, ws=None, stream=None, out=None):
+    n_rows, V = P.shape
+    dt = _dt(P)
+    if out is None:
+        out = torch.empty(n_rows, dtype=torch.float32, device=P.device)
+    ws = ws or Workspace(P.device)
+    buf = ws.get(A.dspark_tv_overlap_workspace(n_rows, V))
+    st = A.dspark_tv_overlap(n_rows, V, dt, float(temp), P, Q, p_stats, q_stats, out, buf,
+                             buf.numel(), _stream(stream))
+    _check(st, "dspark_tv_overlap")
+    return out

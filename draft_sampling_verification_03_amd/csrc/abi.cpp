@@ -1,0 +1,191 @@
+// Host side of the C ABI declared in include/dspark.h: argument validation
+// (which touches no GPU, so it runs and is tested on any host), workspace
+// carving, and kernel launches on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/dspark.h"
+#include "kernels.h"
+
+using namespace dspark;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool bad_temp(float t) { return !(t > 0.0f) || !isfinite(t); }
+
+dspark_status check_common(int R, int gamma, int V, int r, dspark_dtype dt, float temp) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (R < 1 || gamma < 1 || gamma > 64) return DSPARK_ERR_SHAPE;
+  if (V < 8 || V > 262144 || V % 8 != 0) return DSPARK_ERR_SHAPE;
+  if (r < 16 || r % 16 != 0 || r > (dt == DSPARK_F32 ? 128 : 256)) return DSPARK_ERR_SHAPE;
+  if (bad_temp(temp)) return DSPARK_ERR_VALUE;
+  return DSPARK_OK;
+}
+
+dspark_status from_hip(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+char *carve(void *ws, size_t *off, size_t bytes) {
+  char *p = (char *)ws + *off;
+  *off += ws_align(bytes);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "a size is outside the supported limits";
+    case DSPARK_ERR_DTYPE: return "unknown element type";
+    case DSPARK_ERR_VALUE: return "invalid scalar argument (temperature must be finite and > 0)";
+    case DSPARK_ERR_WORKSPACE: return "workspace smaller than the *_workspace() size";
+    case DSPARK_ERR_SPS_TABLE: return "SPS table missing or shorter than R*(1+gamma)+1";
+    case DSPARK_ERR_MODE: return "unknown scheduler mode or missing confidences";
+    case DSPARK_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case DSPARK_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t dspark_draft_workspace(int R, int gamma, int V, int r, dspark_dtype dt) {
+  (void)r; (void)dt;
+  if (R < 1 || gamma < 1 || V < 1) return 0;
+  return draft_ws_bytes(R, gamma, V);
+}
+
+dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                           const void *U, const void *W1, const void *W2, const int32_t *x0,
+                           const void *h, int d, const float *w_conf, float b_conf,
+                           uint64_t seed, uint64_t round, int32_t *x, float *q_stats, float *q_x,
+                           float *c, void *ws, size_t ws_bytes, hipStream_t stream) {
+  dspark_status s = check_common(R, gamma, V, r, dt, temp);
+  if (s != DSPARK_OK) return s;
+  if (!U || !W1 || !W2 || !x0 || !x || !q_stats || !q_x || !ws) return DSPARK_ERR_NULL;
+  if (h != nullptr) {
+    if (!w_conf || !c) return DSPARK_ERR_NULL;
+    if (d < 8 || d > 65536 || d % 8 != 0) return DSPARK_ERR_SHAPE;
+    if (!isfinite(b_conf)) return DSPARK_ERR_VALUE;
+    if (!aligned16(h)) return DSPARK_ERR_ALIGN;
+  }
+  if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(ws)) return DSPARK_ERR_ALIGN;
+  if (ws_bytes < draft_ws_bytes(R, gamma, V)) return DSPARK_ERR_WORKSPACE;
+  size_t off = 0;
+  DraftLaunch L{};
+  L.err = (int32_t *)carve(ws, &off, kWsHeader);
+  L.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
+  L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
+  L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
+  L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
+  L.b_conf = b_conf; L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
+  L.c = c;
+  return from_hip(launch_draft(L, stream));
+}
+
+size_t dspark_schedule_workspace(int R, int gamma) {
+  if (R < 1 || gamma < 1) return 0;
+  return schedule_ws_bytes(R, gamma);
+}
+
+dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode, const float *c,
+                              const float *c_prev2, const double *SPS, int B_max, int32_t *ell,
+                              int32_t *row_offset, float *a, int32_t *n_admitted, double *theta,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (R < 1 || gamma < 1 || gamma > 64 || (int64_t)R * gamma > 8192) return DSPARK_ERR_SHAPE;
+  if ((int)mode < 0 || (int)mode > 3) return DSPARK_ERR_MODE;
+  if (!ell || !row_offset || !n_admitted || !theta || !ws) return DSPARK_ERR_NULL;
+  if (mode != DSPARK_SCHED_OFF && !c) return DSPARK_ERR_MODE;
+  if (mode == DSPARK_SCHED_ASYNC_TOPK && !c_prev2) return DSPARK_ERR_MODE;
+  const bool need_sps = mode != DSPARK_SCHED_OFF || (c != nullptr && SPS != nullptr);
+  if (mode != DSPARK_SCHED_OFF && !SPS) return DSPARK_ERR_SPS_TABLE;
+  if (need_sps && (int64_t)B_max < (int64_t)R * (1 + gamma)) return DSPARK_ERR_SPS_TABLE;
+  if (!aligned16(ws)) return DSPARK_ERR_ALIGN;
+  if (ws_bytes < schedule_ws_bytes(R, gamma)) return DSPARK_ERR_WORKSPACE;
+  ScheduleLaunch L{};
+  L.R = R; L.gamma = gamma; L.mode = (int)mode; L.c = c;
+  L.c_prev2 = mode == DSPARK_SCHED_ASYNC_TOPK ? c_prev2 : nullptr;
+  L.SPS = need_sps ? SPS : nullptr; L.ell = ell; L.row_offset = row_offset;
+  L.a = c ? a : nullptr; L.n_admitted = n_admitted; L.theta = theta; L.err = (int32_t *)ws;
+  return from_hip(launch_schedule(L, stream));
+}
+
+size_t dspark_verify_workspace(int R, int gamma, int V, int rows_capacity) {
+  if (R < 1 || gamma < 1 || V < 1 || rows_capacity < 1) return 0;
+  return verify_ws_bytes(R, gamma, V, rows_capacity);
+}
+
+dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                            const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                            const void *P, const void *U, const void *W1, const void *W2,
+                            const int32_t *x0, const int32_t *x, const float *q_stats,
+                            const float *q_x, uint64_t seed, uint64_t round, int32_t *n_acc,
+                            int32_t *y, float *c_star, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  dspark_status s = check_common(R, gamma, V, r, dt, temp);
+  if (s != DSPARK_OK) return s;
+  if ((int64_t)rows_capacity < R || (int64_t)rows_capacity > (int64_t)R * (1 + gamma))
+    return DSPARK_ERR_SHAPE;
+  if (!ell || !row_offset || !P || !U || !W1 || !W2 || !x0 || !x || !q_stats || !q_x || !n_acc ||
+      !y || !c_star || !ws)
+    return DSPARK_ERR_NULL;
+  if (!aligned16(P) || !aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(ws))
+    return DSPARK_ERR_ALIGN;
+  if (ws_bytes < verify_ws_bytes(R, gamma, V, rows_capacity)) return DSPARK_ERR_WORKSPACE;
+  size_t off = 0;
+  VerifyLaunch L{};
+  L.err = (int32_t *)carve(ws, &off, kWsHeader);
+  L.p_chunks = (float2 *)carve(ws, &off, (size_t)rows_capacity * 4 * 8);
+  L.bonus_tiles = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
+  L.pair_partials = (float2 *)carve(ws, &off, (size_t)R * gamma * n_tiles_of(V) * 8);
+  L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.rows_capacity = rows_capacity;
+  L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp; L.ell = ell; L.row_offset = row_offset;
+  L.P = P; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
+  L.seed = seed; L.round = round; L.n_acc = n_acc; L.y = y; L.c_star = c_star;
+  return from_hip(launch_verify(L, stream));
+}
+
+size_t dspark_tv_overlap_workspace(int n_rows, int V) {
+  if (n_rows < 1 || V < 1) return 0;
+  return overlap_ws_bytes(n_rows, V);
+}
+
+dspark_status dspark_tv_overlap(int n_rows, int V, dspark_dtype dt, float temp, const void *P,
+                                const void *Q, const float *p_stats, const float *q_stats,
+                                float *c_star, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (n_rows < 1 || V < 8 || V > 262144 || V % 8 != 0) return DSPARK_ERR_SHAPE;
+  if (bad_temp(temp)) return DSPARK_ERR_VALUE;
+  if (!P || !Q || !c_star || !ws) return DSPARK_ERR_NULL;
+  if ((p_stats == nullptr) != (q_stats == nullptr)) return DSPARK_ERR_NULL;
+  if (!aligned16(P) || !aligned16(Q) || !aligned16(ws)) return DSPARK_ERR_ALIGN;
+  if (ws_bytes < overlap_ws_bytes(n_rows, V)) return DSPARK_ERR_WORKSPACE;
+  size_t off = 0;
+  OverlapLaunch L{};
+  L.err = (int32_t *)carve(ws, &off, kWsHeader);
+  L.p_chunks = (float2 *)carve(ws, &off, (size_t)n_rows * 4 * 8);
+  L.q_chunks = (float2 *)carve(ws, &off, (size_t)n_rows * 4 * 8);
+  L.partial = (float *)carve(ws, &off, (size_t)n_rows * 4 * 4);
+  L.n_rows = n_rows; L.V = V; L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp; L.P = P; L.Q = Q;
+  L.p_stats = p_stats; L.q_stats = q_stats; L.c_star = c_star;
+  return from_hip(launch_overlap(L, stream));
+}
+
+dspark_status dspark_device_error(const void *ws, int32_t *code, hipStream_t stream) {
+  if (!ws || !code) return DSPARK_ERR_NULL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return DSPARK_ERR_HIP;
+  if (hipMemcpy(code, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return DSPARK_ERR_HIP;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_clear_device_error(void *ws, hipStream_t stream) {
+  if (!ws) return DSPARK_ERR_NULL;
+  if (!aligned16(ws)) return DSPARK_ERR_ALIGN;
+  return from_hip(launch_clear_error((int32_t *)ws, stream));
+}
+
+}  // extern "C"

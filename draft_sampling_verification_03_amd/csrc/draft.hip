@@ -1,0 +1,216 @@
+// Markov-head drafting (Blog, "Markov sequential head"; Bangkok 4.1; KB
+// section 2): gamma serial steps, each = one fused bias-tile launch (partials
+// of z_k per vocabulary tile) + one sampling launch (one workgroup per request).
+//
+// Sampling is an inverse CDF in two levels.  The workgroup of request rho
+// rescales its tile partials to the row maximum, scans them to find the tile
+// whose cumulative mass first exceeds u * S, recomputes z for that tile alone
+// (bit-identical to the fused kernel), and scans inside the tile.  Only the
+// 128-column tile is re-read, never the row.
+#include "bias_tile.h"
+#include "kernels.h"
+
+namespace dspark {
+
+struct SampleParams {
+  int R, gamma, V, r, n_tiles, k;
+  float invT;
+  const void *U, *W1, *W2;
+  const int32_t *x0;
+  int32_t *x;
+  float *q_stats, *q_x;
+  const float2 *tile_stats;  // [R][n_tiles]
+  uint64_t seed, round;
+  // confidence head (Bangkok 4.2.1): c_k = sigmoid(sh[rho][k] + w_e . W1[x_{k-1}] + b)
+  const float *sh;           // [R][gamma] = w_h . h_k, or NULL
+  const float *w_e;          // [r] (the last r weights of w_conf)
+  float b_conf;
+  float *c;
+  int32_t *err;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
+  __shared__ float wbuf[kMaxTiles];
+  __shared__ float zbuf[kTileN];
+  __shared__ __align__(16) T arow[kMaxRank + 16];
+  __shared__ float fred[8];
+  __shared__ int ired[8];
+  __shared__ float s_before;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rho = blockIdx.x, k = p.k, V = p.V, r = p.r, nT = p.n_tiles;
+  const int64_t slot = (int64_t)rho * p.gamma + (k - 1);
+
+  int prev = k == 1 ? p.x0[rho] : p.x[slot - 1];
+  if (prev < 0 || prev >= V) {
+    if (tid == 0) flag_error(p.err, kErrToken);
+    prev = prev < 0 ? 0 : V - 1;
+  }
+
+  // 1. row maximum and tile masses w_t = s_t * exp(m_t - m), scanned in tile order
+  const float2 *part = p.tile_stats + (int64_t)rho * nT;
+  const int cpt = (nT + kBlock - 1) / kBlock;
+  const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
+  float lm = -INFINITY;
+  for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[t].x);
+  const float m = block_max(lm, fred);
+  float ls = 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    const float w = part[t].y * fexp(part[t].x - m);
+    wbuf[t] = w;
+    ls += w;
+  }
+  float S;
+  const float base = block_exclusive_scan(ls, fred, &S);
+  const bool finite = isfinite(m) && isfinite(S) && S > 0.0f;
+
+  // 2. the tile holding the draw
+  const float u = uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamDraft);
+  const float target = u * S;
+  int found = 0x7fffffff;
+  {
+    float run = base;
+    for (int t = t0; t < t1; ++t) {
+      const float nx = run + wbuf[t];
+      if (found == 0x7fffffff && target < nx && wbuf[t] > 0.0f) found = t;
+      run = nx;
+    }
+  }
+  int tstar = block_min_int(found, ired);
+  if (tstar == 0x7fffffff) {  // rounding left no crossing: last tile with mass
+    int lastpos = -1;
+    for (int t = t0; t < t1; ++t)
+      if (wbuf[t] > 0.0f) lastpos = t;
+    tstar = block_max_int(lastpos, ired);
+  }
+  if (tstar < 0 || !finite) {
+    if (tid == 0) flag_error(p.err, kErrNonFinite);
+    tstar = 0;
+  }
+  if (tid == 0) s_before = 0.0f;
+  __syncthreads();
+  if (t0 <= tstar && tstar < t1) {
+    float run = base;
+    for (int t = t0; t < tstar; ++t) run += wbuf[t];
+    s_before = run;
+  }
+
+  // 3. recompute z of that tile, bit-identical to the fused kernel
+  {
+    const T *W1 = reinterpret_cast<const T *>(p.W1);
+    const int pieces = r * (int)sizeof(T) / 16;
+    if (tid < pieces)
+      *reinterpret_cast<uint4 *>(arow + tid * (16 / sizeof(T))) =
+          *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * r + tid * (16 / sizeof(T)));
+  }
+  __syncthreads();
+  const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
+  recompute_tile_z<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
+                      p.invT, zbuf);
+  __syncthreads();
+
+  // 4. scan inside the tile (wave 0, two columns per lane, left to right)
+  if (wave == 0) {
+    const float mt = part[tstar].x;
+    const float scale = fexp(mt - m);
+    const float e0 = fexp(zbuf[2 * lane] - mt), e1 = fexp(zbuf[2 * lane + 1] - mt);
+    const float inc = wave_inclusive_scan(e0 + e1);
+    float exc = __shfl_up(inc, 1);
+    if (lane == 0) exc = 0.0f;
+    const float cdf0 = s_before + scale * (exc + e0);
+    const float cdf1 = s_before + scale * ((exc + e0) + e1);
+    int pick = 0x7fffffff;
+    if (target < cdf0 && e0 > 0.0f) pick = 2 * lane;
+    else if (target < cdf1 && e1 > 0.0f) pick = 2 * lane + 1;
+    pick = wave_min_int(pick);
+    if (pick == 0x7fffffff) {
+      int lp = -1;
+      if (e0 > 0.0f) lp = 2 * lane;
+      if (e1 > 0.0f) lp = 2 * lane + 1;
+      pick = wave_max_int(lp);
+      if (pick < 0) pick = 0;
+    }
+    if (lane == 0) {
+      const int xk = tstar * kTileN + pick;
+      p.x[slot] = finite ? xk : -1;
+      p.q_stats[2 * slot] = m;
+      p.q_stats[2 * slot + 1] = S;
+      p.q_x[slot] = fexp(zbuf[pick] - m) / S;
+    }
+  }
+
+  // 5. confidence head on [h_k ; W1[x_{k-1}]] (wave 1)
+  if (p.sh != nullptr && wave == 1) {
+    float acc = 0.0f;
+    for (int i = lane; i < r; i += kWave) acc = fmaf(p.w_e[i], Elem<T>::at(arow, i), acc);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const float s = p.sh[slot] + acc + p.b_conf;
+      p.c[slot] = 1.0f / (1.0f + expf(-s));
+    }
+  }
+}
+
+// sh[rho][k] = sum_j w[j] h[rho][k][j]: one wave per (rho, k), 16-byte loads.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, int d,
+                                                                 const T *h, const float *w,
+                                                                 float *sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t slot = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (slot >= n_slots) return;
+  constexpr int kPer = Elem<T>::kPerVec;
+  const T *row = h + slot * d;
+  float acc = 0.0f;
+  for (int j = lane * kPer; j < d; j += kWave * kPer) {
+    float hv[kPer];
+    Elem<T>::vec(row, j, hv);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) acc = fmaf(w[j + q], hv[q], acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) sh[slot] = acc;
+}
+
+template <typename T, int TM>
+static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
+  const int n_tiles = (L.V + kTileN - 1) / kTileN;
+  BiasTileParams bp{};
+  bp.R = L.R; bp.gamma = L.gamma; bp.V = L.V; bp.r = L.r; bp.n_tiles = n_tiles;
+  bp.invT = L.invT; bp.U = L.U; bp.W1 = L.W1; bp.W2 = L.W2; bp.x0 = L.x0; bp.x = L.x;
+  bp.err = L.err; bp.tile_stats = L.tile_stats;
+  SampleParams sp{};
+  sp.R = L.R; sp.gamma = L.gamma; sp.V = L.V; sp.r = L.r; sp.n_tiles = n_tiles;
+  sp.invT = L.invT; sp.U = L.U; sp.W1 = L.W1; sp.W2 = L.W2; sp.x0 = L.x0; sp.x = L.x;
+  sp.q_stats = L.q_stats; sp.q_x = L.q_x; sp.tile_stats = L.tile_stats;
+  sp.seed = L.seed; sp.round = L.round; sp.err = L.err;
+  if (L.h != nullptr) {
+    const int n_slots = L.R * L.gamma;
+    head_hidden_dot_kernel<T><<<(n_slots + 3) / 4, kBlock, 0, stream>>>(
+        n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh);
+    sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
+  }
+  const dim3 grid((L.R + TM - 1) / TM, n_tiles);
+  for (int k = 1; k <= L.gamma; ++k) {
+    bp.k = k;
+    sp.k = k;
+    bias_tile_kernel<T, TM, Epi::kDraft><<<grid, kBlock, 0, stream>>>(bp);
+    draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream) {
+  const int tm = tile_rows_for(L.R);
+  if (L.bf16) {
+    if (tm == 128) return launch_draft_t<bf16_t, 128>(L, stream);
+    if (tm == 64) return launch_draft_t<bf16_t, 64>(L, stream);
+    return launch_draft_t<bf16_t, 32>(L, stream);
+  }
+  if (tm == 128) return launch_draft_t<float, 128>(L, stream);
+  if (tm == 64) return launch_draft_t<float, 64>(L, stream);
+  return launch_draft_t<float, 32>(L, stream);
+}
+
+}  // namespace dspark

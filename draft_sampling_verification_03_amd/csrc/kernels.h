@@ -1,0 +1,101 @@
+// Launch descriptors shared by the host-side ABI layer (abi.cpp) and the
+// kernel translation units.  Plain structs of device pointers and sizes; the
+// ABI layer has validated every field before a launch function is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// rows per bias tile for an M-row product
+inline int tile_rows_for(int M) { return M >= 96 ? 128 : (M > 32 ? 64 : 32); }
+
+constexpr size_t kWsHeader = 256;  // sticky error word lives at the start of every workspace
+
+struct DraftLaunch {
+  int R, gamma, V, r, d;
+  bool bf16;
+  float invT;
+  const void *U, *W1, *W2;
+  const int32_t *x0;
+  const void *h;
+  const float *w_conf;
+  float b_conf;
+  uint64_t seed, round;
+  int32_t *x;
+  float *q_stats, *q_x, *c;
+  // workspace pieces
+  int32_t *err;
+  float2 *tile_stats;  // [R][n_tiles]
+  float *sh;           // [R][gamma]
+};
+
+struct ScheduleLaunch {
+  int R, gamma, mode;
+  const float *c, *c_prev2;
+  const double *SPS;
+  int32_t *ell, *row_offset;
+  float *a;
+  int32_t *n_admitted;
+  double *theta;
+  int32_t *err;
+};
+
+struct VerifyLaunch {
+  int R, gamma, V, r, rows_capacity;
+  bool bf16;
+  float invT;
+  const int32_t *ell, *row_offset;
+  const void *P, *U, *W1, *W2;
+  const int32_t *x0, *x;
+  const float *q_stats, *q_x;
+  uint64_t seed, round;
+  int32_t *n_acc, *y;
+  float *c_star;
+  // workspace pieces
+  int32_t *err;
+  float2 *p_chunks;      // [rows_capacity][4]
+  float2 *bonus_tiles;   // [R][n_tiles]
+  float2 *pair_partials; // [R * gamma][n_tiles]
+};
+
+struct OverlapLaunch {
+  int n_rows, V;
+  bool bf16;
+  float invT;
+  const void *P, *Q;
+  const float *p_stats, *q_stats;
+  float *c_star;
+  int32_t *err;
+  float2 *p_chunks, *q_chunks;  // [n_rows][4] each
+  float *partial;               // [n_rows][4]
+};
+
+hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream);
+hipError_t launch_schedule(const ScheduleLaunch &L, hipStream_t stream);
+hipError_t launch_verify(const VerifyLaunch &L, hipStream_t stream);
+hipError_t launch_overlap(const OverlapLaunch &L, hipStream_t stream);
+hipError_t launch_clear_error(int32_t *err, hipStream_t stream);
+
+// workspace layouts (bytes), each piece 256-byte aligned
+inline size_t ws_align(size_t b) { return (b + 255) & ~(size_t)255; }
+inline int n_tiles_of(int V) { return (V + 127) / 128; }
+
+inline size_t draft_ws_bytes(int R, int gamma, int V) {
+  return kWsHeader + ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4);
+}
+inline size_t schedule_ws_bytes(int R, int gamma) {
+  (void)R; (void)gamma;
+  return kWsHeader;
+}
+inline size_t verify_ws_bytes(int R, int gamma, int V, int rows_capacity) {
+  return kWsHeader + ws_align((size_t)rows_capacity * 4 * 8) +
+         ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * n_tiles_of(V) * 8);
+}
+inline size_t overlap_ws_bytes(int n_rows, int V) {
+  (void)V;
+  return kWsHeader + 2 * ws_align((size_t)n_rows * 4 * 8) + ws_align((size_t)n_rows * 4 * 4);
+}
+
+}  // namespace dspark

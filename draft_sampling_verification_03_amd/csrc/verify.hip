@@ -1,0 +1,513 @@
+// Exact speculative-sampling verification of the flattened ragged batch
+// (Blog, "One-token exactness", "Why only the longest accepted prefix
+// survives", "Variable-length verification without wasting kernels"; KB
+// sections 7-8).  Three launches:
+//
+//  1. row_chunk_stats_kernel: one HBM pass over the sum(1 + ell) target rows,
+//     (max, sum exp) per quarter row; the last row of every request (its bonus
+//     position) also keeps per-tile partials for sampling.
+//  2. bias_tile_kernel<Verify>: recompute z_k of every verified draft with the
+//     draft's arithmetic, stream U_k and P_k once, emit per-tile
+//     (sum min(p, q), sum (p - q)_+).
+//  3. verify_finalize_kernel: one workgroup per request: c*_k, the accept
+//     tests in order, the first rejection, and the residual or bonus draw by
+//     a two-level inverse CDF.
+#include "bias_tile.h"
+#include "kernels.h"
+
+namespace dspark {
+
+struct RowStatsParams {
+  int n_rows, V, n_tiles;
+  float invT;
+  const void *X;              // [n_rows][V]
+  const int32_t *row_offset;  // verify: rows >= row_offset[R] are unused; else NULL
+  int R;
+  float2 *chunks;             // [n_rows][kChunks]
+  float2 *bonus_tiles;        // [R][n_tiles], verify only
+  int32_t *err;
+};
+
+__device__ __forceinline__ void online_merge(float &M, float &S, float m, float s) {
+  if (m > M) {
+    S = S * fexp(M - m) + s;
+    M = m;
+  } else if (m != -INFINITY) {
+    S += s * fexp(m - M);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams p) {
+  __shared__ float red[8];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int V = p.V, nT = p.n_tiles;
+  int rho = -1;
+  if (p.row_offset != nullptr) {
+    int used = p.row_offset[p.R];
+    if (used > p.n_rows) {
+      if (row == 0 && c == 0 && tid == 0) flag_error(p.err, kErrLength);
+      used = p.n_rows;
+    }
+    if (row >= used) return;
+    if (p.bonus_tiles != nullptr) {  // is this the last row of its request?
+      int lo = 0, hi = p.R;          // last rho with row_offset[rho] <= row
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
+      }
+      if (p.row_offset[lo + 1] - 1 == row) rho = lo;
+    }
+  }
+  const int tpc = (nT + kChunks - 1) / kChunks;
+  const int tb = min(c * tpc, nT), te = min(tb + tpc, nT);
+  const int vb = tb * kTileN, ve = min(te * kTileN, V);
+  const T *X = reinterpret_cast<const T *>(p.X) + (int64_t)row * V;
+  constexpr int kPer = Elem<T>::kPerVec;
+  float M = -INFINITY, S = 0.0f;
+
+  if (rho < 0) {
+    // online statistics, four 16-byte loads in flight per thread
+    constexpr int kUnroll = 4;
+    for (int v0 = vb + tid * kPer; v0 < ve; v0 += kBlock * kPer * kUnroll) {
+      float x[kUnroll][kPer];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * kBlock * kPer;
+        if (v < ve) {
+          Elem<T>::vec(X, v, x[u]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) x[u][q] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          if (x[u][q] != -INFINITY) x[u][q] *= p.invT;
+          lm = fmaxf(lm, x[u][q]);
+        }
+        if (lm == -INFINITY) continue;
+        if (lm > M) {
+          S = S * fexp(M - lm);
+          M = lm;
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) S += fexp(x[u][q] - M);
+      }
+    }
+  } else {
+    // per-tile partials (kept for the bonus draw), merged into the chunk
+    constexpr int kG = kTileN / kPer;              // threads per tile
+    constexpr int kTilesPerIt = kBlock / kG;
+    for (int t0 = tb; t0 < te; t0 += kTilesPerIt) {
+      const int t = t0 + tid / kG;
+      const int v = t * kTileN + (tid % kG) * kPer;
+      float x[kPer];
+      if (t < te && v < V) {
+        Elem<T>::vec(X, v, x);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) x[q] *= p.invT;
+      } else {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) x[q] = -INFINITY;
+      }
+      float lm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) lm = fmaxf(lm, x[q]);
+      const float mt = group_max<kG>(lm);
+      float ls = 0.0f;
+      if (mt != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) ls += fexp(x[q] - mt);
+      }
+      const float st = group_sum<kG>(ls);
+      if (t < te && (tid % kG) == 0) {
+        p.bonus_tiles[(int64_t)rho * nT + t] = make_float2(mt, st);
+        online_merge(M, S, mt, st);
+      }
+    }
+  }
+  const float m = block_max(M, red);
+  const float s = block_sum(M == -INFINITY ? 0.0f : S * fexp(M - m), red);
+  if (tid == 0) {
+    p.chunks[(int64_t)row * kChunks + c] = make_float2(m, s);
+    if (vb < ve && !(isfinite(m) && isfinite(s))) flag_error(p.err, kErrNonFinite);
+  }
+}
+
+// ------------------------------------------------------------------ finalize
+struct FinalizeParams {
+  int R, gamma, V, r, n_tiles, rows_capacity;
+  float invT;
+  const int32_t *ell, *row_offset;
+  const void *P, *U, *W1, *W2;
+  const int32_t *x0, *x;
+  const float *q_stats, *q_x;
+  uint64_t seed, round;
+  const float2 *p_chunks, *bonus_tiles, *pair_partials;
+  int32_t *n_acc, *y;
+  float *c_star;
+  int32_t *err;
+};
+
+// Two-level inverse CDF over tile masses already in wbuf[0..nT): returns the
+// tile holding u * total and writes the mass before it to *before.
+__device__ int pick_tile(const float *wbuf, int nT, float u, float *fred, int *ired,
+                         float *s_before, float *total_out, float *target_out) {
+  const int tid = threadIdx.x;
+  const int cpt = (nT + kBlock - 1) / kBlock;
+  const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
+  float ls = 0.0f;
+  for (int t = t0; t < t1; ++t) ls += wbuf[t];
+  float total;
+  const float base = block_exclusive_scan(ls, fred, &total);
+  const float target = u * total;
+  int found = 0x7fffffff;
+  float run = base;
+  for (int t = t0; t < t1; ++t) {
+    const float nx = run + wbuf[t];
+    if (found == 0x7fffffff && target < nx && wbuf[t] > 0.0f) found = t;
+    run = nx;
+  }
+  int tstar = block_min_int(found, ired);
+  if (tstar == 0x7fffffff) {
+    int lastpos = -1;
+    for (int t = t0; t < t1; ++t)
+      if (wbuf[t] > 0.0f) lastpos = t;
+    tstar = block_max_int(lastpos, ired);
+  }
+  if (tstar < 0) tstar = 0;
+  if (tid == 0) *s_before = 0.0f;
+  __syncthreads();
+  if (t0 <= tstar && tstar < t1) {
+    float b = base;
+    for (int t = t0; t < tstar; ++t) b += wbuf[t];
+    *s_before = b;
+  }
+  __syncthreads();
+  *total_out = total;
+  *target_out = target;
+  return tstar;
+}
+
+// In-tile scan of 128 masses ebuf[] (wave 0): first column whose cumulative
+// mass before + scale * prefix exceeds target (positive mass only).
+__device__ int pick_in_tile(const float *ebuf, float before, float scale, float target) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float e0 = ebuf[2 * lane], e1 = ebuf[2 * lane + 1];
+  const float inc = wave_inclusive_scan(e0 + e1);
+  float exc = __shfl_up(inc, 1);
+  if (lane == 0) exc = 0.0f;
+  const float cdf0 = before + scale * (exc + e0);
+  const float cdf1 = before + scale * ((exc + e0) + e1);
+  int pick = 0x7fffffff;
+  if (target < cdf0 && e0 > 0.0f) pick = 2 * lane;
+  else if (target < cdf1 && e1 > 0.0f) pick = 2 * lane + 1;
+  pick = wave_min_int(pick);
+  if (pick == 0x7fffffff) {
+    int lp = -1;
+    if (e0 > 0.0f) lp = 2 * lane;
+    if (e1 > 0.0f) lp = 2 * lane + 1;
+    pick = wave_max_int(lp);
+    if (pick < 0) pick = 0;
+  }
+  return pick;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams p) {
+  __shared__ float wbuf[kMaxTiles];
+  __shared__ float zbuf[kTileN];
+  __shared__ float ebuf[kTileN];
+  __shared__ __align__(16) T arow[kMaxRank + 16];
+  __shared__ float fred[8];
+  __shared__ int ired[8];
+  __shared__ float s_before;
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rho = blockIdx.x, gamma = p.gamma, V = p.V, nT = p.n_tiles;
+  int32_t *yrow = p.y + (int64_t)rho * (gamma + 1);
+  float *crow = p.c_star + (int64_t)rho * gamma;
+
+  // ---- validate this request's slice of the ragged batch
+  const int ell = p.ell[rho];
+  const int base = p.row_offset[rho];
+  if (tid == 0) {
+    const int64_t d_off = (int64_t)base - rho;
+    const bool ok = ell >= 0 && ell <= gamma && base >= 0 &&
+                    p.row_offset[rho + 1] == base + 1 + ell && base + ell < p.rows_capacity &&
+                    p.row_offset[p.R] <= p.rows_capacity && d_off >= 0 &&
+                    d_off + ell <= (int64_t)p.R * gamma;
+    s_bad = ok ? 0 : 1;
+    if (!ok) flag_error(p.err, kErrLength);
+  }
+  __syncthreads();
+  if (s_bad) {
+    for (int i = tid; i <= gamma; i += kBlock) yrow[i] = -1;
+    for (int i = tid; i < gamma; i += kBlock) crow[i] = NAN;
+    if (tid == 0) p.n_acc[rho] = 0;
+    return;
+  }
+  const int64_t d_off = (int64_t)base - rho;  // compact index of (rho, k = 1)
+  const int32_t *xr = p.x + (int64_t)rho * gamma;
+
+  // ---- c*_k = sum over tiles of sum_v min(p, q), fixed order per k
+  for (int k = 1 + wave; k <= gamma; k += kBlock / kWave) {
+    float v = NAN;
+    if (k <= ell) {
+      const float2 *pp = p.pair_partials + (d_off + k - 1) * nT;
+      float acc = 0.0f;
+      for (int t = lane; t < nT; t += kWave) acc += pp[t].x;
+      v = wave_sum(acc);
+    }
+    if (lane == 0) crow[k - 1] = v;
+  }
+
+  // ---- accept tests: u * q(x_k) < p(x_k), first rejection
+  int rej = 0x7fffffff;
+  for (int k = 1 + tid; k <= ell; k += kBlock) {
+    int xk = xr[k - 1];
+    if (xk < 0 || xk >= V) {
+      flag_error(p.err, kErrToken);
+      xk = xk < 0 ? 0 : V - 1;
+    }
+    const int row = base + k - 1;
+    const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)row * kChunks);
+    const float t = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)row * V, xk) * p.invT;
+    const double pk = exp((double)t - (double)ps.x) / (double)ps.y;
+    const double qk = (double)p.q_x[(int64_t)rho * gamma + k - 1];
+    const double u = (double)uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamAccept);
+    if (!(u * qk < pk)) rej = min(rej, k);
+  }
+  rej = block_min_int(rej, ired);
+  const int n = rej == 0x7fffffff ? ell : rej - 1;
+  const int j = n + 1;             // position of the final token
+  const int frow = base + n;       // its target row
+  const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)frow * kChunks);
+  const float uf = uniform01(p.seed, p.round, (uint64_t)j, (uint64_t)rho, kStreamFinal);
+  const T *Prow = reinterpret_cast<const T *>(p.P) + (int64_t)frow * V;
+  int final_token = 0;
+
+  bool residual = n < ell;
+  if (residual) {
+    // residual masses per tile from the verify pass
+    const float2 *pp = p.pair_partials + (d_off + j - 1) * nT;
+    for (int t = tid; t < nT; t += kBlock) wbuf[t] = pp[t].y;
+    __syncthreads();
+    float total, target;
+    const int tstar = pick_tile(wbuf, nT, uf, fred, ired, &s_before, &total, &target);
+    if (total > 0.0f) {
+      int prev = j == 1 ? p.x0[rho] : xr[j - 2];
+      if (prev < 0 || prev >= V) prev = prev < 0 ? 0 : V - 1;
+      const T *W1 = reinterpret_cast<const T *>(p.W1);
+      const int pieces = p.r * (int)sizeof(T) / 16;
+      if (tid < pieces)
+        *reinterpret_cast<uint4 *>(arow + tid * (16 / sizeof(T))) =
+            *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * p.r + tid * (16 / sizeof(T)));
+      __syncthreads();
+      const T *Urow = reinterpret_cast<const T *>(p.U) + ((int64_t)rho * gamma + j - 1) * V;
+      recompute_tile_z<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
+                          (int)((d_off + j - 1) & 31), p.invT, zbuf);
+      __syncthreads();
+      if (tid < kTileN) {
+        const int64_t qi = (int64_t)rho * gamma + j - 1;
+        const float mq = p.q_stats[2 * qi], rq = 1.0f / p.q_stats[2 * qi + 1];
+        const float mp = ps.x, rp = 1.0f / ps.y;
+        const int col = tstar * kTileN + tid;
+        float e = 0.0f;
+        if (col < V) {
+          const float qv = fexp(zbuf[tid] - mq) * rq;
+          const float pv = fexp(Elem<T>::at(Prow, col) * p.invT - mp) * rp;
+          e = fmaxf(pv - qv, 0.0f);
+        }
+        ebuf[tid] = e;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int pick = pick_in_tile(ebuf, s_before, 1.0f, target);
+        if (lane == 0) ired[4] = tstar * kTileN + pick;
+      }
+      __syncthreads();
+      final_token = ired[4];
+    } else {
+      residual = false;  // residual mass rounded to zero: fall back to p_j
+    }
+  }
+  if (!residual) {
+    // p_j by tiles: the bonus row has kept partials; a rejected row (fallback)
+    // gets its tile masses by one pass over the row
+    const bool bonus = n == ell;
+    if (bonus) {
+      const float2 *bt = p.bonus_tiles + (int64_t)rho * nT;
+      for (int t = tid; t < nT; t += kBlock) wbuf[t] = bt[t].y * fexp(bt[t].x - ps.x);
+    } else {
+      for (int t = wave; t < nT; t += kBlock / kWave) {
+        float acc = 0.0f;
+        for (int q = lane; q < kTileN; q += kWave) {
+          const int col = t * kTileN + q;
+          if (col < V) acc += fexp(Elem<T>::at(Prow, col) * p.invT - ps.x);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) wbuf[t] = acc;
+      }
+    }
+    __syncthreads();
+    float total, target;
+    const int tstar = pick_tile(wbuf, nT, uf, fred, ired, &s_before, &total, &target);
+    if (tid < kTileN) {
+      const int col = tstar * kTileN + tid;
+      ebuf[tid] = col < V ? fexp(Elem<T>::at(Prow, col) * p.invT - ps.x) : 0.0f;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int pick = pick_in_tile(ebuf, s_before, 1.0f, target);
+      if (lane == 0) ired[4] = tstar * kTileN + pick;
+    }
+    __syncthreads();
+    final_token = ired[4];
+  }
+
+  // ---- outputs
+  for (int i = tid; i <= gamma; i += kBlock) {
+    int v = -1;
+    if (i < n) v = xr[i];
+    else if (i == n) v = final_token;
+    yrow[i] = v;
+  }
+  if (tid == 0) p.n_acc[rho] = n;
+}
+
+template <typename T>
+static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
+  const int nT = n_tiles_of(L.V);
+  RowStatsParams rs{};
+  rs.n_rows = L.rows_capacity; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.X = L.P;
+  rs.row_offset = L.row_offset; rs.R = L.R; rs.chunks = L.p_chunks;
+  rs.bonus_tiles = L.bonus_tiles; rs.err = L.err;
+  row_chunk_stats_kernel<T><<<dim3(kChunks, L.rows_capacity), kBlock, 0, stream>>>(rs);
+
+  BiasTileParams bp{};
+  bp.R = L.R; bp.gamma = L.gamma; bp.V = L.V; bp.r = L.r; bp.n_tiles = nT; bp.invT = L.invT;
+  bp.U = L.U; bp.W1 = L.W1; bp.W2 = L.W2; bp.x0 = L.x0; bp.x = L.x; bp.err = L.err;
+  bp.ell = L.ell; bp.row_offset = L.row_offset; bp.rows_capacity = L.rows_capacity;
+  bp.P = L.P; bp.p_chunks = L.p_chunks; bp.q_stats = L.q_stats; bp.pair_partials = L.pair_partials;
+  const int max_rows = L.R * L.gamma;
+  bias_tile_kernel<T, 128, Epi::kVerify><<<dim3((max_rows + 127) / 128, nT), kBlock, 0, stream>>>(bp);
+
+  FinalizeParams fp{};
+  fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT;
+  fp.rows_capacity = L.rows_capacity; fp.invT = L.invT; fp.ell = L.ell; fp.row_offset = L.row_offset;
+  fp.P = L.P; fp.U = L.U; fp.W1 = L.W1; fp.W2 = L.W2; fp.x0 = L.x0; fp.x = L.x;
+  fp.q_stats = L.q_stats; fp.q_x = L.q_x; fp.seed = L.seed; fp.round = L.round;
+  fp.p_chunks = L.p_chunks; fp.bonus_tiles = L.bonus_tiles; fp.pair_partials = L.pair_partials;
+  fp.n_acc = L.n_acc; fp.y = L.y; fp.c_star = L.c_star; fp.err = L.err;
+  verify_finalize_kernel<T><<<L.R, kBlock, 0, stream>>>(fp);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const VerifyLaunch &L, hipStream_t stream) {
+  return L.bf16 ? launch_verify_t<bf16_t>(L, stream) : launch_verify_t<float>(L, stream);
+}
+
+// ------------------------------------------------------------- tv_overlap
+struct OverlapParams {
+  int n_rows, V, n_tiles;
+  float invT;
+  const void *P, *Q;
+  const float *p_stats, *q_stats;     // given (m, S), or NULL
+  const float2 *p_chunks, *q_chunks;  // computed, when the stats are not given
+  float *partial;                     // [n_rows][kChunks]
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void overlap_chunk_kernel(OverlapParams p) {
+  __shared__ float red[8];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, V = p.V, nT = p.n_tiles;
+  float mp, rp, mq, rq;
+  if (p.p_stats != nullptr) {
+    mp = p.p_stats[2 * (int64_t)row]; rp = 1.0f / p.p_stats[2 * (int64_t)row + 1];
+    mq = p.q_stats[2 * (int64_t)row]; rq = 1.0f / p.q_stats[2 * (int64_t)row + 1];
+  } else {
+    const float2 a = combine_chunk_stats(p.p_chunks + (int64_t)row * kChunks);
+    const float2 b = combine_chunk_stats(p.q_chunks + (int64_t)row * kChunks);
+    mp = a.x; rp = 1.0f / a.y; mq = b.x; rq = 1.0f / b.y;
+  }
+  const int tpc = (nT + kChunks - 1) / kChunks;
+  const int vb = min(c * tpc, nT) * kTileN, ve = min(min(c * tpc + tpc, nT) * kTileN, V);
+  const T *Pr = reinterpret_cast<const T *>(p.P) + (int64_t)row * V;
+  const T *Qr = reinterpret_cast<const T *>(p.Q) + (int64_t)row * V;
+  constexpr int kPer = Elem<T>::kPerVec;
+  constexpr int kUnroll = 2;
+  float acc = 0.0f;
+  for (int v0 = vb + tid * kPer; v0 < ve; v0 += kBlock * kPer * kUnroll) {
+    float a[kUnroll][kPer], b[kUnroll][kPer];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock * kPer;
+      ok[u] = v < ve;
+      if (ok[u]) {
+        Elem<T>::vec(Pr, v, a[u]);
+        Elem<T>::vec(Qr, v, b[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const float pv = fexp(a[u][q] * p.invT - mp) * rp;
+        const float qv = fexp(b[u][q] * p.invT - mq) * rq;
+        acc += fminf(pv, qv);
+      }
+    }
+  }
+  const float s = block_sum(acc, red);
+  if (tid == 0) p.partial[(int64_t)row * kChunks + c] = s;
+}
+
+__global__ void overlap_combine_kernel(int n_rows, const float *partial, float *c_star) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) s += partial[(int64_t)row * kChunks + c];
+  c_star[row] = s;
+}
+
+template <typename T>
+static hipError_t launch_overlap_t(const OverlapLaunch &L, hipStream_t stream) {
+  const int nT = n_tiles_of(L.V);
+  if (L.p_stats == nullptr) {
+    RowStatsParams rs{};
+    rs.n_rows = L.n_rows; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.err = L.err;
+    rs.X = L.P; rs.chunks = L.p_chunks;
+    row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs);
+    rs.X = L.Q; rs.chunks = L.q_chunks;
+    row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs);
+  }
+  OverlapParams op{};
+  op.n_rows = L.n_rows; op.V = L.V; op.n_tiles = nT; op.invT = L.invT; op.P = L.P; op.Q = L.Q;
+  op.p_stats = L.p_stats; op.q_stats = L.q_stats; op.p_chunks = L.p_chunks;
+  op.q_chunks = L.q_chunks; op.partial = L.partial;
+  overlap_chunk_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(op);
+  overlap_combine_kernel<<<(L.n_rows + 255) / 256, 256, 0, stream>>>(L.n_rows, L.partial, L.c_star);
+  return hipGetLastError();
+}
+
+hipError_t launch_overlap(const OverlapLaunch &L, hipStream_t stream) {
+  return L.bf16 ? launch_overlap_t<bf16_t>(L, stream) : launch_overlap_t<float>(L, stream);
+}
+
+__global__ void clear_error_kernel(int32_t *err) { *err = 0; }
+
+hipError_t launch_clear_error(int32_t *err, hipStream_t stream) {
+  clear_error_kernel<<<1, 1, 0, stream>>>(err);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

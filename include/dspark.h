@@ -1,0 +1,227 @@
+/*
+ * dspark.h -- C ABI of the DSpark per-round speculative-decoding hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: DSpark, "Confidence-Scheduled Speculative Decoding with
+ * Semi-Autoregressive Generation" (arXiv 2607.05147), as described by
+ *   [Blog]    numb3r33 blog, "DSpark: confidence-scheduled speculative decoding"
+ *   [Bangkok] vllmbangkok blog, "DSpark"
+ *   [KB]      edgeai1 speculative-decoding knowledge base, "DSpark 精读"
+ *   [Reaper]  mkdocs.reaper.mx, "3 · DSpark"
+ *
+ * Four operations, each one call:
+ *   dspark_draft       Markov-head drafting of a gamma-token block per request
+ *   dspark_schedule    confidence scheduler: how many drafts each request verifies
+ *   dspark_verify      exact speculative-sampling verification of the ragged batch
+ *   dspark_tv_overlap  the soft confidence label c* = sum_v min(p, q) on logit pairs
+ *
+ * Notation.  q is the draft law and p the target law (Blog, "One-token
+ * exactness").  R requests, indexed rho = 0..R-1; block length gamma; draft
+ * positions k = 1..gamma; vocabulary size V; rank r of the low-rank transition
+ * B = W1 W2 (Blog, "Markov sequential head"); temperature T ("temp").
+ *
+ * Conventions for every entry point.
+ *  - Array pointers are DEVICE pointers (memory of the GPU that is current on
+ *    the calling thread), 16-byte aligned, densely packed, row-major unless
+ *    stated.  Inputs are never modified.  The caller owns every buffer; the
+ *    library allocates nothing and keeps no state except inside the caller's
+ *    workspace.
+ *  - Each call validates its arguments on the host first; on failure it returns
+ *    the status and enqueues nothing.  Otherwise it enqueues kernels on
+ *    `stream` and returns DSPARK_OK without waiting (asynchronous).  A launch
+ *    failure returns DSPARK_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Element type dt applies to every logit and weight array of a call:
+ *    DSPARK_F32 = IEEE binary32, DSPARK_BF16 = bfloat16.  Accumulation is fp32.
+ *  - Shape limits: 1 <= R; 1 <= gamma <= 64; 8 <= V <= 262144 with V % 8 == 0;
+ *    r a multiple of 16 with 16 <= r <= 256 (r <= 128 for DSPARK_F32).
+ *  - Random numbers: counter-based Philox4x64-10 (Salmon et al., SC'11) with
+ *    key (seed, 0) and counter (position, rho, stream, round); the uniform is
+ *    the top 24 bits of the first output word times 2^-24.  Streams: 0 = draft
+ *    sample, 1 = accept test, 2 = final (residual or bonus) sample.  A round is
+ *    reproducible bit for bit from (seed, round).
+ *  - Device-side data errors (a token outside [0, V), a confidence outside
+ *    [0, 1] or NaN, an inconsistent ell/row_offset, a non-finite logit
+ *    statistic) cannot be seen by the host.  Kernels then stay in bounds, write
+ *    sentinel outputs and OR a DSPARK_DEVERR_* bit into a sticky word held in
+ *    the first 256 bytes of the call's workspace.  dspark_device_error reads it;
+ *    dspark_clear_device_error clears it.  Clear a workspace once after
+ *    allocating it.
+ *  - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Scheduler modes (KB section 4; Bangkok 4.2.2; Blog "Async scheduler in
+ * practice").  OFF verifies every draft (ell = gamma, the offline setting of
+ * Bangkok 5.1).  EARLY_STOP admits along the sorted path while the throughput
+ * strictly increases (the non-anticipating ideal).  FULL_SEARCH takes the
+ * smallest admission count that maximizes throughput over the whole path (for
+ * a stepped SPS table).  ASYNC_TOPK takes the capacity K from the confidences
+ * of round t-2 (FULL_SEARCH on c_prev2) and admits the top K by current
+ * survival. */
+typedef enum {
+  DSPARK_SCHED_OFF = 0,
+  DSPARK_SCHED_EARLY_STOP = 1,
+  DSPARK_SCHED_FULL_SEARCH = 2,
+  DSPARK_SCHED_ASYNC_TOPK = 3
+} dspark_sched_mode;
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_NULL = 1,      /* a required pointer is NULL                     */
+  DSPARK_ERR_SHAPE = 2,     /* a size outside the limits above                */
+  DSPARK_ERR_DTYPE = 3,     /* unknown element type                           */
+  DSPARK_ERR_VALUE = 4,     /* temp not finite and > 0, or a bad scalar       */
+  DSPARK_ERR_WORKSPACE = 5, /* ws_bytes below the *_workspace() size          */
+  DSPARK_ERR_SPS_TABLE = 6, /* SPS table missing or shorter than R(1+gamma)+1 */
+  DSPARK_ERR_MODE = 7,      /* unknown scheduler mode or missing c / c_prev2  */
+  DSPARK_ERR_ALIGN = 8,     /* a pointer not 16-byte aligned                  */
+  DSPARK_ERR_HIP = 9        /* a HIP launch or runtime call failed            */
+} dspark_status;
+
+/* Bits of the sticky device error word. */
+#define DSPARK_DEVERR_TOKEN 1      /* a token (anchor or draft) outside [0, V)      */
+#define DSPARK_DEVERR_CONFIDENCE 2 /* a confidence outside [0, 1] or NaN           */
+#define DSPARK_DEVERR_LENGTH 4     /* ell outside [0, gamma] or row_offset mismatch */
+#define DSPARK_DEVERR_NONFINITE 8  /* a row max or normalizer not finite           */
+
+/* ------------------------------------------------------------------ draft --
+ * Semi-autoregressive Markov-head drafting (Blog "Markov sequential head";
+ * Bangkok 4.1; KB section 2).  For every request rho, with x_0 = x0[rho], for
+ * k = 1..gamma (left to right; step k needs x_{k-1}):
+ *   z_k(v) = (U[rho][k-1][v] + sum_i W1[x_{k-1}][i] * W2(i, v)) * (1/temp)
+ *   q_k    = softmax(z_k),  m = max_v z_k(v),  S = sum_v exp(z_k(v) - m)
+ *   x_k    = smallest v with u*S < sum_{w<=v} exp(z_k(w) - m),
+ *            u = uniform(position k, rho, stream 0, round)
+ * The bias row W1[x_{k-1}] W2 is a [R, r] x [r, V] product on bf16 matrix
+ * cores with fp32 accumulation.  Optional confidence head (Bangkok 4.2.1; KB
+ * section 4): c_k = sigmoid(sum_j w_conf[j] h[rho][k-1][j]
+ *                          + sum_i w_conf[d+i] W1[x_{k-1}][i] + b_conf).
+ *
+ * Inputs
+ *   U      [R][gamma][V]  draft base logits U_k of the parallel backbone (dt)
+ *   W1     [V][r]         row x is the transition embedding W1[x, :] (dt)
+ *   W2     r x V factor stored COLUMN-major: element (i, v) at W2[v*r + i],
+ *          so the r coefficients of vocabulary entry v are contiguous (dt)
+ *   x0     [R]            anchor tokens (the target's last token), int32
+ *   h      [R][gamma][d]  backbone hidden states for the confidence head (dt), or NULL
+ *   d      width of h (d % 8 == 0, 8 <= d <= 65536); ignored when h == NULL
+ *   w_conf [d + r] fp32 head weights; b_conf fp32 bias; ignored when h == NULL
+ *   seed, round           Philox key and round counter
+ * Outputs
+ *   x       [R][gamma]    drafted tokens x_1..x_gamma, int32
+ *   q_stats [R][gamma][2] (m, S) of z_k, so q_k(v) = exp(z_k(v) - m) / S, fp32
+ *   q_x     [R][gamma]    q_k(x_k), fp32
+ *   c       [R][gamma]    confidences c_k, written iff h != NULL (may be NULL otherwise)
+ * Workspace: dspark_draft_workspace(R, gamma, V, r, dt) bytes. */
+size_t dspark_draft_workspace(int R, int gamma, int V, int r, dspark_dtype dt);
+dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                           const void *U, const void *W1, const void *W2, const int32_t *x0,
+                           const void *h, int d, const float *w_conf, float b_conf,
+                           uint64_t seed, uint64_t round,
+                           int32_t *x, float *q_stats, float *q_x, float *c,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------- schedule --
+ * Hardware-aware prefix scheduler (KB section 4; Blog "Scheduler objective",
+ * "Greedy prefix allocation"; Reaper 3.3).  One workgroup:
+ *   a[rho][j] = fl32(a[rho][j-1] * c[rho][j]), a[rho][0] = 1, binary32 left to right
+ *   candidates (rho, j), sorted by a descending, then j ascending, then rho ascending
+ *   A_n = sum of floor(a * 2^32) over the first n candidates (int64)
+ *   tau_n = R + A_n * 2^-32,  B_n = R + n,  theta_n = tau_n * SPS[B_n]   (fp64)
+ *   n* by mode; ell[rho] = admitted candidates of rho (a prefix by the order);
+ *   row_offset = exclusive scan of (1 + ell).
+ * Inputs
+ *   c       [R][gamma] conditional confidences in [0, 1], fp32 (may be NULL in OFF mode)
+ *   c_prev2 [R][gamma] confidences of round t-2, ASYNC_TOPK only (else ignored)
+ *   SPS     [B_max + 1] target steps per second indexed by verify batch size B,
+ *           fp64; B_max >= R * (1 + gamma).  May be NULL in OFF mode.
+ *   R * gamma <= 16384.
+ * Outputs
+ *   ell [R], row_offset [R + 1] int32; a [R][gamma] fp32 (may be NULL);
+ *   n_admitted [1] int32; theta [1] fp64 (theta_{n*}; NaN when c is NULL).
+ * Workspace: dspark_schedule_workspace(R, gamma) bytes. */
+size_t dspark_schedule_workspace(int R, int gamma);
+dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode,
+                              const float *c, const float *c_prev2,
+                              const double *SPS, int B_max,
+                              int32_t *ell, int32_t *row_offset, float *a,
+                              int32_t *n_admitted, double *theta,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- verify --
+ * Exact speculative-sampling verification of the flattened ragged batch (Blog
+ * "One-token exactness", "Why only the longest accepted prefix survives",
+ * "Variable-length verification without wasting kernels"; KB sections 7-8).
+ * For request rho with ell = ell[rho] and base = row_offset[rho]:
+ *   p_k = softmax(P[base + k - 1] * (1/temp)), k = 1..ell+1
+ *   q_k = the draft law of dspark_draft at position k (z_k recomputed from
+ *         x_{k-1} with the draft's arithmetic; normalized by q_stats)
+ *   accept x_k iff uniform(k, rho, stream 1, round) * q_x[rho][k-1] < p_k(x_k)
+ *   n = (first rejected k) - 1, or ell when all are accepted
+ *   final token: if n < ell, drawn from (p_{n+1} - q_{n+1})_+ (from p_{n+1}
+ *   if that mass is not positive); otherwise the bonus token from p_{ell+1};
+ *   both by inverse CDF with uniform(position, rho, stream 2, round)
+ *   c*_k = sum_v min(p_k(v), q_k(v)) = 1 - TV(p_k, q_k), k = 1..ell
+ * Inputs
+ *   ell [R], row_offset [R+1]: as written by dspark_schedule (ell in [0, gamma],
+ *        row_offset[rho+1] = row_offset[rho] + 1 + ell[rho], row_offset[0] = 0)
+ *   rows_capacity: host bound on row_offset[R], R <= rows_capacity <= R(1+gamma)
+ *   P   [rows_capacity][V] target logits; row row_offset[rho] + k - 1 holds
+ *       position k = 1..ell+1 of request rho (dt)
+ *   U, W1, W2, x0: as given to dspark_draft; x [R][gamma] the drafted tokens
+ *   q_stats, q_x: as written by dspark_draft (verification uses the SAME q)
+ * Outputs
+ *   n_acc  [R]           accepted drafts n, int32
+ *   y      [R][gamma+1]  x_1..x_n, then the final token, then -1, int32
+ *   c_star [R][gamma]    c*_k for k <= ell, NaN beyond, fp32
+ * Workspace: dspark_verify_workspace(R, gamma, V, rows_capacity) bytes. */
+size_t dspark_verify_workspace(int R, int gamma, int V, int rows_capacity);
+dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                            const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                            const void *P, const void *U, const void *W1, const void *W2,
+                            const int32_t *x0, const int32_t *x,
+                            const float *q_stats, const float *q_x,
+                            uint64_t seed, uint64_t round,
+                            int32_t *n_acc, int32_t *y, float *c_star,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- tv_overlap --
+ * Soft confidence label on explicit logit pairs (Blog "Total variation label";
+ * KB section 4): c*[i] = sum_v min(p_i(v), q_i(v)) with p_i = softmax(P[i]/temp)
+ * and q_i = softmax(Q[i]/temp).
+ * Inputs
+ *   P, Q [n_rows][V] logits (dt)
+ *   p_stats, q_stats [n_rows][2] fp32 (m, S) with p(v) = exp(P[i][v]/temp - m) / S,
+ *   both given (one pass over P and Q) or both NULL (computed: two passes)
+ * Output: c_star [n_rows] fp32.
+ * Workspace: dspark_tv_overlap_workspace(n_rows, V) bytes. */
+size_t dspark_tv_overlap_workspace(int n_rows, int V);
+dspark_status dspark_tv_overlap(int n_rows, int V, dspark_dtype dt, float temp,
+                                const void *P, const void *Q,
+                                const float *p_stats, const float *q_stats,
+                                float *c_star, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- utilities -- */
+const char *dspark_status_string(dspark_status s);
+/* Waits for `stream`, then copies the sticky device error word of workspace ws
+ * to *code (0 = no error).  Returns DSPARK_ERR_HIP if the stream faulted. */
+dspark_status dspark_device_error(const void *ws, int32_t *code, hipStream_t stream);
+/* Enqueues a kernel on `stream` that zeroes the sticky error word of ws. */
+dspark_status dspark_clear_device_error(void *ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */
