@@ -218,3 +218,35 @@ def flatten_target(T: np.ndarray, row_offset: np.ndarray, ell: np.ndarray) -> np
     """The verify batch: rows row_offset[rho] + k - 1 = T[rho][k-1], k = 1..ell+1."""
     rows = [T[rho, : int(ell[rho]) + 1] for rho in range(T.shape[0])]
     return np.ascontiguousarray(np.concatenate(rows, axis=0))
+
+
+def request_rows(cfg: Config, rho: int, sig: Optional[np.ndarray] = None):
+    """(U_req [gamma][V], T_req [gamma+1][V]) of one request, each target row drawn once."""
+    s = np.float32(sigma(cfg)[rho] if sig is None else sig[rho])
+    Tq = np.empty((cfg.gamma + 1, cfg.V), dtype=np.uint16 if cfg.dtype == BF16 else np.float32)
+    Uq = np.empty((cfg.gamma, cfg.V), dtype=Tq.dtype)
+    for k in range(1, cfg.gamma + 2):
+        t32 = _target_row32(cfg, rho, k)
+        Tq[k - 1] = _store(cfg, t32)
+        if k <= cfg.gamma:
+            noise = _rng(cfg, _T_UNOISE, rho, k).standard_normal(cfg.V, dtype=np.float32)
+            Uq[k - 1] = _store(cfg, t32 + s * noise)
+    return Uq, Tq
+
+
+def generate(cfg: Config, workers: int = 8, requests=None):
+    """U [R][gamma][V] and T [R][gamma+1][V] (or only the listed requests), drawn in
+    parallel threads; bytes are identical to the per-row functions above."""
+    from concurrent.futures import ThreadPoolExecutor
+    reqs = list(range(cfg.R)) if requests is None else list(requests)
+    sig = sigma(cfg)
+    dt = np.uint16 if cfg.dtype == BF16 else np.float32
+    U = np.empty((len(reqs), cfg.gamma, cfg.V), dtype=dt)
+    T = np.empty((len(reqs), cfg.gamma + 1, cfg.V), dtype=dt)
+
+    def one(i):
+        U[i], T[i] = request_rows(cfg, reqs[i], sig)
+
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        list(ex.map(one, range(len(reqs))))
+    return U, T

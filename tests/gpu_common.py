@@ -1,0 +1,190 @@
+"""Shared helpers of the GPU tests: seeded inputs on the device, one round of
+the hot path through the C ABI, and comparisons with the CPU oracle under the
+stated tolerances (stage by stage: the oracle always conditions on the GPU's
+upstream outputs, so one boundary draw cannot cascade)."""
+import math
+
+import numpy as np
+import torch
+
+import draft_sampling_verification_03_amd as ds
+import oracle
+import synth
+
+DRAW_WINDOW = 1e-6   # a differing draw is exempt iff u is this close to an oracle CDF boundary
+ACCEPT_WINDOW = 1e-6  # a differing accept test is exempt iff |u - p/q| is below this
+
+
+def prob_tol(cfg):
+    """Probabilities and c*: 1e-5 absolute for fp32 inputs, 2e-3 for bf16 inputs."""
+    return 1e-5 if cfg.dtype == synth.F32 else 2e-3
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a)
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to("cuda")
+
+
+class Inputs:
+    """Host arrays (numpy, exactly the bytes the oracle reads) and device copies."""
+
+    def __init__(self, cfg, workers=16):
+        self.cfg = cfg
+        print(f"[inputs] config {cfg.cid} {cfg.name}: R={cfg.R} gamma={cfg.gamma} V={cfg.V}",
+              flush=True)
+        self.U, self.T = synth.generate(cfg, workers=workers)
+        self.W1, self.W2, self.x0 = synth.W1(cfg), synth.W2(cfg), synth.anchors(cfg)
+        self.c = synth.confidences(cfg)
+        self.c_prev2 = synth.confidences(cfg, older=True)
+        self.sps = synth.sps_table(cfg)
+        self.h = self.w_conf = self.b_conf = None
+        if cfg.conf == "head":
+            self.h, self.w_conf, self.b_conf = synth.head(cfg)
+        self.dU, self.dW1, self.dW2, self.dx0 = dev(self.U), dev(self.W1), dev(self.W2), dev(self.x0)
+        self.dT = dev(self.T.reshape(cfg.R * (cfg.gamma + 1), cfg.V))
+        self.dh = dev(self.h) if self.h is not None else None
+        self.dw = dev(self.w_conf) if self.w_conf is not None else None
+        self.dsps = dev(self.sps) if self.sps is not None else None
+        torch.cuda.synchronize()
+
+    def flatten_on_device(self, ell, row_offset):
+        """The verify batch P[row_offset[rho] + k - 1] = T[rho][k - 1], k = 1..ell+1,
+        padded to rows_capacity rows (gathered with torch: data movement only)."""
+        cfg = self.cfg
+        idx = np.concatenate([rho * (cfg.gamma + 1) + np.arange(int(ell[rho]) + 1)
+                              for rho in range(cfg.R)])
+        P = torch.zeros((cfg.rows_capacity, cfg.V), dtype=self.dT.dtype, device="cuda")
+        P[: idx.size] = self.dT.index_select(0, torch.from_numpy(idx).to("cuda"))
+        return P
+
+    def P_request(self, rho, ell):
+        return self.T[rho, : int(ell) + 1]
+
+
+def run_round(inp, mode=None, seed=None, rnd=None, temp=None):
+    """draft -> schedule -> verify on the device; returns host copies."""
+    cfg = inp.cfg
+    mode = cfg.mode if mode is None else mode
+    seed = cfg.seed if seed is None else seed
+    rnd = cfg.round if rnd is None else rnd
+    temp = cfg.temp if temp is None else temp
+    wsd, wss, wsv = ds.Workspace(), ds.Workspace(), ds.Workspace()
+    d = ds.draft(inp.dU, inp.dW1, inp.dW2, inp.dx0, temp=temp, seed=seed, round=rnd, h=inp.dh,
+                 w_conf=inp.dw, b_conf=0.0 if inp.b_conf is None else float(inp.b_conf), ws=wsd)
+    c_dev = d["c"] if inp.dh is not None else (dev(inp.c) if inp.c is not None else None)
+    cp_dev = dev(inp.c_prev2) if (mode == synth.SCHED_ASYNC_TOPK) else None
+    s = ds.schedule(c_dev, inp.dsps, mode, c_prev2=cp_dev, R=cfg.R, gamma=cfg.gamma, ws=wss)
+    torch.cuda.synchronize()
+    ell, ro = s["ell"].cpu().numpy(), s["row_offset"].cpu().numpy()
+    P = inp.flatten_on_device(ell, ro)
+    v = ds.verify(s["ell"], s["row_offset"], P, inp.dU, inp.dW1, inp.dW2, inp.dx0, d["x"],
+                  d["q_stats"], d["q_x"], temp=temp, seed=seed, round=rnd, ws=wsv)
+    torch.cuda.synchronize()
+    out = dict(x=d["x"].cpu().numpy(), q_stats=d["q_stats"].cpu().numpy(),
+               q_x=d["q_x"].cpu().numpy(), c=c_dev.cpu().numpy() if c_dev is not None else None,
+               ell=ell, row_offset=ro, a=s["a"].cpu().numpy() if s["a"] is not None else None,
+               n_admitted=int(s["n_admitted"].cpu()[0]), theta=float(s["theta"].cpu()[0]),
+               n_acc=v["n_acc"].cpu().numpy(), y=v["y"].cpu().numpy(),
+               c_star=v["c_star"].cpu().numpy(), P=P,
+               err=(wsd.error_code(), wss.error_code(), wsv.error_code()),
+               mode=mode, seed=seed, round=rnd, temp=temp)
+    return out
+
+
+def check_draft_position(inp, g, rho, k, stats):
+    """Oracle draw at (rho, k) conditioned on the GPU's x_{k-1}."""
+    cfg = inp.cfg
+    prev = int(inp.x0[rho]) if k == 1 else int(g["x"][rho, k - 2])
+    u = oracle.uniform(g["seed"], g["round"], k, rho, oracle.STREAM_DRAFT)
+    o = oracle.draft_position(inp.U[rho, k - 1], inp.W1, inp.W2, prev, u, temp=g["temp"],
+                              want_law=True)
+    gx = int(g["x"][rho, k - 1])
+    assert 0 <= gx < cfg.V
+    if gx != o["x"]:
+        lo = o["cdf"][gx - 1] if gx > 0 else 0.0
+        hi = o["cdf"][gx]
+        assert lo - DRAW_WINDOW <= u < hi + DRAW_WINDOW, \
+            f"draft draw (rho={rho}, k={k}): gpu {gx} oracle {o['x']} u={u} cdf=[{lo}, {hi})"
+        stats["draw_exempt"] += 1
+    tol = prob_tol(cfg)
+    assert abs(g["q_x"][rho, k - 1] - o["q"][gx]) <= tol
+    m, S = g["q_stats"][rho, k - 1]
+    assert abs((m + math.log(S)) - (o["m"] + math.log(o["S"]))) <= tol * max(1.0, abs(o["m"]))
+    if inp.h is not None:
+        oc = oracle.conf_head(inp.h[rho, k - 1], inp.w_conf, inp.b_conf, inp.W1, prev)
+        assert abs(g["c"][rho, k - 1] - oc) <= tol
+    stats["draws"] += 1
+
+
+def check_schedule(inp, g):
+    cfg = inp.cfg
+    if g["c"] is None:
+        o = oracle.schedule(None, None, g["mode"], R=cfg.R, gamma=cfg.gamma)
+    else:
+        o = oracle.schedule(g["c"], inp.sps, g["mode"], c_prev2=inp.c_prev2)
+    assert (g["ell"] == o["ell"]).all(), "ell differs"
+    assert (g["row_offset"] == o["row_offset"]).all(), "row_offset differs"
+    assert g["n_admitted"] == o["n_admitted"]
+    if math.isnan(o["theta"]):
+        assert math.isnan(g["theta"])
+    else:
+        assert g["theta"] == o["theta"], f"theta {g['theta']!r} vs {o['theta']!r}"
+    if g["a"] is not None:
+        assert (g["a"] == o["a"]).all(), "survival products differ"
+    return o
+
+
+def check_verify_request(inp, g, rho, stats):
+    cfg = inp.cfg
+    ell = int(g["ell"][rho])
+    P_req = inp.P_request(rho, ell)
+    args = (P_req, inp.U[rho], inp.W1, inp.W2, int(inp.x0[rho]), g["x"][rho], ell, g["seed"],
+            g["round"], rho)
+    o = oracle.verify_request(*args, temp=g["temp"])
+    tol = prob_tol(cfg)
+    gc = g["c_star"][rho]
+    assert np.allclose(gc[:ell], o["c_star"][:ell], atol=tol), f"c* differs (rho={rho})"
+    assert np.isnan(gc[ell:]).all()
+    gn = int(g["n_acc"][rho])
+    if gn != o["n_acc"]:
+        k0 = min(gn, o["n_acc"])  # first position whose decisions differ is k0 + 1
+        u, ratio = o["u_acc"][k0], o["ratio"][k0]
+        assert abs(u - ratio) < ACCEPT_WINDOW, \
+            f"accept test (rho={rho}, k={k0 + 1}): gpu n={gn} oracle n={o['n_acc']} u={u} p/q={ratio}"
+        stats["accept_exempt"] += 1
+    of = oracle.verify_request(*args, temp=g["temp"], force_n=gn, want_cdf=True)
+    gy = g["y"][rho]
+    assert (gy[:gn] == g["x"][rho, :gn]).all()
+    assert (gy[gn + 1:] == -1).all()
+    gf = int(gy[gn])
+    assert 0 <= gf < cfg.V
+    if gf != of["y"][gn]:
+        cdf, u = of["final_cdf"], of["final_u"]
+        lo = cdf[gf - 1] if gf > 0 else 0.0
+        assert lo - DRAW_WINDOW <= u < cdf[gf] + DRAW_WINDOW, \
+            f"final draw (rho={rho}): gpu {gf} oracle {of['y'][gn]} u={u}"
+        stats["draw_exempt"] += 1
+    stats["requests"] += 1
+
+
+def check_properties(inp, g):
+    """Invariants at every position, any size."""
+    cfg = inp.cfg
+    assert g["err"] == (0, 0, 0), f"device error words {g['err']}"
+    x = g["x"]
+    assert ((x >= 0) & (x < cfg.V)).all()
+    assert ((g["q_x"] > 0) & (g["q_x"] <= 1.0 + 1e-6)).all()
+    assert (g["q_stats"][..., 1] >= 1.0 - 1e-6).all()
+    ell, n = g["ell"], g["n_acc"]
+    assert ((ell >= 0) & (ell <= cfg.gamma)).all()
+    assert ((n >= 0) & (n <= ell)).all()
+    for rho in range(cfg.R):
+        y = g["y"][rho]
+        assert (y[: n[rho]] == x[rho, : n[rho]]).all() and 0 <= y[n[rho]] < cfg.V
+        assert (y[n[rho] + 1:] == -1).all()
+        cs = g["c_star"][rho]
+        assert ((cs[: ell[rho]] >= -1e-6) & (cs[: ell[rho]] <= 1 + 1e-5)).all()
+        assert np.isnan(cs[ell[rho]:]).all()
