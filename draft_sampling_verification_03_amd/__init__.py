@@ -11,5 +11,6 @@ from ._abi import (  # noqa: F401
     DSPARK_SCHED_FULL_SEARCH, DSPARK_SCHED_OFF, DSparkError, LIB_PATH, STATUS_NAMES,
     dspark_clear_device_error, dspark_device_error, dspark_draft, dspark_draft_workspace,
     dspark_schedule, dspark_schedule_workspace, dspark_status_string, dspark_tv_overlap,
-    dspark_tv_overlap_workspace, dspark_verify, dspark_verify_workspace, library)
+    dspark_tv_overlap_workspace, dspark_trace_collect, dspark_trace_enable, dspark_trace_entry,
+    dspark_verify, dspark_verify_workspace, library, trace_summary)
 from .api import draft, schedule, tv_overlap, verify, Workspace  # noqa: F401

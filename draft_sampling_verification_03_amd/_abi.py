@@ -55,8 +55,13 @@ def library():
         L.dspark_tv_overlap.argtypes = [_i, _i, _i, _f] + [_vp] * 6 + [_sz, _vp]
         L.dspark_device_error.argtypes = [_vp, _vp, _vp]
         L.dspark_clear_device_error.argtypes = [_vp, _vp]
+        L.dspark_trace_enable.argtypes = [_i]
+        L.dspark_trace_collect.argtypes = []
+        L.dspark_trace_entry.argtypes = [_i, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
+                                         C.POINTER(C.c_int)]
         for name in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_tv_overlap",
-                     "dspark_device_error", "dspark_clear_device_error"):
+                     "dspark_device_error", "dspark_clear_device_error", "dspark_trace_enable",
+                     "dspark_trace_collect", "dspark_trace_entry"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -134,3 +139,31 @@ def dspark_device_error(ws, stream):
 
 def dspark_clear_device_error(ws, stream):
     return library().dspark_clear_device_error(_p(ws), _s(stream))
+
+
+def dspark_trace_enable(on):
+    return library().dspark_trace_enable(1 if on else 0)
+
+
+def dspark_trace_collect():
+    return library().dspark_trace_collect()
+
+
+def dspark_trace_entry(i):
+    """Returns (status, name, total_ms, launches)."""
+    name, ms, n = C.c_char_p(), C.c_double(), C.c_int()
+    st = library().dspark_trace_entry(i, C.byref(name), C.byref(ms), C.byref(n))
+    return st, (name.value.decode() if name.value else None), ms.value, n.value
+
+
+def trace_summary():
+    """{kernel name: (total_ms, launches)} of the records since dspark_trace_enable(1)."""
+    n = dspark_trace_collect()
+    if n < 0:
+        raise DSparkError(9, "dspark_trace_collect")
+    out = {}
+    for i in range(n):
+        st, name, ms, cnt = dspark_trace_entry(i)
+        if st == 0:
+            out[name] = (ms, cnt)
+    return out

@@ -79,6 +79,8 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   L.err = (int32_t *)carve(ws, &off, kWsHeader);
   L.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
   L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
+  L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
   L.b_conf = b_conf; L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
@@ -141,6 +143,8 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
   L.p_chunks = (float2 *)carve(ws, &off, (size_t)rows_capacity * 4 * 8);
   L.bonus_tiles = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
   L.pair_partials = (float2 *)carve(ws, &off, (size_t)R * gamma * n_tiles_of(V) * 8);
+  L.row_map = (int4 *)carve(ws, &off, (size_t)R * gamma * 16);
+  L.A_rows = carve(ws, &off, (size_t)R * gamma * kMaxRowBytes);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.rows_capacity = rows_capacity;
   L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp; L.ell = ell; L.row_offset = row_offset;
   L.P = P; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.x = x; L.q_stats = q_stats; L.q_x = q_x;

@@ -208,113 +208,134 @@ template <typename T> __host__ __device__ constexpr int lds_pitch(int r) {
   return r + 16 / (int)sizeof(T);
 }
 
-// Bias main loop for one wave: acc[mb][nb] (32 x 32 blocks) += A * B^T over
-// K = r, where
-//   A rows come from LDS:   row (a_row0 + 32 mb + lane % 32), pitch a_pitch
-//                           (a_pitch = 0 makes every row read the same data)
-//   B rows from global:     W2 column v = b_col0 + 32 nb + lane % 32 (r contiguous
-//                           coefficients); columns >= V read as zero
-// K advances in steps of 16 (bf16: one 32x32x16 MFMA) in increasing order, and
-// each accumulator starts at zero.  Output element (row i, column j) of a block
-// is in lane (j + 32 * ((i / 4) % 2)), register 4 * (i / 8) + i % 4.
-template <int WMB, int WNB>
-__device__ __forceinline__ void bias_mainloop(const bf16_t *ldsA, int a_pitch, int a_row0,
-                                              const bf16_t *W2, int V, int r, int b_col0,
-                                              floatx16 (&acc)[WMB][WNB]) {
+// Matrix-core bias product.  A wave owns one 32-column block of a vocabulary
+// tile: its B operand (the r coefficients of each of the 32 W2 columns) is
+// loaded once into registers, all K at a time, and reused for every 32-row
+// block of A.  A rows come from LDS: row (a_row0 + 32 mb + lane % 32) at pitch
+// a_pitch (a_pitch = 0 makes every row read the same data).  K advances in
+// increasing order (bf16: one 32x32x16 MFMA per 16; fp32: one 32x32x2 MFMA per
+// 2) from a zero accumulator.  Every kernel that forms z uses these two
+// functions, so the same element always comes out of the same instruction
+// sequence.  Output element (row i, column j) of a 32x32 block is in lane
+// (j + 32 * ((i / 4) % 2)), register 4 * (i / 8) + i % 4.
+template <typename T> struct BFrag;
+template <> struct BFrag<bf16_t> {
+  static constexpr int kSteps = kMaxRank / 16;  // K = 16 per step
+  u16x8 v[kSteps];
+};
+template <> struct BFrag<float> {
+  static constexpr int kSteps = 128 / 2;        // fp32: r <= 128, K = 2 per step
+  float v[kSteps];
+};
+
+// Columns >= V read as zero.  Every load is issued unconditionally from a
+// clamped in-bounds address (no branches between them) and masked afterwards.
+__device__ __forceinline__ void load_bfrag(const bf16_t *W2, int V, int r, int b_col0,
+                                           BFrag<bf16_t> &b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int v = b_col0 + (lane & 31);
+  const bool ok = v < V;
+  const bf16_t *ptr = W2 + (int64_t)(ok ? v : 0) * r + (lane >> 5) * 8;
+  const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < BFrag<bf16_t>::kSteps; ++ks) {
+    const int kk = ks * 16 < r ? ks * 16 : r - 16;
+    const u16x8 t = *reinterpret_cast<const u16x8 *>(ptr + kk);
+    b.v[ks] = (ok && ks * 16 < r) ? t : zero;
+  }
+}
+__device__ __forceinline__ void load_bfrag(const float *W2, int V, int r, int b_col0,
+                                           BFrag<float> &b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int v = b_col0 + (lane & 31);
+  const bool ok = v < V;
+  const float *ptr = W2 + (int64_t)(ok ? v : 0) * r + (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < BFrag<float>::kSteps; ++ks) {
+    const int kk = ks * 2 < r ? ks * 2 : r - 2;
+    const float t = ptr[kk];
+    b.v[ks] = (ok && ks * 2 < r) ? t : 0.0f;
+  }
+}
+
+template <int WMB>
+__device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_row0, int r,
+                                         const BFrag<bf16_t> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int kq = (lane >> 5) * 8;
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb)
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
-  const bf16_t *bptr[WNB];
-  bool bvalid[WNB];
+  for (int ks = 0; ks < BFrag<bf16_t>::kSteps; ++ks) {
+    if (ks * 16 < r) {
 #pragma unroll
-  for (int nb = 0; nb < WNB; ++nb) {
-    const int v = b_col0 + 32 * nb + (lane & 31);
-    bvalid[nb] = v < V;
-    bptr[nb] = W2 + (int64_t)(bvalid[nb] ? v : 0) * r + kq;
-  }
-  const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-  u16x8 bnext[WNB];
-#pragma unroll
-  for (int nb = 0; nb < WNB; ++nb)
-    bnext[nb] = bvalid[nb] ? *reinterpret_cast<const u16x8 *>(bptr[nb]) : zero;
-  for (int k0 = 0; k0 < r; k0 += 16) {
-    u16x8 bcur[WNB];
-#pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) bcur[nb] = bnext[nb];
-    if (k0 + 16 < r) {
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-        bnext[nb] = bvalid[nb] ? *reinterpret_cast<const u16x8 *>(bptr[nb] + k0 + 16) : zero;
+      for (int mb = 0; mb < WMB; ++mb) {
+        const u16x8 a = *reinterpret_cast<const u16x8 *>(
+            ldsA + (a_row0 + 32 * mb + (lane & 31)) * a_pitch + ks * 16 + kq);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b.v[ks]), acc[mb], 0, 0, 0);
+      }
     }
-    u16x8 a[WMB];
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-      a[mb] = *reinterpret_cast<const u16x8 *>(ldsA + (a_row0 + 32 * mb + (lane & 31)) * a_pitch +
-                                               k0 + kq);
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a[mb]), __builtin_bit_cast(bf16x8, bcur[nb]), acc[mb][nb],
-            0, 0, 0);
   }
 }
-
-// fp32 variant: one 32x32x2 fp32 MFMA per K step of 2, K order increasing.
-template <int WMB, int WNB>
-__device__ __forceinline__ void bias_mainloop(const float *ldsA, int a_pitch, int a_row0,
-                                              const float *W2, int V, int r, int b_col0,
-                                              floatx16 (&acc)[WMB][WNB]) {
+template <int WMB>
+__device__ __forceinline__ void mma_rows(const float *ldsA, int a_pitch, int a_row0, int r,
+                                         const BFrag<float> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
   const int kq = lane >> 5;
 #pragma unroll
   for (int mb = 0; mb < WMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb)
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
-  const float *bptr[WNB];
-  bool bvalid[WNB];
+  for (int ks = 0; ks < BFrag<float>::kSteps; ++ks) {
+    if (ks * 2 < r) {
 #pragma unroll
-  for (int nb = 0; nb < WNB; ++nb) {
-    const int v = b_col0 + 32 * nb + (lane & 31);
-    bvalid[nb] = v < V;
-    bptr[nb] = W2 + (int64_t)(bvalid[nb] ? v : 0) * r + kq;
+      for (int mb = 0; mb < WMB; ++mb) {
+        const float a = ldsA[(a_row0 + 32 * mb + (lane & 31)) * a_pitch + ks * 2 + kq];
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b.v[ks], acc[mb], 0, 0, 0);
+      }
+    }
   }
-  for (int k0 = 0; k0 < r; k0 += 2) {
-    float b[WNB], a[WMB];
+}
+
+// 16 bytes of row data as floats (8 bf16 or 4 fp32)
+__device__ __forceinline__ void unpack16(const uint4 &v, bf16_t *, float *out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int nb = 0; nb < WNB; ++nb) b[nb] = bvalid[nb] ? bptr[nb][k0] : 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const uint4 &v, float *, float *out) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+
+// Copy n elements (n <= kBlock * MAXIT) from global memory to LDS, thread-strided
+// and unrolled so that every load is in flight before the first store.
+template <int MAXIT, typename E>
+__device__ __forceinline__ void stage_to_lds(const E *__restrict__ src, int n, E *dst) {
+  E v[MAXIT];
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-      a[mb] = ldsA[(a_row0 + 32 * mb + (lane & 31)) * a_pitch + k0 + kq];
+  for (int j = 0; j < MAXIT; ++j) {
+    const int i = threadIdx.x + j * kBlock;
+    if (i < n) v[j] = src[i];
+  }
 #pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < WNB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+  for (int j = 0; j < MAXIT; ++j) {
+    const int i = threadIdx.x + j * kBlock;
+    if (i < n) dst[i] = v[j];
   }
 }
 
 // Row i (0..31) of a 32x32 accumulator block: which lane half and register.
 __device__ __forceinline__ int acc_half_of_row(int i) { return (i >> 2) & 1; }
 __device__ __forceinline__ int acc_reg_of_row(int i) { return 4 * (i >> 3) + (i & 3); }
-
-// Copy one r-wide row (W1[x]) from global memory to LDS with 16-byte pieces.
-template <typename T>
-__device__ __forceinline__ void copy_row_to_lds(T *dst, const T *src, int r, int piece,
-                                                int n_pieces_per_row) {
-  constexpr int kPer = Elem<T>::kPerVec;
-  (void)n_pieces_per_row;
-  *reinterpret_cast<uint4 *>(dst + piece * kPer) =
-      *reinterpret_cast<const uint4 *>(src + piece * kPer);
-  (void)r;
-}
 
 }  // namespace dspark

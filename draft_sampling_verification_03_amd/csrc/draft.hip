@@ -7,8 +7,14 @@
 // whose cumulative mass first exceeds u * S, recomputes z for that tile alone
 // (bit-identical to the fused kernel), and scans inside the tile.  Only the
 // 128-column tile is re-read, never the row.
+//
+// The transition rows W1[x_{k-1}] of step k sit in a contiguous [R][r] buffer
+// (A_k) written by the sampler of step k-1 (by a gather kernel for k = 1), so
+// the tile kernel loads them together with its W2 columns and U rows, with no
+// dependent token lookup in between.
 #include "bias_tile.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dspark {
 
@@ -16,7 +22,8 @@ struct SampleParams {
   int R, gamma, V, r, n_tiles, k;
   float invT;
   const void *U, *W1, *W2;
-  const int32_t *x0;
+  const void *A_cur;         // [R][r]: W1[x_{k-1}] of every request
+  void *A_next;              // [R][r]: receives W1[x_k] (NULL at the last step)
   int32_t *x;
   float *q_stats, *q_x;
   const float2 *tile_stats;  // [R][n_tiles]
@@ -32,24 +39,31 @@ struct SampleParams {
 template <typename T>
 __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   __shared__ float wbuf[kMaxTiles];
+  __shared__ float2 pbuf[kMaxTiles];
   __shared__ float zbuf[kTileN];
   __shared__ __align__(16) T arow[kMaxRank + 16];
   __shared__ float fred[8];
   __shared__ int ired[8];
   __shared__ float s_before;
+  __shared__ int s_token;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rho = blockIdx.x, k = p.k, V = p.V, r = p.r, nT = p.n_tiles;
   const int64_t slot = (int64_t)rho * p.gamma + (k - 1);
+  constexpr int kPer = 16 / (int)sizeof(T);
+  const int pieces = r * (int)sizeof(T) / 16;
 
-  int prev = k == 1 ? p.x0[rho] : p.x[slot - 1];
-  if (prev < 0 || prev >= V) {
-    if (tid == 0) flag_error(p.err, kErrToken);
-    prev = prev < 0 ? 0 : V - 1;
+  // 1. stage the row's tile partials and W1[x_{k-1}] (= A_k[rho]) in LDS, one
+  //    round trip; then the row maximum and tile masses w_t = s_t exp(m_t - m)
+  {
+    const T *Acur = reinterpret_cast<const T *>(p.A_cur) + (int64_t)rho * r;
+    uint4 a = make_uint4(0, 0, 0, 0);
+    if (tid < pieces) a = *reinterpret_cast<const uint4 *>(Acur + tid * kPer);
+    stage_to_lds<kMaxTiles / kBlock>(p.tile_stats + (int64_t)rho * nT, nT, pbuf);
+    if (tid < pieces) *reinterpret_cast<uint4 *>(arow + tid * kPer) = a;
   }
-
-  // 1. row maximum and tile masses w_t = s_t * exp(m_t - m), scanned in tile order
-  const float2 *part = p.tile_stats + (int64_t)rho * nT;
+  __syncthreads();
+  const float2 *part = pbuf;
   const int cpt = (nT + kBlock - 1) / kBlock;
   const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
   float lm = -INFINITY;
@@ -97,13 +111,6 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   }
 
   // 3. recompute z of that tile, bit-identical to the fused kernel
-  {
-    const T *W1 = reinterpret_cast<const T *>(p.W1);
-    const int pieces = r * (int)sizeof(T) / 16;
-    if (tid < pieces)
-      *reinterpret_cast<uint4 *>(arow + tid * (16 / sizeof(T))) =
-          *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * r + tid * (16 / sizeof(T)));
-  }
   __syncthreads();
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
   recompute_tile_z<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
@@ -137,6 +144,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       p.q_stats[2 * slot] = m;
       p.q_stats[2 * slot + 1] = S;
       p.q_x[slot] = fexp(zbuf[pick] - m) / S;
+      s_token = xk;  // in [0, V): a picked column always has positive mass
     }
   }
 
@@ -150,6 +158,36 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       p.c[slot] = 1.0f / (1.0f + expf(-s));
     }
   }
+
+  // 6. the next step's transition row: A_{k+1}[rho] = W1[x_k]
+  if (p.A_next != nullptr) {
+    __syncthreads();
+    const int xk = min(max(s_token, 0), V - 1);
+    if (tid < pieces)
+      *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_next) + (int64_t)rho * r + tid * kPer) =
+          *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) + (int64_t)xk * r +
+                                           tid * kPer);
+  }
+}
+
+// rows[i] = W1[tokens[i]] for i < n (r elements each); tokens outside [0, V)
+// are flagged and clamped.  8 rows per workgroup, 32 threads per row.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gather_rows_kernel(int n, int V, int r, const T *W1,
+                                                             const int32_t *tokens, T *rows,
+                                                             int32_t *err) {
+  constexpr int kPer = 16 / (int)sizeof(T);
+  const int i = blockIdx.x * 8 + threadIdx.x / 32, pc = threadIdx.x & 31;
+  const int pieces = r * (int)sizeof(T) / 16;
+  if (i >= n) return;
+  int t = tokens[i];
+  if (t < 0 || t >= V) {
+    if (pc == 0) flag_error(err, kErrToken);
+    t = t < 0 ? 0 : V - 1;
+  }
+  if (pc < pieces)
+    *reinterpret_cast<uint4 *>(rows + (int64_t)i * r + pc * kPer) =
+        *reinterpret_cast<const uint4 *>(W1 + (int64_t)t * r + pc * kPer);
 }
 
 // sh[rho][k] = sum_j w[j] h[rho][k][j]: one wave per (rho, k), 16-byte loads.
@@ -182,21 +220,33 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   bp.err = L.err; bp.tile_stats = L.tile_stats;
   SampleParams sp{};
   sp.R = L.R; sp.gamma = L.gamma; sp.V = L.V; sp.r = L.r; sp.n_tiles = n_tiles;
-  sp.invT = L.invT; sp.U = L.U; sp.W1 = L.W1; sp.W2 = L.W2; sp.x0 = L.x0; sp.x = L.x;
+  sp.invT = L.invT; sp.U = L.U; sp.W1 = L.W1; sp.W2 = L.W2; sp.x = L.x;
   sp.q_stats = L.q_stats; sp.q_x = L.q_x; sp.tile_stats = L.tile_stats;
   sp.seed = L.seed; sp.round = L.round; sp.err = L.err;
   if (L.h != nullptr) {
     const int n_slots = L.R * L.gamma;
-    head_hidden_dot_kernel<T><<<(n_slots + 3) / 4, kBlock, 0, stream>>>(
-        n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh);
+    DSPARK_LAUNCH("head_hidden_dot", stream,
+                  head_hidden_dot_kernel<T><<<(n_slots + 3) / 4, kBlock, 0, stream>>>(
+                      n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh));
     sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
   }
-  const dim3 grid((L.R + TM - 1) / TM, n_tiles);
+  void *A[2] = {L.A0, L.A1};
+  DSPARK_LAUNCH("gather_rows", stream,
+                gather_rows_kernel<T><<<(L.R + 7) / 8, kBlock, 0, stream>>>(
+                    L.R, L.V, L.r, reinterpret_cast<const T *>(L.W1), L.x0,
+                    reinterpret_cast<T *>(A[0]), L.err));
+  // x: vocabulary tiles; one workgroup walks every row tile of its vocabulary
+  // tile with the same W2 columns in registers, so W2 crosses HBM once a step
+  const dim3 grid(n_tiles, 1);
   for (int k = 1; k <= L.gamma; ++k) {
     bp.k = k;
+    bp.A = A[(k - 1) & 1];
     sp.k = k;
-    bias_tile_kernel<T, TM, Epi::kDraft><<<grid, kBlock, 0, stream>>>(bp);
-    draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp);
+    sp.A_cur = A[(k - 1) & 1];
+    sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
+    DSPARK_LAUNCH("bias_tile_draft", stream,
+                  draft_tile_kernel<T><<<grid, kBlock, 0, stream>>>(bp));
+    DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp));
   }
   return hipGetLastError();
 }
@@ -204,11 +254,9 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
 hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream) {
   const int tm = tile_rows_for(L.R);
   if (L.bf16) {
-    if (tm == 128) return launch_draft_t<bf16_t, 128>(L, stream);
     if (tm == 64) return launch_draft_t<bf16_t, 64>(L, stream);
     return launch_draft_t<bf16_t, 32>(L, stream);
   }
-  if (tm == 128) return launch_draft_t<float, 128>(L, stream);
   if (tm == 64) return launch_draft_t<float, 64>(L, stream);
   return launch_draft_t<float, 32>(L, stream);
 }

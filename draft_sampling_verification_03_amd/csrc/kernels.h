@@ -8,8 +8,9 @@
 
 namespace dspark {
 
-// rows per bias tile for an M-row product
-inline int tile_rows_for(int M) { return M >= 96 ? 128 : (M > 32 ? 64 : 32); }
+// rows per bias tile for an M-row product (64-row tiles fit the register file
+// without spills next to the resident W2 columns and the prefetched U)
+inline int tile_rows_for(int M) { return M > 32 ? 64 : 32; }
 
 constexpr size_t kWsHeader = 256;  // sticky error word lives at the start of every workspace
 
@@ -29,6 +30,7 @@ struct DraftLaunch {
   int32_t *err;
   float2 *tile_stats;  // [R][n_tiles]
   float *sh;           // [R][gamma]
+  void *A0, *A1;       // [R][r] each: transition rows of the current and next step
 };
 
 struct ScheduleLaunch {
@@ -58,6 +60,8 @@ struct VerifyLaunch {
   float2 *p_chunks;      // [rows_capacity][4]
   float2 *bonus_tiles;   // [R][n_tiles]
   float2 *pair_partials; // [R * gamma][n_tiles]
+  int4 *row_map;         // [R * gamma]
+  void *A_rows;          // [R * gamma][r] transition rows of the compact rows
 };
 
 struct OverlapLaunch {
@@ -82,8 +86,12 @@ hipError_t launch_clear_error(int32_t *err, hipStream_t stream);
 inline size_t ws_align(size_t b) { return (b + 255) & ~(size_t)255; }
 inline int n_tiles_of(int V) { return (V + 127) / 128; }
 
+// a transition row W1[x] holds r <= 256 bf16 or r <= 128 fp32 values: <= 512 bytes
+constexpr size_t kMaxRowBytes = 512;
+
 inline size_t draft_ws_bytes(int R, int gamma, int V) {
-  return kWsHeader + ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4);
+  return kWsHeader + ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4) +
+         2 * ws_align((size_t)R * kMaxRowBytes);
 }
 inline size_t schedule_ws_bytes(int R, int gamma) {
   (void)R; (void)gamma;
@@ -91,7 +99,8 @@ inline size_t schedule_ws_bytes(int R, int gamma) {
 }
 inline size_t verify_ws_bytes(int R, int gamma, int V, int rows_capacity) {
   return kWsHeader + ws_align((size_t)rows_capacity * 4 * 8) +
-         ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * n_tiles_of(V) * 8);
+         ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * n_tiles_of(V) * 8) +
+         ws_align((size_t)R * gamma * 16) + ws_align((size_t)R * gamma * kMaxRowBytes);
 }
 inline size_t overlap_ws_bytes(int n_rows, int V) {
   (void)V;

@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dspark {
 
@@ -26,6 +27,7 @@ constexpr int kMaxCandidates = 8192;
 
 struct SchedShared {
   uint64_t keys[kMaxCandidates];
+  float conf[kMaxCandidates];  // the confidences being ranked, staged from global memory
   int64_t wave_i64[kSchedWaves];
   double wave_d[kSchedWaves];
   int wave_i[kSchedWaves];
@@ -39,6 +41,23 @@ __device__ __forceinline__ float survival_step(float run, float c, int32_t *err,
   }
   (void)err;
   return run * c;
+}
+
+// c -> sh.conf with every load of a thread in flight at once (coalesced)
+__device__ __forceinline__ void stage_confidences(const float *c, int N, SchedShared &sh) {
+  constexpr int kIt = kMaxCandidates / kSchedThreads;
+  float v[kIt];
+#pragma unroll
+  for (int j = 0; j < kIt; ++j) {
+    const int i = threadIdx.x + j * kSchedThreads;
+    v[j] = i < N ? c[i] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < kIt; ++j) {
+    const int i = threadIdx.x + j * kSchedThreads;
+    if (i < N) sh.conf[i] = v[j];
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ uint64_t cand_key(float a, int j, int rho) {
@@ -124,12 +143,13 @@ __device__ int sorted_candidates(int R, int gamma, const float *c, float *a_out,
   const int N = R * gamma;
   int P2 = 1;
   while (P2 < N) P2 <<= 1;
+  stage_confidences(c, N, sh);
   bool bad = false;
   for (int rho = threadIdx.x; rho < R; rho += kSchedThreads) {
     float run = 1.0f;
     for (int j = 1; j <= gamma; ++j) {
       const int64_t idx = (int64_t)rho * gamma + (j - 1);
-      run = survival_step(run, c[idx], err, &bad);
+      run = survival_step(run, sh.conf[idx], err, &bad);
       if (a_out) a_out[idx] = run;
       sh.keys[idx] = cand_key(run, j, rho);
     }
@@ -217,13 +237,14 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleLaunch 
   uint64_t threshold = ~(uint64_t)0;  // OFF: everything admitted
   if (L.mode == 0) {
     if (L.c != nullptr) {
+      stage_confidences(L.c, N, sh);
       bool bad = false;
       int64_t local = 0;
       for (int rho = threadIdx.x; rho < R; rho += kSchedThreads) {
         float run = 1.0f;
         for (int j = 1; j <= gamma; ++j) {
           const int64_t idx = (int64_t)rho * gamma + (j - 1);
-          run = survival_step(run, L.c[idx], L.err, &bad);
+          run = survival_step(run, sh.conf[idx], L.err, &bad);
           if (L.a) L.a[idx] = run;
           local += fixed_weight(run);
         }
@@ -262,28 +283,41 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleLaunch 
   __syncthreads();
 
   // lengths: count each request's keys <= threshold (a prefix), then offsets
+  // (sh.conf holds the current confidences: the last array staged)
+  constexpr int kMaxPerThread = kMaxCandidates / kSchedThreads;  // R <= N <= 8192
   const int cpr = (R + kSchedThreads - 1) / kSchedThreads;
   const int r0 = min((int)threadIdx.x * cpr, R), r1 = min(r0 + cpr, R);
+  int lens[kMaxPerThread];
   int64_t local = 0;
-  for (int rho = r0; rho < r1; ++rho) {
-    int l = gamma;
-    if (L.mode != 0) {
-      bool bad = false;
-      float run = 1.0f;
-      l = 0;
-      for (int j = 1; j <= gamma; ++j) {
-        run = survival_step(run, L.c[(int64_t)rho * gamma + (j - 1)], L.err, &bad);
-        if (cand_key(run, j, rho) <= threshold && n_star > 0) l = j; else break;
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int rho = r0 + q;
+    lens[q] = 0;
+    if (rho < r1) {
+      int l = gamma;
+      if (L.mode != 0) {
+        bool bad = false;
+        float run = 1.0f;
+        l = 0;
+        for (int j = 1; j <= gamma; ++j) {
+          run = survival_step(run, sh.conf[(int64_t)rho * gamma + (j - 1)], L.err, &bad);
+          if (cand_key(run, j, rho) <= threshold && n_star > 0) l = j; else break;
+        }
       }
+      L.ell[rho] = l;
+      lens[q] = l;
+      local += 1 + l;
     }
-    L.ell[rho] = l;
-    local += 1 + l;
   }
   int64_t total;
   int64_t off = sched_exclusive_scan_i64(local, sh, &total);
-  for (int rho = r0; rho < r1; ++rho) {
-    L.row_offset[rho] = (int32_t)off;
-    off += 1 + L.ell[rho];
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int rho = r0 + q;
+    if (rho < r1) {
+      L.row_offset[rho] = (int32_t)off;
+      off += 1 + lens[q];
+    }
   }
   if (threadIdx.x == 0) {
     L.row_offset[R] = (int32_t)total;
@@ -293,7 +327,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleLaunch 
 }
 
 hipError_t launch_schedule(const ScheduleLaunch &L, hipStream_t stream) {
-  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(L);
+  DSPARK_LAUNCH("schedule", stream, schedule_kernel<<<1, kSchedThreads, 0, stream>>>(L));
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@
 //     a two-level inverse CDF.
 #include "bias_tile.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace dspark {
 
@@ -26,6 +27,13 @@ struct RowStatsParams {
   float2 *chunks;             // [n_rows][kChunks]
   float2 *bonus_tiles;        // [R][n_tiles], verify only
   int32_t *err;
+  // verify only: the compact-row map of the verified drafts
+  int gamma;
+  const int32_t *x0, *x;
+  int4 *row_map;              // [R*gamma]: (rho, k, x_{k-1}, target row)
+  int r;
+  const void *W1;
+  void *A_rows;               // [R*gamma][r]: W1[x_{k-1}] of compact row i
 };
 
 __device__ __forceinline__ void online_merge(float &M, float &S, float m, float s) {
@@ -50,13 +58,33 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
       used = p.n_rows;
     }
     if (row >= used) return;
-    if (p.bonus_tiles != nullptr) {  // is this the last row of its request?
-      int lo = 0, hi = p.R;          // last rho with row_offset[rho] <= row
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
+    int lo = 0, hi = p.R;  // request of the row: the last rho with row_offset[rho] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
+    }
+    const int base = p.row_offset[lo];
+    if (p.row_offset[lo + 1] - 1 == row) {
+      rho = lo;  // the last row of its request: the bonus position keeps tile partials
+    } else if (c == 0 && tid < 32) {
+      // a verified draft (k <= ell): its entry of the compact-row map and its
+      // transition row W1[x_{k-1}] for the verify pass
+      const int k = row - base + 1, i = row - lo;
+      if (k >= 1 && k <= p.gamma && i >= 0 && i < p.R * p.gamma) {
+        int prev = k == 1 ? p.x0[lo] : p.x[(int64_t)lo * p.gamma + k - 2];
+        if (prev < 0 || prev >= V) {
+          if (tid == 0) flag_error(p.err, kErrToken);
+          prev = prev < 0 ? 0 : V - 1;
+        }
+        if (tid == 0) p.row_map[i] = make_int4(lo, k, prev, row);
+        constexpr int kPerA = 16 / (int)sizeof(T);
+        if (tid < p.r * (int)sizeof(T) / 16)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r + tid * kPerA) =
+              *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
+                                               (int64_t)prev * p.r + tid * kPerA);
+      } else if (tid == 0) {
+        flag_error(p.err, kErrLength);
       }
-      if (p.row_offset[lo + 1] - 1 == row) rho = lo;
     }
   }
   const int tpc = (nT + kChunks - 1) / kChunks;
@@ -67,8 +95,8 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
   float M = -INFINITY, S = 0.0f;
 
   if (rho < 0) {
-    // online statistics, four 16-byte loads in flight per thread
-    constexpr int kUnroll = 4;
+    // online statistics, eight 16-byte loads in flight per thread
+    constexpr int kUnroll = 8;
     for (int v0 = vb + tid * kPer; v0 < ve; v0 += kBlock * kPer * kUnroll) {
       float x[kUnroll][kPer];
 #pragma unroll
@@ -261,7 +289,11 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
     if (k <= ell) {
       const float2 *pp = p.pair_partials + (d_off + k - 1) * nT;
       float acc = 0.0f;
-      for (int t = lane; t < nT; t += kWave) acc += pp[t].x;
+#pragma unroll
+      for (int j = 0; j < kMaxTiles / kWave; ++j) {  // all loads in flight, fixed order
+        const int t = lane + j * kWave;
+        if (t < nT) acc += pp[t].x;
+      }
       v = wave_sum(acc);
     }
     if (lane == 0) crow[k - 1] = v;
@@ -296,7 +328,11 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   if (residual) {
     // residual masses per tile from the verify pass
     const float2 *pp = p.pair_partials + (d_off + j - 1) * nT;
-    for (int t = tid; t < nT; t += kBlock) wbuf[t] = pp[t].y;
+#pragma unroll
+    for (int j = 0; j < kMaxTiles / kBlock; ++j) {
+      const int t = tid + j * kBlock;
+      if (t < nT) wbuf[t] = pp[t].y;
+    }
     __syncthreads();
     float total, target;
     const int tstar = pick_tile(wbuf, nT, uf, fred, ired, &s_before, &total, &target);
@@ -343,7 +379,11 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
     const bool bonus = n == ell;
     if (bonus) {
       const float2 *bt = p.bonus_tiles + (int64_t)rho * nT;
-      for (int t = tid; t < nT; t += kBlock) wbuf[t] = bt[t].y * fexp(bt[t].x - ps.x);
+#pragma unroll
+      for (int j = 0; j < kMaxTiles / kBlock; ++j) {
+        const int t = tid + j * kBlock;
+        if (t < nT) wbuf[t] = bt[t].y * fexp(bt[t].x - ps.x);
+      }
     } else {
       for (int t = wave; t < nT; t += kBlock / kWave) {
         float acc = 0.0f;
@@ -388,15 +428,26 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   rs.n_rows = L.rows_capacity; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.X = L.P;
   rs.row_offset = L.row_offset; rs.R = L.R; rs.chunks = L.p_chunks;
   rs.bonus_tiles = L.bonus_tiles; rs.err = L.err;
-  row_chunk_stats_kernel<T><<<dim3(kChunks, L.rows_capacity), kBlock, 0, stream>>>(rs);
+  rs.gamma = L.gamma; rs.x0 = L.x0; rs.x = L.x; rs.row_map = L.row_map;
+  rs.r = L.r; rs.W1 = L.W1; rs.A_rows = L.A_rows;
+  DSPARK_LAUNCH("row_chunk_stats", stream,
+                row_chunk_stats_kernel<T><<<dim3(kChunks, L.rows_capacity), kBlock, 0, stream>>>(rs));
 
   BiasTileParams bp{};
   bp.R = L.R; bp.gamma = L.gamma; bp.V = L.V; bp.r = L.r; bp.n_tiles = nT; bp.invT = L.invT;
   bp.U = L.U; bp.W1 = L.W1; bp.W2 = L.W2; bp.x0 = L.x0; bp.x = L.x; bp.err = L.err;
   bp.ell = L.ell; bp.row_offset = L.row_offset; bp.rows_capacity = L.rows_capacity;
   bp.P = L.P; bp.p_chunks = L.p_chunks; bp.q_stats = L.q_stats; bp.pair_partials = L.pair_partials;
-  const int max_rows = L.R * L.gamma;
-  bias_tile_kernel<T, 128, Epi::kVerify><<<dim3((max_rows + 127) / 128, nT), kBlock, 0, stream>>>(bp);
+  bp.row_map = L.row_map;
+  bp.A = L.A_rows;
+  // the number of verified drafts lives on the device: every workgroup walks
+  // the row tiles of its group (y) up to sum(ell) with its W2 columns resident;
+  // 64-row tiles leave room in registers for the prefetched U and P segments
+  constexpr int TMv = 64;
+  const int max_mt = (L.R * L.gamma + TMv - 1) / TMv;
+  DSPARK_LAUNCH("bias_tile_verify", stream,
+                bias_tile_kernel<T, TMv, Epi::kVerify>
+                <<<dim3(nT, max_mt < 2 ? max_mt : 2), kBlock, 0, stream>>>(bp));
 
   FinalizeParams fp{};
   fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT;
@@ -405,7 +456,7 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   fp.q_stats = L.q_stats; fp.q_x = L.q_x; fp.seed = L.seed; fp.round = L.round;
   fp.p_chunks = L.p_chunks; fp.bonus_tiles = L.bonus_tiles; fp.pair_partials = L.pair_partials;
   fp.n_acc = L.n_acc; fp.y = L.y; fp.c_star = L.c_star; fp.err = L.err;
-  verify_finalize_kernel<T><<<L.R, kBlock, 0, stream>>>(fp);
+  DSPARK_LAUNCH("verify_finalize", stream, verify_finalize_kernel<T><<<L.R, kBlock, 0, stream>>>(fp));
   return hipGetLastError();
 }
 
@@ -486,16 +537,21 @@ static hipError_t launch_overlap_t(const OverlapLaunch &L, hipStream_t stream) {
     RowStatsParams rs{};
     rs.n_rows = L.n_rows; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.err = L.err;
     rs.X = L.P; rs.chunks = L.p_chunks;
-    row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs);
+    DSPARK_LAUNCH("row_chunk_stats", stream,
+                  row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs));
     rs.X = L.Q; rs.chunks = L.q_chunks;
-    row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs);
+    DSPARK_LAUNCH("row_chunk_stats", stream,
+                  row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs));
   }
   OverlapParams op{};
   op.n_rows = L.n_rows; op.V = L.V; op.n_tiles = nT; op.invT = L.invT; op.P = L.P; op.Q = L.Q;
   op.p_stats = L.p_stats; op.q_stats = L.q_stats; op.p_chunks = L.p_chunks;
   op.q_chunks = L.q_chunks; op.partial = L.partial;
-  overlap_chunk_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(op);
-  overlap_combine_kernel<<<(L.n_rows + 255) / 256, 256, 0, stream>>>(L.n_rows, L.partial, L.c_star);
+  DSPARK_LAUNCH("overlap_chunk", stream,
+                overlap_chunk_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(op));
+  DSPARK_LAUNCH("overlap_combine", stream,
+                overlap_combine_kernel<<<(L.n_rows + 255) / 256, 256, 0, stream>>>(
+                    L.n_rows, L.partial, L.c_star));
   return hipGetLastError();
 }
 

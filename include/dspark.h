@@ -221,6 +221,18 @@ dspark_status dspark_device_error(const void *ws, int32_t *code, hipStream_t str
 /* Enqueues a kernel on `stream` that zeroes the sticky error word of ws. */
 dspark_status dspark_clear_device_error(void *ws, hipStream_t stream);
 
+/* Opt-in kernel timing (diagnostics; off by default).  While enabled, every
+ * kernel the library launches is bracketed by two HIP events on its stream.
+ * dspark_trace_enable(1) discards earlier records; dspark_trace_collect waits
+ * for the recorded events and returns the number of distinct kernel names (or
+ * -1 on a HIP error); dspark_trace_entry(i, ...) returns the i-th name (a
+ * string owned by the library, valid until the next collect or enable), its
+ * summed elapsed milliseconds and its launch count.  Not for concurrent use
+ * from several host threads while enabled. */
+dspark_status dspark_trace_enable(int on);
+int dspark_trace_collect(void);
+dspark_status dspark_trace_entry(int i, const char **name, double *total_ms, int *launches);
+
 #ifdef __cplusplus
 }
 #endif

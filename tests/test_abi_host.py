@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ds.library()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in dspark.h but not exported"
 
