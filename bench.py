@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=10,
                     help="requests in the CPU-oracle sample (0 disables)")
     ap.add_argument("--workers", type=int, default=16, help="host threads drawing the inputs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters); not part of the timed steps")
     return ap.parse_args()
 
 
@@ -96,6 +99,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     wsd, wss, wsv, wso = ds.Workspace(), ds.Workspace(), ds.Workspace(), ds.Workspace()
+    if args.copy_calibration_mib > 0:
+        # a plain elementwise copy kernel: bf16 -> fp32 conversion of n/2 elements
+        # reads n bytes and writes 2n bytes
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
+        dst = src.float()
+        torch.cuda.synchronize()
+        del src, dst
 
     def draft():
         return ds.draft(dU, dW1, dW2, dx0, temp=cfg.temp, seed=cfg.seed, round=cfg.round, h=dh,
@@ -188,16 +199,21 @@ def main():
     # ---- algorithmic work per launch of each kernel
     rows_used = R + sum_ell
     n_ov = Pp.shape[0]
+    # The fused tile kernels do 2*M*r*V flops on (M + r)*V*s bytes (M rows of U or
+    # U and P, plus W2): 2*128*256/((128 + 256)*2) = 85 flop/B for the draft step,
+    # below the MI355X ridge (~312 flop/B), so their roofline is HBM bandwidth;
+    # their matrix-core use is reported beside it.
     work = {
         "bias_tile_draft": dict(bytes=R * V * s_el + r * V * s_el + R * r * s_el + R * nT * 8,
-                                flops=2.0 * R * r * V, bound="mfma"),
+                                flops=2.0 * R * r * V, bound="hbm"),
         "draft_sample": dict(bytes=R * nT * 8 + R * 128 * (r + 1) * s_el, flops=0.0, bound="hbm"),
         "head_hidden_dot": dict(bytes=R * gamma * cfg.d * s_el, flops=2.0 * R * gamma * cfg.d,
                                 bound="hbm"),
         "schedule": dict(bytes=R * gamma * 4 * 2, flops=0.0, bound="hbm"),
         "row_chunk_stats": dict(bytes=rows_used * V * s_el + rows_used * 32, flops=0.0, bound="hbm"),
         "bias_tile_verify": dict(bytes=2 * sum_ell * V * s_el + r * V * s_el + sum_ell * nT * 8,
-                                 flops=2.0 * sum_ell * r * V, bound="mfma"),
+                                 flops=2.0 * sum_ell * r * V, bound="hbm"),
+        "gather_rows": dict(bytes=2 * R * r * s_el, flops=0.0, bound="hbm"),
         "verify_finalize": dict(bytes=sum_ell * nT * 8 + R * nT * 8, flops=0.0, bound="hbm"),
         "overlap_chunk": dict(bytes=2 * n_ov * V * s_el, flops=0.0, bound="hbm"),
         "overlap_combine": dict(bytes=n_ov * 20, flops=0.0, bound="hbm"),
@@ -221,6 +237,7 @@ def main():
         roof = dict(bound="hbm", achieved=dk["gbps"], peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(dk["gbps"] / PEAK_HBM_GBPS, 4))
     roof["kernel"] = dom
+    roof["mfma_frac"] = round(dk["tflops"] / PEAK_BF16_TFLOPS, 4)
     roof["traffic"] = None
     traffic_file = os.path.join(PROFILE_DIR, f"traffic_{dom}_config{cfg.cid}.json")
     if os.path.exists(traffic_file):

@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kBlock, 3) void draft_tile_kernel(BiasTileParams p)
     // address of out-of-range pieces, whose values the epilogue masks
 #pragma unroll
     for (int j = 0; j < kVec; ++j)
-      uv[j] = *reinterpret_cast<const uint4 *>(Urow + min(vbase + j * kPer, V - kPer));
+      uv[j] = ld_stream(Urow + min(vbase + j * kPer, V - kPer));
   };
   auto store_a = [&](int buf, const uint4 (&av)[kMaxA]) {
     T *dst = reinterpret_cast<T *>(abuf[buf]);
@@ -374,6 +374,151 @@ __global__ __launch_bounds__(kBlock, 3) void draft_tile_kernel(BiasTileParams p)
       p.tile_stats[(int64_t)rho * p.n_tiles + nt] = make_float2(mx, s);
 #pragma unroll
     for (int j = 0; j < kVec; ++j) u_cur[j] = u_next[j];
+  }
+}
+
+// Verify product, software-pipelined over 32-row tiles of the compacted verified
+// drafts.  Per tile t the workgroup, with its W2 columns resident: loads the
+// compact-row map entry of tile t+1 (one per epilogue row) while multiplying
+// tile t; issues tile t+1's A rows, U and P row segments and row statistics
+// while reducing tile t; epilogue arithmetic is bias_tile_kernel's verify
+// epilogue (sum min(p, q), sum (p - q)_+ per row and tile).
+template <typename T>
+__global__ __launch_bounds__(kBlock, 2) void verify_tile_kernel(BiasTileParams p) {
+  constexpr int TM = 32;
+  constexpr int kG = kBlock / TM;             // 8 threads per epilogue row
+  constexpr int kSeg = TM * kTileN / kBlock;  // 16 columns per thread
+  constexpr int kPer = 16 / (int)sizeof(T);
+  constexpr int kVec = kSeg / kPer;
+  constexpr int kPitchC = kTileN + 4;
+  constexpr int kMaxA = TM * 32 / kBlock;
+  __shared__ __align__(16) unsigned char abuf[2][TM * kLdsBytesPerRow];
+  __shared__ __align__(16) float cbuf[TM * kPitchC];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int nt = blockIdx.x, V = p.V, r = p.r;
+  int n_rows = p.row_offset[p.R] - p.R;  // sum of ell
+  if (n_rows > p.R * p.gamma) n_rows = p.R * p.gamma;
+  const int n_mt = n_rows > 0 ? (n_rows + TM - 1) / TM : 0;
+  if ((int)blockIdx.y >= n_mt) return;
+  const int pieces = r * (int)sizeof(T) / 16;
+  const int total = TM * pieces;
+  const int a_pitch = lds_pitch<T>(r);
+  const T *Ab = reinterpret_cast<const T *>(p.A);
+  const T *U = reinterpret_cast<const T *>(p.U);
+  const T *P = reinterpret_cast<const T *>(p.P);
+  const int erow = tid / kG, c0 = (tid % kG) * kSeg, vbase = nt * kTileN + c0;
+  const int step = gridDim.y;
+
+  BFrag<T> bfr;
+  load_bfrag(reinterpret_cast<const T *>(p.W2), V, r, nt * kTileN + wave * 32, bfr);
+
+  // compact-row map entry of this thread's epilogue row in tile mt, checked
+  auto load_map = [&](int mt) -> int4 {
+    const int i = mt * TM + erow;
+    int4 e = make_int4(-1, 0, 0, 0);
+    if (mt < n_mt && i < n_rows) {
+      e = p.row_map[i];
+      if (e.x < 0 || e.x >= p.R || e.y < 1 || e.y > p.gamma || e.w < 0 || e.w >= p.rows_capacity) {
+        flag_error(p.err, kErrLength);
+        e.x = -1;
+      }
+    }
+    return e;
+  };
+  // loads of tile mt: A pieces (masked for padding rows), U and P segments of
+  // the thread's row, and the row's draft and target statistics
+  struct Stage {
+    uint4 u[kVec], t[kVec];
+    float mq, rq, mp, rp;
+  };
+  auto load_tile = [&](int mt, int4 e, uint4 (&av)[kMaxA], Stage &s) {
+#pragma unroll
+    for (int j = 0; j < kMaxA; ++j) {
+      const int idx = min(tid + j * kBlock, total - 1);
+      const int row = idx / pieces, pc = idx - row * pieces;
+      const int gi = min(mt * TM + row, n_rows - 1);
+      av[j] = *reinterpret_cast<const uint4 *>(Ab + (int64_t)gi * r + pc * kPer);
+      if (mt * TM + row >= n_rows) av[j] = make_uint4(0, 0, 0, 0);
+    }
+    const bool live = e.x >= 0;
+    const int rho = live ? e.x : 0, k = live ? e.y : 1, prow = live ? e.w : 0;
+    const T *Urow = U + ((int64_t)rho * p.gamma + (k - 1)) * V;
+    const T *Prow = P + (int64_t)prow * V;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int v = min(vbase + j * kPer, V - kPer);  // all-in or all-out pieces (V % 8 == 0)
+      s.u[j] = ld_stream(Urow + v);
+      s.t[j] = ld_stream(Prow + v);
+    }
+    const int64_t qi = (int64_t)rho * p.gamma + k - 1;
+    s.mq = p.q_stats[2 * qi];
+    s.rq = 1.0f / p.q_stats[2 * qi + 1];
+    const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)prow * kChunks);
+    s.mp = ps.x;
+    s.rp = 1.0f / ps.y;
+  };
+  auto store_a = [&](int buf, const uint4 (&av)[kMaxA]) {
+    T *dst = reinterpret_cast<T *>(abuf[buf]);
+#pragma unroll
+    for (int j = 0; j < kMaxA; ++j) {
+      const int idx = tid + j * kBlock;
+      if (idx < total) {
+        const int row = idx / pieces, pc = idx - row * pieces;
+        *reinterpret_cast<uint4 *>(dst + row * a_pitch + pc * kPer) = av[j];
+      }
+    }
+  };
+
+  int mt = blockIdx.y;
+  uint4 a_next[kMaxA];
+  Stage cur, nxt;
+  int4 e_cur = load_map(mt);
+  load_tile(mt, e_cur, a_next, cur);
+  store_a(0, a_next);
+  int buf = 0;
+  for (; mt < n_mt; mt += step) {
+    __syncthreads();  // A of tile mt in LDS; the previous epilogue is done with cbuf
+    const bool more = mt + step < n_mt;
+    const int4 e_next = load_map(mt + step);
+    floatx16 acc[1];
+    mma_rows<1>(reinterpret_cast<const T *>(abuf[buf]), a_pitch, 0, r, bfr, acc);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      cbuf[row * kPitchC + wave * 32 + (lane & 31)] = acc[0][e];
+    }
+    if (more) load_tile(mt + step, e_next, a_next, nxt);
+    __syncthreads();
+    // epilogue of tile mt
+    float smin = 0.0f, sres = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      float u[kPer], t[kPer];
+      unpack16(cur.u[j], (T *)nullptr, u);
+      unpack16(cur.t[j], (T *)nullptr, t);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int col = j * kPer + q;
+        const float zz = (cbuf[erow * kPitchC + c0 + col] + u[q]) * p.invT;
+        const float qv = fexp(zz - cur.mq) * cur.rq;
+        const float pv = fexp(t[q] * p.invT - cur.mp) * cur.rp;
+        const bool in = vbase + col < V;
+        smin += in ? fminf(pv, qv) : 0.0f;
+        sres += in ? fmaxf(pv - qv, 0.0f) : 0.0f;
+      }
+    }
+    smin = group_sum<kG>(smin);
+    sres = group_sum<kG>(sres);
+    const int i = mt * TM + erow;
+    if (e_cur.x >= 0 && (tid % kG) == 0)
+      p.pair_partials[(int64_t)i * p.n_tiles + nt] = make_float2(smin, sres);
+    if (more) {
+      store_a(buf ^ 1, a_next);
+      cur = nxt;
+    }
+    e_cur = e_next;
+    buf ^= 1;
   }
 }
 

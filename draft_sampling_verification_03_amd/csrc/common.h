@@ -59,6 +59,14 @@ template <> struct Elem<bf16_t> {
   }
 };
 
+// 16 bytes of a stream that is read once (logit rows): a non-temporal load, so
+// it does not displace data that is re-read (the W2 factor) from the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // e^x on the transcendental unit: 2^(x log2 e).  Every kernel uses this one
 // function, so equal arguments give equal results everywhere.
 __device__ __forceinline__ float fexp(float x) {

@@ -443,11 +443,9 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   // the number of verified drafts lives on the device: every workgroup walks
   // the row tiles of its group (y) up to sum(ell) with its W2 columns resident;
   // 64-row tiles leave room in registers for the prefetched U and P segments
-  constexpr int TMv = 64;
-  const int max_mt = (L.R * L.gamma + TMv - 1) / TMv;
+  const int max_mt = (L.R * L.gamma + 31) / 32;
   DSPARK_LAUNCH("bias_tile_verify", stream,
-                bias_tile_kernel<T, TMv, Epi::kVerify>
-                <<<dim3(nT, max_mt < 2 ? max_mt : 2), kBlock, 0, stream>>>(bp));
+                verify_tile_kernel<T><<<dim3(nT, max_mt < 2 ? max_mt : 2), kBlock, 0, stream>>>(bp));
 
   FinalizeParams fp{};
   fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT;
