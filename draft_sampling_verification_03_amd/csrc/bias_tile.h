@@ -22,11 +22,12 @@
 // LDS for a row-wise epilogue, and the U (and P) row segments that epilogue
 // reads are prefetched into registers before the matrix-core work starts.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace dspark {
 
-constexpr int kLdsBytesPerRow = 528;  // max(r_max + 8 bf16, r_max + 4 fp32, 132 fp32)
 constexpr int kChunks = 4;            // target-row statistics are kept per quarter row
 
 // Combined statistics of one target row from its kChunks partials, in chunk
@@ -68,470 +69,404 @@ struct BiasTileParams {
 
 enum class Epi { kDraft, kVerify };
 
-template <typename T, int TM, Epi E>
-__global__ __launch_bounds__(kBlock, 2) void bias_tile_kernel(BiasTileParams p) {
-  constexpr int WMB = TM / 32;                // 32-row blocks per wave
-  constexpr int kG = kBlock / TM;             // threads per epilogue row
-  constexpr int kSeg = TM * kTileN / kBlock;  // columns per thread in the epilogue
-  constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte piece
-  constexpr int kVec = kSeg / kPer;           // 16-byte pieces per segment
-  constexpr int kPitchC = kTileN + 4;         // fp32 pitch of the transposed tile
-  constexpr int kMaxA = TM * 32 / kBlock;     // gathered 16-byte pieces per thread (r max)
+// ------------------------------------------------------------------------
+// Row-stationary streaming tile kernel.
+//
+// A workgroup of 4 waves takes a row group of 128 product rows (wave w: rows
+// 32w..32w+31) and a contiguous range of vocabulary tiles.  Each wave keeps
+// the A operand of its 32 rows (all of K) in registers for the whole range;
+// W2 streams through in blocks of 32 columns: loaded into registers two
+// blocks ahead, written to one half of a double-buffered LDS stage (pieces
+// XOR-swizzled per column so the operand reads are free of bank conflicts),
+// and read by all four waves.  U (and P) row segments stream into a register
+// ring two blocks ahead.  After the product a wave transposes its 32x32
+// accumulator through its own LDS scratch so that each lane holds 16
+// consecutive columns of one row, adds U, and folds the block into running
+// per-row sums that are written once per 128-column tile.
+//
+// The loop body covers one tile (4 blocks) with a fixed instruction sequence
+// (loads past the range are clamped, stores of lanes without an output go to
+// a sink), so every wait the compiler inserts counts exactly the loads it
+// needs.
+constexpr int kRowGroup = 128;                          // rows per workgroup
+constexpr int kBlockCols = 32;                          // W2 columns per block
+constexpr int kBlocksPerTile = kTileN / kBlockCols;     // 4
+constexpr int kColPieces = kMaxRank * 2 / 16;           // 16-byte pieces per W2 column (max)
+constexpr int kColPitch = kColPieces + 1;               // pieces per LDS column: one of padding
+constexpr int kStageBytes = kBlockCols * kColPitch * 16;  // one W2 block in LDS: 16.5 KB
+constexpr int kScratchPitch = 36;                       // floats per scratch row
+constexpr int kFlushTiles = 8;                          // tile partials kept in LDS
+
+// the A operand of one wave's 32 rows, all K
+template <typename T> struct AFrag;
+template <> struct AFrag<bf16_t> {
+  static constexpr int kSteps = kMaxRank / 16;
+  u16x8 v[kSteps];
+};
+template <> struct AFrag<float> {
+  static constexpr int kSteps = 64;
+  float v[kSteps];
+};
+
+// Rows past the last real row read a clamped real row (finite values whose
+// outputs are discarded).
+__device__ __forceinline__ void load_afrag(const bf16_t *A, int r, int row, AFrag<bf16_t> &a,
+                                           int ks_static) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bf16_t *ptr = A + (int64_t)row * r + (lane >> 5) * 8;
+  const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < AFrag<bf16_t>::kSteps; ++ks) {
+    const bool in = ks_static > 0 ? ks < ks_static : ks * 16 < r;
+    const int kk = in ? ks * 16 : 0;
+    const u16x8 t = *reinterpret_cast<const u16x8 *>(ptr + kk);
+    a.v[ks] = in ? t : zero;
+  }
+}
+__device__ __forceinline__ void load_afrag(const float *A, int r, int row, AFrag<float> &a,
+                                           int ks_static) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float *ptr = A + (int64_t)row * r + (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < AFrag<float>::kSteps; ++ks) {
+    const bool in = ks_static > 0 ? ks < ks_static : ks * 2 < r;
+    const float t = ptr[in ? ks * 2 : 0];
+    a.v[ks] = in ? t : 0.0f;
+  }
+}
+
+// 16-byte piece pc of column c of a W2 block in LDS.  The column pitch of
+// kColPitch (odd) pieces puts the same piece of 16 consecutive columns in 16
+// different bank groups, and keeps every offset within a column affine.
+__device__ __forceinline__ int w2_slot(int c, int pc) { return c * kColPitch + pc; }
+
+// Product of one wave's 32 rows with one W2 block from LDS.  K advances in
+// increasing order from a zero accumulator with the same instruction as
+// mma_rows, the A operand in registers and the B operand in LDS: the same
+// element comes out of the same instruction sequence.
+template <int KS>
+__device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned char *stage,
+                                          int r, floatx16 &acc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane & 31;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < (KS > 0 ? KS : AFrag<bf16_t>::kSteps); ++ks) {
+    if (KS > 0 || ks * 16 < r) {
+      const u16x8 b = *reinterpret_cast<const u16x8 *>(
+          stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+  }
+}
+template <int KS>
+__device__ __forceinline__ void mma_block(const AFrag<float> &a, const unsigned char *stage,
+                                          int r, floatx16 &acc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane & 31;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < (KS > 0 ? KS : AFrag<float>::kSteps); ++ks) {
+    if (KS > 0 || ks * 2 < r) {
+      const int k = 2 * ks + (lane >> 5);
+      const float b = *reinterpret_cast<const float *>(stage + 16 * w2_slot(c, 0) + 4 * k);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[ks], b, acc, 0, 0, 0);
+    }
+  }
+}
+
+// exchange with the neighbouring lane (l ^ 1)
+__device__ __forceinline__ float pair_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// log2 of a probability exp(x / T - m) / S from a logit x before the
+// temperature and the row's (m, S): x / T - m in one rounding (so an entry
+// near the maximum keeps full relative precision), then scaled to base 2.
+// The verify pass and the residual draw form every per-entry quantity with
+// this function, so they agree element by element.
+__device__ __forceinline__ float log2_prob(float x, float invT, float m, float log2S) {
+  return fmaf(fmaf(x, invT, -m), kLog2e, -log2S);
+}
+
+template <typename T, Epi E, int KS>
+__global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p) {
   constexpr bool kVerify = E == Epi::kVerify;
-  __shared__ __align__(16) unsigned char smem[TM * kLdsBytesPerRow];
-  __shared__ int row_prev[TM];  // token whose W1 row feeds the row (-1: padding row)
-  __shared__ int row_req[TM];   // request of the row
-  __shared__ int row_pos[TM];   // draft position k of the row (0: skipped)
-  __shared__ int row_out[TM];   // output row index
-  __shared__ int row_prow[TM];  // verify: target row of the row
+  constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  constexpr int kSegV = 16 / kPer;            // pieces per 16-column row segment
+  constexpr int kWPieces = kColPieces / 8;     // W2 pieces per thread per block (4)
+  __shared__ __align__(16) unsigned char w2s[2][kStageBytes];
+  __shared__ __align__(16) float scratch[4][32 * kScratchPitch];
+  __shared__ float2 pbuf[kRowGroup][kFlushTiles];  // partials of the last tiles, by row
+  __shared__ int pout[kRowGroup];                  // output row of each row, -1 for none
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int nt = blockIdx.x;
-  const int V = p.V, r = p.r;
+  const int V = p.V, n_tiles = p.n_tiles;
+  const int r = KS > 0 ? KS * (sizeof(T) == 2 ? 16 : 2) : p.r;
+  const int npieces = r * (int)sizeof(T) / 16;  // W2 pieces per column, <= 32
+  const float invT = p.invT, cl = invT * kLog2e;
 
-  int n_rows_total;
-  if constexpr (!kVerify) {
-    n_rows_total = p.R;
+  int n_rows = p.R;
+  if constexpr (kVerify) {
+    n_rows = p.row_offset[p.R] - p.R;  // sum of ell
+    if (n_rows > p.R * p.gamma) n_rows = p.R * p.gamma;
+  }
+  if (n_rows <= 0) return;
+  const int n_rg = (n_rows + kRowGroup - 1) / kRowGroup;
+  // Work: (row group, vocabulary tile) items.  With several row groups and a
+  // grid of 8 * q workgroups, the n_rg workgroups that share a range of tiles
+  // get the same XCD (workgroups are dealt to the 8 XCDs round robin), start
+  // together and walk the same W2 blocks, so W2 comes from that XCD's L2 after
+  // the first of them.  Otherwise: equal contiguous ranges, row-group major.
+  int t0, t1;
+  const int q8 = (int)gridDim.x / 8, cpx = n_rg > 1 && ((int)gridDim.x & 7) == 0 ? q8 / n_rg : 0;
+  if (cpx > 0) {
+    const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int rg = q % n_rg, cx = q / n_rg, n_cr = cpx * 8, c = cx * 8 + x;
+    if (cx >= cpx) return;
+    t0 = rg * n_tiles + (int)((int64_t)c * n_tiles / n_cr);
+    t1 = rg * n_tiles + (int)((int64_t)(c + 1) * n_tiles / n_cr);
   } else {
-    n_rows_total = p.row_offset[p.R] - p.R;  // sum of ell
-    if (n_rows_total > p.R * p.gamma) n_rows_total = p.R * p.gamma;
+    const int total = n_rg * n_tiles;
+    const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    t0 = (int)blockIdx.x * per;
+    t1 = min(total, t0 + per);
   }
-  const int n_mt = n_rows_total > 0 ? (n_rows_total + TM - 1) / TM : 0;
-  if ((int)blockIdx.y >= n_mt) return;  // uniform across the workgroup
 
-  // the wave's 32 W2 columns, all of K, kept for every row tile
-  BFrag<T> bfr;
-  load_bfrag(reinterpret_cast<const T *>(p.W2), V, r, nt * kTileN + wave * 32, bfr);
-
-  T *ldsA = reinterpret_cast<T *>(smem);
-  float *ldsC = reinterpret_cast<float *>(smem);
-  const int a_pitch = lds_pitch<T>(r);
-  const int erow = tid / kG;         // epilogue row of the tile
-  const int c0 = (tid % kG) * kSeg;  // first column of the thread's segment
-  const int vbase = nt * kTileN + c0;
-  const int pieces = r * (int)sizeof(T) / 16;  // 16-byte pieces per W1 row, <= 32
-
-  for (int mt = blockIdx.y; mt < n_mt; mt += gridDim.y) {
-    __syncthreads();  // the previous tile's epilogue is done with LDS
-    // ---- row info: none for the draft (row = request), one load of the
-    //      compact-row map (written by the target-row statistics pass) to verify
-    if (tid < TM) {
-      const int i = mt * TM + tid;
-      int prev = -1, rho = 0, k = 0, prow = 0;
-      if (i < n_rows_total) {
-        if constexpr (!kVerify) {
-          rho = i;
-          k = p.k;
-          prev = 0;  // the row's W1[x_{k-1}] is A[i]
-        } else {
-          const int4 e = p.row_map[i];  // (rho, k, prev, target row), checked when written
-          rho = e.x; k = e.y; prev = e.z; prow = e.w;
-          if (rho < 0 || rho >= p.R || k < 1 || k > p.gamma || prev < 0 || prev >= V ||
-              prow < 0 || prow >= p.rows_capacity) {
-            flag_error(p.err, kErrLength);
-            prev = -1; rho = 0; k = 0; prow = 0;
-          }
-        }
-      }
-      row_prev[tid] = prev;
-      row_req[tid] = rho;
-      row_pos[tid] = k;
-      row_out[tid] = i;
-      row_prow[tid] = prow;
-    }
-    __syncthreads();
-
-    // ---- A rows of this tile from the contiguous transition-row buffer: every
-    //      load in flight before the first store; clamped addresses, masked
-    //      values (zero rows for padding)
-    {
-      const int total = TM * pieces;
-      const T *Ab = reinterpret_cast<const T *>(p.A);
-      const int last_row = n_rows_total - 1;
-      uint4 av[kMaxA];
-#pragma unroll
-      for (int j = 0; j < kMaxA; ++j) {
-        const int idx = min(tid + j * kBlock, total - 1);
-        const int row = idx / pieces, pc = idx - row * pieces;
-        const int gi = min(mt * TM + row, last_row);
-        const uint4 v = *reinterpret_cast<const uint4 *>(Ab + (int64_t)gi * r + pc * kPer);
-        av[j] = row_prev[row] >= 0 ? v : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < kMaxA; ++j) {
-        const int idx = tid + j * kBlock;
-        if (idx < total) {
-          const int row = idx / pieces, pc = idx - row * pieces;
-          *reinterpret_cast<uint4 *>(ldsA + row * a_pitch + pc * kPer) = av[j];
-        }
-      }
-    }
-
-    // ---- prefetch the epilogue's U (and P) row segments: their latency
-    //      overlaps the matrix-core work
-    const int k = row_pos[erow];
-    const bool live = row_prev[erow] >= 0 && k >= 1;
-    const int rho = row_req[erow];
-    const T *Urow =
-        reinterpret_cast<const T *>(p.U) + ((int64_t)rho * p.gamma + (k >= 1 ? k - 1 : 0)) * V;
-    const T *Prow = reinterpret_cast<const T *>(p.P) + (int64_t)row_prow[erow] * V;
-    uint4 upre[kVec], ppre[kVerify ? kVec : 1];
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int v0 = min(vbase + j * kPer, V - kPer);  // V % 8 == 0: pieces are all in or out
-      const uint4 u = *reinterpret_cast<const uint4 *>(Urow + v0);
-      upre[j] = u;
-      if constexpr (kVerify) ppre[j] = *reinterpret_cast<const uint4 *>(Prow + v0);
-    }
-    __syncthreads();
-
-    floatx16 acc[WMB];
-    mma_rows<WMB>(ldsA, a_pitch, 0, r, bfr, acc);
-    __syncthreads();  // A no longer needed: the LDS takes the transposed tile
-#pragma unroll
-    for (int mb = 0; mb < WMB; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        ldsC[row * kPitchC + wave * 32 + (lane & 31)] = acc[mb][e];
-      }
-    __syncthreads();
-
-    // ---- row-wise epilogue on the thread's kSeg consecutive columns
-    if constexpr (!kVerify) {
-      // two passes over the segment (max, then sum of exp); z is formed by the
-      // same expression both times instead of being held in registers
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        float u[kPer];
-        unpack16(upre[j], (T *)nullptr, u);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int col = j * kPer + q;
-          const float zz = (ldsC[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-          mx = fmaxf(mx, (vbase + col < V) ? zz : -INFINITY);
-        }
-      }
-      mx = group_max<kG>(mx);
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        float u[kPer];
-        unpack16(upre[j], (T *)nullptr, u);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int col = j * kPer + q;
-          const float zz = (ldsC[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-          s += (vbase + col < V) ? fexp(zz - mx) : 0.0f;
-        }
-      }
-      s = group_sum<kG>(s);
-      if (live && (tid % kG) == 0)
-        p.tile_stats[(int64_t)row_out[erow] * p.n_tiles + nt] = make_float2(mx, s);
-    } else {
-      float mq = 0.0f, rq = 0.0f, mp = 0.0f, rp = 0.0f;
-      if (live) {
-        const int64_t qi = (int64_t)rho * p.gamma + k - 1;
-        mq = p.q_stats[2 * qi];
-        rq = 1.0f / p.q_stats[2 * qi + 1];
-        const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)row_prow[erow] * kChunks);
-        mp = ps.x;
-        rp = 1.0f / ps.y;
-      }
-      float smin = 0.0f, sres = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        float u[kPer], t[kPer];
-        unpack16(upre[j], (T *)nullptr, u);
-        unpack16(ppre[j], (T *)nullptr, t);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int col = j * kPer + q;
-          const float zz = (ldsC[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-          const float qv = fexp(zz - mq) * rq;
-          const float pv = fexp(t[q] * p.invT - mp) * rp;
-          const bool in = vbase + col < V;
-          smin += in ? fminf(pv, qv) : 0.0f;
-          sres += in ? fmaxf(pv - qv, 0.0f) : 0.0f;
-        }
-      }
-      smin = group_sum<kG>(smin);
-      sres = group_sum<kG>(sres);
-      if (live && (tid % kG) == 0)
-        p.pair_partials[(int64_t)row_out[erow] * p.n_tiles + nt] = make_float2(smin, sres);
-    }
-  }
-}
-
-// Draft product, software-pipelined over 32-row tiles.  One workgroup owns one
-// 128-column vocabulary tile for all R rows: each wave keeps its 32 W2 columns
-// in registers; the A rows of tile t+1 (from the contiguous transition-row
-// buffer, into the other half of a double-buffered LDS area) and its U row
-// segments (into a second register set) are loaded while tile t is multiplied
-// and reduced.  Arithmetic per element is that of bias_tile_kernel's draft
-// epilogue: z = (acc + U) * (1/T), max, then sum of exp(z - max).
-template <typename T>
-__global__ __launch_bounds__(kBlock, 3) void draft_tile_kernel(BiasTileParams p) {
-  constexpr int TM = 32;
-  constexpr int kG = kBlock / TM;             // 8 threads per epilogue row
-  constexpr int kSeg = TM * kTileN / kBlock;  // 16 columns per thread
-  constexpr int kPer = 16 / (int)sizeof(T);
-  constexpr int kVec = kSeg / kPer;           // 16-byte U pieces per thread
-  constexpr int kPitchC = kTileN + 4;
-  constexpr int kMaxA = TM * 32 / kBlock;     // 16-byte A pieces per thread (r max)
-  __shared__ __align__(16) unsigned char abuf[2][TM * kLdsBytesPerRow];
-  __shared__ __align__(16) float cbuf[TM * kPitchC];
-
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int nt = blockIdx.x, V = p.V, r = p.r, R = p.R;
-  const int n_mt = (R + TM - 1) / TM;
-  const int pieces = r * (int)sizeof(T) / 16;
-  const int total = TM * pieces;
-  const int a_pitch = lds_pitch<T>(r);
   const T *Ab = reinterpret_cast<const T *>(p.A);
-  const T *U = reinterpret_cast<const T *>(p.U);
-  const int erow = tid / kG, c0 = (tid % kG) * kSeg, vbase = nt * kTileN + c0;
-
-  BFrag<T> bfr;
-  load_bfrag(reinterpret_cast<const T *>(p.W2), V, r, nt * kTileN + wave * 32, bfr);
-
-  // loads of one row tile: A pieces (masked for padding rows) and U segments
-  auto load_tile = [&](int mt, uint4 (&av)[kMaxA], uint4 (&uv)[kVec]) {
-#pragma unroll
-    for (int j = 0; j < kMaxA; ++j) {
-      const int idx = min(tid + j * kBlock, total - 1);
-      const int row = idx / pieces, pc = idx - row * pieces;
-      const int gi = min(mt * TM + row, R - 1);
-      av[j] = *reinterpret_cast<const uint4 *>(Ab + (int64_t)gi * r + pc * kPer);
-      if (mt * TM + row >= R) av[j] = make_uint4(0, 0, 0, 0);
-    }
-    const int rho = min(mt * TM + erow, R - 1);
-    const T *Urow = U + ((int64_t)rho * p.gamma + (p.k - 1)) * V;
-    // a 16-byte piece is all in or all out of [0, V) (V % 8 == 0): clamp the
-    // address of out-of-range pieces, whose values the epilogue masks
-#pragma unroll
-    for (int j = 0; j < kVec; ++j)
-      uv[j] = ld_stream(Urow + min(vbase + j * kPer, V - kPer));
-  };
-  auto store_a = [&](int buf, const uint4 (&av)[kMaxA]) {
-    T *dst = reinterpret_cast<T *>(abuf[buf]);
-#pragma unroll
-    for (int j = 0; j < kMaxA; ++j) {
-      const int idx = tid + j * kBlock;
-      if (idx < total) {
-        const int row = idx / pieces, pc = idx - row * pieces;
-        *reinterpret_cast<uint4 *>(dst + row * a_pitch + pc * kPer) = av[j];
-      }
-    }
-  };
-
-  uint4 a_next[kMaxA], u_cur[kVec], u_next[kVec];
-  load_tile(0, a_next, u_cur);
-  store_a(0, a_next);
-  for (int mt = 0; mt < n_mt; ++mt) {
-    __syncthreads();  // A of tile mt in LDS; the previous epilogue is done with cbuf
-    const bool more = mt + 1 < n_mt;
-    if (more) load_tile(mt + 1, a_next, u_next);
-    floatx16 acc[1];
-    mma_rows<1>(reinterpret_cast<const T *>(abuf[mt & 1]), a_pitch, 0, r, bfr, acc);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      cbuf[row * kPitchC + wave * 32 + (lane & 31)] = acc[0][e];
-    }
-    if (more) store_a((mt + 1) & 1, a_next);
-    __syncthreads();
-    // epilogue of tile mt: two passes (max, then sum of exp) over 16 columns
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      float u[kPer];
-      unpack16(u_cur[j], (T *)nullptr, u);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int col = j * kPer + q;
-        const float zz = (cbuf[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-        mx = fmaxf(mx, (vbase + col < V) ? zz : -INFINITY);
-      }
-    }
-    mx = group_max<kG>(mx);
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      float u[kPer];
-      unpack16(u_cur[j], (T *)nullptr, u);
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int col = j * kPer + q;
-        const float zz = (cbuf[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-        s += (vbase + col < V) ? fexp(zz - mx) : 0.0f;
-      }
-    }
-    s = group_sum<kG>(s);
-    const int rho = mt * TM + erow;
-    if (rho < R && (tid % kG) == 0)
-      p.tile_stats[(int64_t)rho * p.n_tiles + nt] = make_float2(mx, s);
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) u_cur[j] = u_next[j];
-  }
-}
-
-// Verify product, software-pipelined over 32-row tiles of the compacted verified
-// drafts.  Per tile t the workgroup, with its W2 columns resident: loads the
-// compact-row map entry of tile t+1 (one per epilogue row) while multiplying
-// tile t; issues tile t+1's A rows, U and P row segments and row statistics
-// while reducing tile t; epilogue arithmetic is bias_tile_kernel's verify
-// epilogue (sum min(p, q), sum (p - q)_+ per row and tile).
-template <typename T>
-__global__ __launch_bounds__(kBlock, 2) void verify_tile_kernel(BiasTileParams p) {
-  constexpr int TM = 32;
-  constexpr int kG = kBlock / TM;             // 8 threads per epilogue row
-  constexpr int kSeg = TM * kTileN / kBlock;  // 16 columns per thread
-  constexpr int kPer = 16 / (int)sizeof(T);
-  constexpr int kVec = kSeg / kPer;
-  constexpr int kPitchC = kTileN + 4;
-  constexpr int kMaxA = TM * 32 / kBlock;
-  __shared__ __align__(16) unsigned char abuf[2][TM * kLdsBytesPerRow];
-  __shared__ __align__(16) float cbuf[TM * kPitchC];
-
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-  const int nt = blockIdx.x, V = p.V, r = p.r;
-  int n_rows = p.row_offset[p.R] - p.R;  // sum of ell
-  if (n_rows > p.R * p.gamma) n_rows = p.R * p.gamma;
-  const int n_mt = n_rows > 0 ? (n_rows + TM - 1) / TM : 0;
-  if ((int)blockIdx.y >= n_mt) return;
-  const int pieces = r * (int)sizeof(T) / 16;
-  const int total = TM * pieces;
-  const int a_pitch = lds_pitch<T>(r);
-  const T *Ab = reinterpret_cast<const T *>(p.A);
+  const T *W2 = reinterpret_cast<const T *>(p.W2);
   const T *U = reinterpret_cast<const T *>(p.U);
   const T *P = reinterpret_cast<const T *>(p.P);
-  const int erow = tid / kG, c0 = (tid % kG) * kSeg, vbase = nt * kTileN + c0;
-  const int step = gridDim.y;
+  float *ws = scratch[wave];
+  const int erow_w = lane >> 1;          // epilogue row within the wave
+  const int ec0 = (lane & 1) * 16;       // first epilogue column within the block
+  bool bad_entry = false;
 
-  BFrag<T> bfr;
-  load_bfrag(reinterpret_cast<const T *>(p.W2), V, r, nt * kTileN + wave * 32, bfr);
+  while (t0 < t1) {
+    __syncthreads();  // the previous range's flush is done with pbuf and pout
+    const int rg = t0 / n_tiles, tile0 = t0 - rg * n_tiles;
+    const int ntile = min(n_tiles - tile0, t1 - t0);
+    t0 += ntile;
+    const int nblk = ntile * kBlocksPerTile;
+    const int cb0 = tile0 * kBlocksPerTile;  // first column block
 
-  // compact-row map entry of this thread's epilogue row in tile mt, checked
-  auto load_map = [&](int mt) -> int4 {
-    const int i = mt * TM + erow;
-    int4 e = make_int4(-1, 0, 0, 0);
-    if (mt < n_mt && i < n_rows) {
-      e = p.row_map[i];
-      if (e.x < 0 || e.x >= p.R || e.y < 1 || e.y > p.gamma || e.w < 0 || e.w >= p.rows_capacity) {
-        flag_error(p.err, kErrLength);
-        e.x = -1;
-      }
+    // ---- the wave's A rows (product row = lane % 32 of the wave's 32)
+    AFrag<T> af;
+    load_afrag(Ab, r, min(rg * kRowGroup + wave * 32 + (lane & 31), n_rows - 1), af, KS);
+
+    // ---- this lane's epilogue row: source rows and statistics
+    const int erow = rg * kRowGroup + wave * 32 + erow_w;
+    bool live = erow < n_rows;
+    int rho = 0, k = 1, prow = 0;
+    if constexpr (kVerify) {
+      const int4 e = p.row_map[live ? erow : 0];  // written by the target-row statistics pass
+      const bool bad = e.x < 0 || e.x >= p.R || e.y < 1 || e.y > p.gamma || e.w < 0 ||
+                       e.w >= p.rows_capacity;
+      bad_entry |= live && bad;
+      live = live && !bad;
+      if (live) { rho = e.x; k = e.y; prow = e.w; }
+    } else {
+      if (live) { rho = erow; k = p.k; }
     }
-    return e;
-  };
-  // loads of tile mt: A pieces (masked for padding rows), U and P segments of
-  // the thread's row, and the row's draft and target statistics
-  struct Stage {
-    uint4 u[kVec], t[kVec];
-    float mq, rq, mp, rp;
-  };
-  auto load_tile = [&](int mt, int4 e, uint4 (&av)[kMaxA], Stage &s) {
-#pragma unroll
-    for (int j = 0; j < kMaxA; ++j) {
-      const int idx = min(tid + j * kBlock, total - 1);
-      const int row = idx / pieces, pc = idx - row * pieces;
-      const int gi = min(mt * TM + row, n_rows - 1);
-      av[j] = *reinterpret_cast<const uint4 *>(Ab + (int64_t)gi * r + pc * kPer);
-      if (mt * TM + row >= n_rows) av[j] = make_uint4(0, 0, 0, 0);
-    }
-    const bool live = e.x >= 0;
-    const int rho = live ? e.x : 0, k = live ? e.y : 1, prow = live ? e.w : 0;
+    if ((lane & 1) == 0) pout[wave * 32 + erow_w] = live ? erow : -1;
+    const bool wave_live = rg * kRowGroup + wave * 32 < n_rows;  // uniform per wave
     const T *Urow = U + ((int64_t)rho * p.gamma + (k - 1)) * V;
     const T *Prow = P + (int64_t)prow * V;
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int v = min(vbase + j * kPer, V - kPer);  // all-in or all-out pieces (V % 8 == 0)
-      s.u[j] = ld_stream(Urow + v);
-      s.t[j] = ld_stream(Prow + v);
+    float mq = 0.0f, lq = 0.0f, mp = 0.0f, lp = 0.0f;  // (m, log2 S) of q and p
+    if constexpr (kVerify) {
+      const int64_t qi = (int64_t)rho * p.gamma + k - 1;
+      mq = p.q_stats[2 * qi];
+      lq = log2_fast(p.q_stats[2 * qi + 1]);
+      const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)prow * kChunks);
+      mp = ps.x;
+      lp = log2_fast(ps.y);
     }
-    const int64_t qi = (int64_t)rho * p.gamma + k - 1;
-    s.mq = p.q_stats[2 * qi];
-    s.rq = 1.0f / p.q_stats[2 * qi + 1];
-    const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)prow * kChunks);
-    s.mp = ps.x;
-    s.rp = 1.0f / ps.y;
-  };
-  auto store_a = [&](int buf, const uint4 (&av)[kMaxA]) {
-    T *dst = reinterpret_cast<T *>(abuf[buf]);
-#pragma unroll
-    for (int j = 0; j < kMaxA; ++j) {
-      const int idx = tid + j * kBlock;
-      if (idx < total) {
-        const int row = idx / pieces, pc = idx - row * pieces;
-        *reinterpret_cast<uint4 *>(dst + row * a_pitch + pc * kPer) = av[j];
-      }
-    }
-  };
+    float2 *out = kVerify ? p.pair_partials : p.tile_stats;
 
-  int mt = blockIdx.y;
-  uint4 a_next[kMaxA];
-  Stage cur, nxt;
-  int4 e_cur = load_map(mt);
-  load_tile(mt, e_cur, a_next, cur);
-  store_a(0, a_next);
-  int buf = 0;
-  for (; mt < n_mt; mt += step) {
-    __syncthreads();  // A of tile mt in LDS; the previous epilogue is done with cbuf
-    const bool more = mt + step < n_mt;
-    const int4 e_next = load_map(mt + step);
-    floatx16 acc[1];
-    mma_rows<1>(reinterpret_cast<const T *>(abuf[buf]), a_pitch, 0, r, bfr, acc);
+    // ---- loads of block j (clamped past the range)
+    // native vectors, so that the stages stay in registers
+    struct WRegs { u32x4 w[kWPieces]; };
+    struct URegs { u32x4 u[kSegV]; u32x4 t[kVerify ? kSegV : 1]; };
+    // W2 pieces of a block: thread t takes column t / 8 and pieces
+    // (t % 8) + 8 i, i < 4 (pieces past the column's npieces repeat its last)
+    const int wc = tid >> 3, wp = tid & 7;
+    auto load_w = [&](WRegs &wr, int j) __attribute__((always_inline)) {
+      const int col = min((cb0 + min(j, nblk - 1)) * kBlockCols + wc, V - 1);
+      const T *src = W2 + (int64_t)col * r;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      cbuf[row * kPitchC + wave * 32 + (lane & 31)] = acc[0][e];
-    }
-    if (more) load_tile(mt + step, e_next, a_next, nxt);
-    __syncthreads();
-    // epilogue of tile mt
-    float smin = 0.0f, sres = 0.0f;
+      for (int i = 0; i < kWPieces; ++i)
+        wr.w[i] = *reinterpret_cast<const u32x4 *>(src + min(wp + 8 * i, npieces - 1) * kPer);
+    };
+    auto store_w = [&](int stage, const WRegs &wr) __attribute__((always_inline)) {
+      unsigned char *dst = w2s[stage] + 16 * w2_slot(wc, wp);
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      float u[kPer], t[kPer];
-      unpack16(cur.u[j], (T *)nullptr, u);
-      unpack16(cur.t[j], (T *)nullptr, t);
+      for (int i = 0; i < kWPieces; ++i)
+        if (KS > 0 ? 8 * i < npieces : wp + 8 * i < npieces)
+          *reinterpret_cast<u32x4 *>(dst + 16 * 8 * i) = wr.w[i];
+    };
+    auto load_u = [&](URegs &ur, int j) __attribute__((always_inline)) {
+      const int cb = cb0 + min(j, nblk - 1);
+      // a 16-byte piece is all in or all out of [0, V) (V % 8 == 0)
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int col = j * kPer + q;
-        const float zz = (cbuf[erow * kPitchC + c0 + col] + u[q]) * p.invT;
-        const float qv = fexp(zz - cur.mq) * cur.rq;
-        const float pv = fexp(t[q] * p.invT - cur.mp) * cur.rp;
-        const bool in = vbase + col < V;
-        smin += in ? fminf(pv, qv) : 0.0f;
-        sres += in ? fmaxf(pv - qv, 0.0f) : 0.0f;
+      for (int i = 0; i < kSegV; ++i) {
+        const int col = min(cb * kBlockCols + ec0 + i * kPer, V - kPer);
+        ur.u[i] = ld_stream4(Urow + col);
+        if constexpr (kVerify) ur.t[i] = ld_stream4(Prow + col);
       }
+    };
+
+    // running sums of the current tile
+    float run_m = -INFINITY, run_s = 0.0f;  // draft: max of acc + u, sum of exp
+    float run_min = 0.0f, run_res = 0.0f;   // verify: sum min(p, q), sum (p - q)_+
+
+    // ---- one block: product, transpose, epilogue
+    auto block = [&](int j, const URegs &ur, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool kMask = decltype(mask_tag)::value;
+      floatx16 acc;
+      mma_block<KS>(af, w2s[j & 1], r, acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        ws[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * kScratchPitch + (lane & 31)] = acc[e];
+      wave_sync();  // the other lanes' accumulators are in the scratch
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 c4 = *reinterpret_cast<const floatx4 *>(ws + erow_w * kScratchPitch + ec0 + 4 * q);
+        v[4 * q] = c4[0]; v[4 * q + 1] = c4[1]; v[4 * q + 2] = c4[2]; v[4 * q + 3] = c4[3];
+      }
+      const int col0 = (cb0 + j) * kBlockCols + ec0;
+#pragma unroll
+      for (int i = 0; i < kSegV; ++i) {
+        float u[kPer];
+        unpack16(ur.u[i], (T *)nullptr, u);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) v[i * kPer + q] += u[q];  // v = acc + u
+      }
+      if constexpr (!kVerify) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) bm = fmaxf(bm, (kMask && col0 + c >= V) ? -INFINITY : v[c]);
+        const float mn = fmaxf(run_m, bm);
+        if (!kMask || mn != -INFINITY) {
+          // exp(z - z_max) = 2^((v - v_max) log2(e) / T): v - v_max keeps the
+          // precision of the terms near the maximum
+          float sb = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const float e = exp2_fast((v[c] - mn) * cl);
+            sb += (kMask && col0 + c >= V) ? 0.0f : e;
+          }
+          run_s = fmaf(run_s, exp2_fast((run_m - mn) * cl), sb);
+          run_m = mn;
+        }
+      } else {
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < kSegV; ++i) unpack16(ur.t[i], (T *)nullptr, t + i * kPer);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const float a = log2_prob(t[c], invT, mp, lp);  // log2 p
+          const float b = log2_prob(v[c], invT, mq, lq);  // log2 q
+          const float mn = exp2_fast(fminf(a, b));
+          const float pe = exp2_fast(a);
+          const bool in = !kMask || col0 + c < V;
+          run_min += in ? mn : 0.0f;
+          run_res += in ? pe - mn : 0.0f;
+        }
+      }
+    };
+    // ---- end of a tile: combine the lane pair of each row into the LDS
+    //      partial buffer, reset; every kFlushTiles tiles the buffer goes out
+    auto tile_end = [&](int tl) __attribute__((always_inline)) {
+      float2 o;
+      if constexpr (!kVerify) {
+        const float om = pair_swap(run_m), os = pair_swap(run_s);
+        const float M = fmaxf(run_m, om);
+        float S = 0.0f;
+        if (M != -INFINITY)
+          S = run_s * exp2_fast((run_m - M) * cl) + os * exp2_fast((om - M) * cl);
+        o = make_float2(M * invT, S);  // max z = (max of acc + u) / T, exactly
+        run_m = -INFINITY;
+        run_s = 0.0f;
+      } else {
+        o = make_float2(run_min + pair_swap(run_min), run_res + pair_swap(run_res));
+        run_min = run_res = 0.0f;
+      }
+      if ((lane & 1) == 0) pbuf[wave * 32 + erow_w][tl % kFlushTiles] = o;
+    };
+    auto flush = [&](int tl) __attribute__((always_inline)) {
+      __syncthreads();
+      const int n = tl % kFlushTiles + 1, ft = tile0 + tl + 1 - n;
+      for (int i = tid; i < kRowGroup * n; i += kBlock) {
+        const int row = i / n, t = i - row * n;
+        const int orow = pout[row];
+        if (orow >= 0) out[(int64_t)orow * n_tiles + ft + t] = pbuf[row][t];
+      }
+    };
+
+    // ---- pipeline: W2 of block j+1 goes to LDS during block j; loads run two
+    //      blocks ahead of their use
+    WRegs wr0, wr1;
+    URegs ur0, ur1;
+    __syncthreads();  // the previous range is done with both LDS stages
+    load_w(wr0, 0);
+    load_w(wr1, 1);
+    load_u(ur0, 0);
+    load_u(ur1, 1);
+    store_w(0, wr0);
+    load_w(wr0, 2);
+    // block j: `wnext` holds W2 of block j + 1 and is refilled with block j + 3;
+    // `ucur` holds U (P) of block j and is refilled with block j + 2
+    auto step = [&](int j, bool masked, WRegs &wnext, URegs &ucur) __attribute__((always_inline)) {
+      __syncthreads();  // block j in LDS stage j & 1; stage (j + 1) & 1 is free
+      if (!wave_live) {
+      } else if (masked) {
+        block(j, ucur, std::true_type{});
+      } else {
+        block(j, ucur, std::false_type{});
+      }
+      store_w((j + 1) & 1, wnext);
+      load_w(wnext, j + 3);
+      load_u(ucur, j + 2);
+    };
+    const bool mask_last = (int64_t)(tile0 + ntile) * kTileN > V;
+    for (int tl = 0; tl < ntile; ++tl) {
+      const bool masked = mask_last && tl == ntile - 1;
+      const int j = tl * kBlocksPerTile;
+      step(j, masked, wr1, ur0);
+      step(j + 1, masked, wr0, ur1);
+      step(j + 2, masked, wr1, ur0);
+      step(j + 3, masked, wr0, ur1);
+      tile_end(tl);
+      if (tl % kFlushTiles == kFlushTiles - 1 || tl == ntile - 1) flush(tl);
     }
-    smin = group_sum<kG>(smin);
-    sres = group_sum<kG>(sres);
-    const int i = mt * TM + erow;
-    if (e_cur.x >= 0 && (tid % kG) == 0)
-      p.pair_partials[(int64_t)i * p.n_tiles + nt] = make_float2(smin, sres);
-    if (more) {
-      store_a(buf ^ 1, a_next);
-      cur = nxt;
-    }
-    e_cur = e_next;
-    buf ^= 1;
   }
+  if (bad_entry) flag_error(p.err, kErrLength);
 }
 
-// Recompute z for one row and one vocabulary tile with the same matrix-core
-// sequence and epilogue arithmetic as bias_tile_kernel.  Called by all 256
-// threads; wave w produces columns 32w..32w+31 of the tile.  ldsArow holds
-// W1[prev] (r elements); the row sits at position `row_in_block` (= its row
-// index mod 32) of its 32-row block, which is where bias_tile_kernel computed
-// it.  Writes z (or -inf past V) to zout[0..127].
+// Workgroups of a stream_tile_kernel launch: at most two per compute unit,
+// each with the same number of (row group, tile) items.
+inline int stream_tile_grid(int total_items, int max_groups) {
+  if (total_items <= 0) return 1;
+  const int per = (total_items + max_groups - 1) / max_groups;
+  return (total_items + per - 1) / per;
+}
+
+// v = acc + U (before the temperature) of one row over one vocabulary tile,
+// formed by the same instruction sequence as stream_tile_kernel: the row's A
+// operand from LDS (ldsArow: r elements; every position of the 32-row block
+// reads it, and the row is taken from position row_in_block = its row index
+// mod 32, where stream_tile_kernel had it), W2 columns from global memory, K in
+// increasing order from a zero accumulator.  Called by all 256 threads; wave w
+// produces columns 32w..32w+31 of the tile.  Writes v (or -inf past V) to
+// vout[0..127].
 template <typename T>
-__device__ __forceinline__ void recompute_tile_z(const T *ldsArow, const T *W2, const T *Urow,
+__device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, const T *Urow,
                                                  int V, int r, int tile, int row_in_block,
-                                                 float invT, float *zout) {
+                                                 float *vout) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   BFrag<T> bfr;
   load_bfrag(W2, V, r, tile * kTileN + wave * 32, bfr);
@@ -544,9 +479,9 @@ __device__ __forceinline__ void recompute_tile_z(const T *ldsArow, const T *W2, 
     for (int e = 0; e < 16; ++e)
       if (e == reg) a = acc[0][e];
     const int col = tile * kTileN + wave * 32 + (lane & 31);
-    float z = -INFINITY;
-    if (col < V) z = (a + Elem<T>::at(Urow, col)) * invT;
-    zout[wave * 32 + (lane & 31)] = z;
+    float v = -INFINITY;
+    if (col < V) v = a + Elem<T>::at(Urow, col);
+    vout[wave * 32 + (lane & 31)] = v;
   }
 }
 

@@ -62,15 +62,28 @@ template <> struct Elem<bf16_t> {
 // 16 bytes of a stream that is read once (logit rows): a non-temporal load, so
 // it does not displace data that is re-read (the W2 factor) from the caches.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld_stream4(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ uint4 ld_stream(const void *p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  const u32x4 v = ld_stream4(p);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // e^x on the transcendental unit: 2^(x log2 e).  Every kernel uses this one
 // function, so equal arguments give equal results everywhere.
-__device__ __forceinline__ float fexp(float x) {
-  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// 2^x and log2(x) on the transcendental unit
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Order LDS accesses of the lanes of one wave (LDS executes a wave's accesses
+// in issue order; this keeps the compiler from reordering them).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ void flag_error(int32_t *err, int bits) {
@@ -266,7 +279,11 @@ __device__ __forceinline__ void load_bfrag(const float *W2, int V, int r, int b_
   }
 }
 
-template <int WMB>
+// KS > 0 fixes the number of K steps at compile time (r = 16 KS for bf16, 2 KS
+// for fp32: no branch between the matrix-core instructions, so the LDS reads
+// of later steps are issued early); KS = 0 takes r at run time.  Both forms
+// issue the same instructions in the same order for the same r.
+template <int WMB, int KS = 0>
 __device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_row0, int r,
                                          const BFrag<bf16_t> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -276,8 +293,8 @@ __device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < BFrag<bf16_t>::kSteps; ++ks) {
-    if (ks * 16 < r) {
+  for (int ks = 0; ks < (KS > 0 ? KS : BFrag<bf16_t>::kSteps); ++ks) {
+    if (KS > 0 || ks * 16 < r) {
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb) {
         const u16x8 a = *reinterpret_cast<const u16x8 *>(
@@ -288,7 +305,7 @@ __device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_
     }
   }
 }
-template <int WMB>
+template <int WMB, int KS = 0>
 __device__ __forceinline__ void mma_rows(const float *ldsA, int a_pitch, int a_row0, int r,
                                          const BFrag<float> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -298,8 +315,8 @@ __device__ __forceinline__ void mma_rows(const float *ldsA, int a_pitch, int a_r
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < BFrag<float>::kSteps; ++ks) {
-    if (ks * 2 < r) {
+  for (int ks = 0; ks < (KS > 0 ? KS : BFrag<float>::kSteps); ++ks) {
+    if (KS > 0 || ks * 2 < r) {
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb) {
         const float a = ldsA[(a_row0 + 32 * mb + (lane & 31)) * a_pitch + ks * 2 + kq];
@@ -317,6 +334,17 @@ __device__ __forceinline__ void unpack16(const uint4 &v, bf16_t *, float *out) {
     out[2 * i] = __uint_as_float(w[i] << 16);
     out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
+}
+__device__ __forceinline__ void unpack16(const u32x4 &v, bf16_t *, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(v[i] << 16);
+    out[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const u32x4 &v, float *, float *out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
 }
 __device__ __forceinline__ void unpack16(const uint4 &v, float *, float *out) {
   out[0] = __uint_as_float(v.x);

@@ -113,8 +113,9 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   // 3. recompute z of that tile, bit-identical to the fused kernel
   __syncthreads();
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
-  recompute_tile_z<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
-                      p.invT, zbuf);
+  recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31, zbuf);
+  __syncthreads();
+  if (tid < kTileN) zbuf[tid] *= p.invT;  // z = (acc + u) / T, the draft's exact arithmetic
   __syncthreads();
 
   // 4. scan inside the tile (wave 0, two columns per lane, left to right)
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, in
   if (lane == 0) sh[slot] = acc;
 }
 
-template <typename T, int TM>
+template <typename T, int KS>
 static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   const int n_tiles = (L.V + kTileN - 1) / kTileN;
   BiasTileParams bp{};
@@ -235,9 +236,9 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
                 gather_rows_kernel<T><<<(L.R + 7) / 8, kBlock, 0, stream>>>(
                     L.R, L.V, L.r, reinterpret_cast<const T *>(L.W1), L.x0,
                     reinterpret_cast<T *>(A[0]), L.err));
-  // x: vocabulary tiles; one workgroup walks every row tile of its vocabulary
-  // tile with the same W2 columns in registers, so W2 crosses HBM once a step
-  const dim3 grid(n_tiles, 1);
+  // row groups of 128 requests x vocabulary tiles, in equal contiguous ranges
+  const int n_items = (L.R + kRowGroup - 1) / kRowGroup * n_tiles;
+  const int grid = L.R > kRowGroup ? 2 * kComputeUnits : stream_tile_grid(n_items, 2 * kComputeUnits);
   for (int k = 1; k <= L.gamma; ++k) {
     bp.k = k;
     bp.A = A[(k - 1) & 1];
@@ -245,20 +246,20 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     sp.A_cur = A[(k - 1) & 1];
     sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
     DSPARK_LAUNCH("bias_tile_draft", stream,
-                  draft_tile_kernel<T><<<grid, kBlock, 0, stream>>>(bp));
+                  stream_tile_kernel<T, Epi::kDraft, KS><<<grid, kBlock, 0, stream>>>(bp));
     DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp));
   }
   return hipGetLastError();
 }
 
 hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream) {
-  const int tm = tile_rows_for(L.R);
+  // the full rank gets a product with its K steps fixed at compile time
   if (L.bf16) {
-    if (tm == 64) return launch_draft_t<bf16_t, 64>(L, stream);
-    return launch_draft_t<bf16_t, 32>(L, stream);
+    if (L.r == kMaxRank) return launch_draft_t<bf16_t, kMaxRank / 16>(L, stream);
+    return launch_draft_t<bf16_t, 0>(L, stream);
   }
-  if (tm == 64) return launch_draft_t<float, 64>(L, stream);
-  return launch_draft_t<float, 32>(L, stream);
+  if (L.r == 128) return launch_draft_t<float, 64>(L, stream);
+  return launch_draft_t<float, 0>(L, stream);
 }
 
 }  // namespace dspark

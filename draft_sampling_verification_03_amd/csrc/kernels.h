@@ -8,11 +8,11 @@
 
 namespace dspark {
 
-// rows per bias tile for an M-row product (64-row tiles fit the register file
-// without spills next to the resident W2 columns and the prefetched U)
-inline int tile_rows_for(int M) { return M > 32 ? 64 : 32; }
+constexpr int kComputeUnits = 256;  // MI355X
 
-constexpr size_t kWsHeader = 256;  // sticky error word lives at the start of every workspace
+// bytes 0..3 of every workspace hold the sticky error word; bytes 128..255 are
+// a write-only sink for lanes that have no output
+constexpr size_t kWsHeader = 256;
 
 struct DraftLaunch {
   int R, gamma, V, r, d;

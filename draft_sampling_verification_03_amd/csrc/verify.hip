@@ -6,7 +6,7 @@
 //  1. row_chunk_stats_kernel: one HBM pass over the sum(1 + ell) target rows,
 //     (max, sum exp) per quarter row; the last row of every request (its bonus
 //     position) also keeps per-tile partials for sampling.
-//  2. bias_tile_kernel<Verify>: recompute z_k of every verified draft with the
+//  2. tile_kernel<Verify>: recompute z_k of every verified draft with the
 //     draft's arithmetic, stream U_k and P_k once, emit per-tile
 //     (sum min(p, q), sum (p - q)_+).
 //  3. verify_finalize_kernel: one workgroup per request: c*_k, the accept
@@ -346,19 +346,20 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
             *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * p.r + tid * (16 / sizeof(T)));
       __syncthreads();
       const T *Urow = reinterpret_cast<const T *>(p.U) + ((int64_t)rho * gamma + j - 1) * V;
-      recompute_tile_z<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
-                          (int)((d_off + j - 1) & 31), p.invT, zbuf);
+      recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
+                          (int)((d_off + j - 1) & 31), zbuf);
       __syncthreads();
       if (tid < kTileN) {
+        // (p - q)_+ = p - min(p, q), each term formed as in the verify pass
         const int64_t qi = (int64_t)rho * gamma + j - 1;
-        const float mq = p.q_stats[2 * qi], rq = 1.0f / p.q_stats[2 * qi + 1];
-        const float mp = ps.x, rp = 1.0f / ps.y;
+        const float mq = p.q_stats[2 * qi], lq = log2_fast(p.q_stats[2 * qi + 1]);
+        const float lp = log2_fast(ps.y);
         const int col = tstar * kTileN + tid;
         float e = 0.0f;
         if (col < V) {
-          const float qv = fexp(zbuf[tid] - mq) * rq;
-          const float pv = fexp(Elem<T>::at(Prow, col) * p.invT - mp) * rp;
-          e = fmaxf(pv - qv, 0.0f);
+          const float a = log2_prob(Elem<T>::at(Prow, col), p.invT, ps.x, lp);
+          const float b = log2_prob(zbuf[tid], p.invT, mq, lq);
+          e = exp2_fast(a) - exp2_fast(fminf(a, b));
         }
         ebuf[tid] = e;
       }
@@ -440,12 +441,17 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   bp.P = L.P; bp.p_chunks = L.p_chunks; bp.q_stats = L.q_stats; bp.pair_partials = L.pair_partials;
   bp.row_map = L.row_map;
   bp.A = L.A_rows;
-  // the number of verified drafts lives on the device: every workgroup walks
-  // the row tiles of its group (y) up to sum(ell) with its W2 columns resident;
-  // 64-row tiles leave room in registers for the prefetched U and P segments
-  const int max_mt = (L.R * L.gamma + 31) / 32;
-  DSPARK_LAUNCH("bias_tile_verify", stream,
-                verify_tile_kernel<T><<<dim3(nT, max_mt < 2 ? max_mt : 2), kBlock, 0, stream>>>(bp));
+  // the number of verified drafts lives on the device: each workgroup takes an
+  // equal share of the (row group, tile) items it finds there
+  const int grid = 2 * kComputeUnits;
+  if (L.r == (L.bf16 ? kMaxRank : 128)) {
+    DSPARK_LAUNCH("bias_tile_verify", stream,
+                  (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64>
+                   <<<grid, kBlock, 0, stream>>>(bp)));
+  } else {
+    DSPARK_LAUNCH("bias_tile_verify", stream,
+                  (stream_tile_kernel<T, Epi::kVerify, 0><<<grid, kBlock, 0, stream>>>(bp)));
+  }
 
   FinalizeParams fp{};
   fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT;
