@@ -88,7 +88,7 @@ enum class Epi { kDraft, kVerify };
 // (loads past the range are clamped, stores of lanes without an output go to
 // a sink), so every wait the compiler inserts counts exactly the loads it
 // needs.
-constexpr int kRowGroup = 128;                          // rows per workgroup
+constexpr int kRowsPerWave = 32;                        // product rows of one wave
 constexpr int kBlockCols = 32;                          // W2 columns per block
 constexpr int kBlocksPerTile = kTileN / kBlockCols;     // 4
 constexpr int kColPieces = kMaxRank * 2 / 16;           // 16-byte pieces per W2 column (max)
@@ -192,14 +192,19 @@ __device__ __forceinline__ float log2_prob(float x, float invT, float m, float l
   return fmaf(fmaf(x, invT, -m), kLog2e, -log2S);
 }
 
-template <typename T, Epi E, int KS>
-__global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p) {
+// NW waves per workgroup (a row group of 32 NW product rows); one workgroup
+// per compute unit.
+template <typename T, Epi E, int KS, int NW>
+__global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTileParams p) {
   constexpr bool kVerify = E == Epi::kVerify;
+  constexpr int kThreads = NW * kWave;
+  constexpr int kRowGroup = NW * kRowsPerWave;
   constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int kSegV = 16 / kPer;            // pieces per 16-column row segment
-  constexpr int kWPieces = kColPieces / 8;     // W2 pieces per thread per block (4)
+  constexpr int kTpc = kThreads / kBlockCols;  // threads per W2 column of a block
+  constexpr int kWPieces = kColPieces / kTpc;  // W2 pieces per thread per block
   __shared__ __align__(16) unsigned char w2s[2][kStageBytes];
-  __shared__ __align__(16) float scratch[4][32 * kScratchPitch];
+  __shared__ __align__(16) float scratch[NW][32 * kScratchPitch];
   __shared__ float2 pbuf[kRowGroup][kFlushTiles];  // partials of the last tiles, by row
   __shared__ int pout[kRowGroup];                  // output row of each row, -1 for none
 
@@ -216,20 +221,10 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
   }
   if (n_rows <= 0) return;
   const int n_rg = (n_rows + kRowGroup - 1) / kRowGroup;
-  // Work: (row group, vocabulary tile) items.  With several row groups and a
-  // grid of 8 * q workgroups, the n_rg workgroups that share a range of tiles
-  // get the same XCD (workgroups are dealt to the 8 XCDs round robin), start
-  // together and walk the same W2 blocks, so W2 comes from that XCD's L2 after
-  // the first of them.  Otherwise: equal contiguous ranges, row-group major.
+  // Work: (row group, vocabulary tile) items in equal contiguous ranges,
+  // row-group major; one workgroup per compute unit.
   int t0, t1;
-  const int q8 = (int)gridDim.x / 8, cpx = n_rg > 1 && ((int)gridDim.x & 7) == 0 ? q8 / n_rg : 0;
-  if (cpx > 0) {
-    const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int rg = q % n_rg, cx = q / n_rg, n_cr = cpx * 8, c = cx * 8 + x;
-    if (cx >= cpx) return;
-    t0 = rg * n_tiles + (int)((int64_t)c * n_tiles / n_cr);
-    t1 = rg * n_tiles + (int)((int64_t)(c + 1) * n_tiles / n_cr);
-  } else {
+  {
     const int total = n_rg * n_tiles;
     const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
     t0 = (int)blockIdx.x * per;
@@ -290,22 +285,22 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
     // native vectors, so that the stages stay in registers
     struct WRegs { u32x4 w[kWPieces]; };
     struct URegs { u32x4 u[kSegV]; u32x4 t[kVerify ? kSegV : 1]; };
-    // W2 pieces of a block: thread t takes column t / 8 and pieces
-    // (t % 8) + 8 i, i < 4 (pieces past the column's npieces repeat its last)
-    const int wc = tid >> 3, wp = tid & 7;
+    // W2 pieces of a block: thread t takes column t / kTpc and pieces
+    // (t % kTpc) + kTpc i (pieces past the column's npieces repeat its last)
+    const int wc = tid / kTpc, wp = tid % kTpc;
     auto load_w = [&](WRegs &wr, int j) __attribute__((always_inline)) {
       const int col = min((cb0 + min(j, nblk - 1)) * kBlockCols + wc, V - 1);
       const T *src = W2 + (int64_t)col * r;
 #pragma unroll
       for (int i = 0; i < kWPieces; ++i)
-        wr.w[i] = *reinterpret_cast<const u32x4 *>(src + min(wp + 8 * i, npieces - 1) * kPer);
+        wr.w[i] = *reinterpret_cast<const u32x4 *>(src + min(wp + kTpc * i, npieces - 1) * kPer);
     };
     auto store_w = [&](int stage, const WRegs &wr) __attribute__((always_inline)) {
       unsigned char *dst = w2s[stage] + 16 * w2_slot(wc, wp);
 #pragma unroll
       for (int i = 0; i < kWPieces; ++i)
-        if (KS > 0 ? 8 * i < npieces : wp + 8 * i < npieces)
-          *reinterpret_cast<u32x4 *>(dst + 16 * 8 * i) = wr.w[i];
+        if (KS > 0 ? kTpc * i < npieces : wp + kTpc * i < npieces)
+          *reinterpret_cast<u32x4 *>(dst + 16 * kTpc * i) = wr.w[i];
     };
     auto load_u = [&](URegs &ur, int j) __attribute__((always_inline)) {
       const int cb = cb0 + min(j, nblk - 1);
@@ -400,7 +395,7 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
     auto flush = [&](int tl) __attribute__((always_inline)) {
       __syncthreads();
       const int n = tl % kFlushTiles + 1, ft = tile0 + tl + 1 - n;
-      for (int i = tid; i < kRowGroup * n; i += kBlock) {
+      for (int i = tid; i < kRowGroup * n; i += kThreads) {
         const int row = i / n, t = i - row * n;
         const int orow = pout[row];
         if (orow >= 0) out[(int64_t)orow * n_tiles + ft + t] = pbuf[row][t];
@@ -409,6 +404,9 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
 
     // ---- pipeline: W2 of block j+1 goes to LDS during block j; loads run two
     //      blocks ahead of their use
+    // two register sets each: W2 of block j + 1 goes to LDS during block j and
+    // its set is refilled with block j + 3; U (P) of block j is used in block j
+    // and its set refilled with block j + 2
     WRegs wr0, wr1;
     URegs ur0, ur1;
     __syncthreads();  // the previous range is done with both LDS stages
@@ -418,8 +416,6 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
     load_u(ur1, 1);
     store_w(0, wr0);
     load_w(wr0, 2);
-    // block j: `wnext` holds W2 of block j + 1 and is refilled with block j + 3;
-    // `ucur` holds U (P) of block j and is refilled with block j + 2
     auto step = [&](int j, bool masked, WRegs &wnext, URegs &ucur) __attribute__((always_inline)) {
       __syncthreads();  // block j in LDS stage j & 1; stage (j + 1) & 1 is free
       if (!wave_live) {
@@ -447,8 +443,8 @@ __global__ __launch_bounds__(kBlock, 2) void stream_tile_kernel(BiasTileParams p
   if (bad_entry) flag_error(p.err, kErrLength);
 }
 
-// Workgroups of a stream_tile_kernel launch: at most two per compute unit,
-// each with the same number of (row group, tile) items.
+// Workgroups of a stream_tile_kernel launch: at most max_groups (one per
+// compute unit), each with the same number of (row group, tile) items.
 inline int stream_tile_grid(int total_items, int max_groups) {
   if (total_items <= 0) return 1;
   const int per = (total_items + max_groups - 1) / max_groups;

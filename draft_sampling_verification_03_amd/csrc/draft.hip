@@ -236,17 +236,24 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
                 gather_rows_kernel<T><<<(L.R + 7) / 8, kBlock, 0, stream>>>(
                     L.R, L.V, L.r, reinterpret_cast<const T *>(L.W1), L.x0,
                     reinterpret_cast<T *>(A[0]), L.err));
-  // row groups of 128 requests x vocabulary tiles, in equal contiguous ranges
-  const int n_items = (L.R + kRowGroup - 1) / kRowGroup * n_tiles;
-  const int grid = L.R > kRowGroup ? 2 * kComputeUnits : stream_tile_grid(n_items, 2 * kComputeUnits);
+  // row groups of 32 NW requests x vocabulary tiles, in equal contiguous ranges
+  // over one workgroup per compute unit: 4 waves up to 128 requests, else 8
+  const bool wide = L.R > 4 * kRowsPerWave;
+  const int n_items = (L.R + (wide ? 8 : 4) * kRowsPerWave - 1) / ((wide ? 8 : 4) * kRowsPerWave) * n_tiles;
+  const int grid = stream_tile_grid(n_items, kComputeUnits);
   for (int k = 1; k <= L.gamma; ++k) {
     bp.k = k;
     bp.A = A[(k - 1) & 1];
     sp.k = k;
     sp.A_cur = A[(k - 1) & 1];
     sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
-    DSPARK_LAUNCH("bias_tile_draft", stream,
-                  stream_tile_kernel<T, Epi::kDraft, KS><<<grid, kBlock, 0, stream>>>(bp));
+    if (wide) {
+      DSPARK_LAUNCH("bias_tile_draft", stream,
+                    (stream_tile_kernel<T, Epi::kDraft, KS, 8><<<grid, 8 * kWave, 0, stream>>>(bp)));
+    } else {
+      DSPARK_LAUNCH("bias_tile_draft", stream,
+                    (stream_tile_kernel<T, Epi::kDraft, KS, 4><<<grid, 4 * kWave, 0, stream>>>(bp)));
+    }
     DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp));
   }
   return hipGetLastError();
