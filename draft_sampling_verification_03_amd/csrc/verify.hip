@@ -36,133 +36,148 @@ struct RowStatsParams {
   void *A_rows;               // [R*gamma][r]: W1[x_{k-1}] of compact row i
 };
 
-__device__ __forceinline__ void online_merge(float &M, float &S, float m, float s) {
-  if (m > M) {
-    S = S * fexp(M - m) + s;
-    M = m;
-  } else if (m != -INFINITY) {
-    S += s * fexp(m - M);
-  }
-}
-
+// One quarter of one row per workgroup, in rounds of kBatch 16-byte pieces per
+// thread (all in flight together; few registers, so many workgroups share a
+// compute unit).  The request lookup of the row runs while the first round's
+// loads are outstanding.  Per round:
+//   - a verified-draft row: max and sum of exp over the thread's elements in
+//     two passes, then one workgroup reduction;
+//   - the last row of a request (its bonus position): (max, sum of exp) per
+//     128-column tile as well, kept for the bonus draw.
+// exp(x / T - m) is formed as 2^((x - x_max) log2(e) / T), with m = x_max / T
+// exactly (T > 0).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams p) {
   __shared__ float red[8];
+  constexpr int kPer = Elem<T>::kPerVec;
+  constexpr int kBatch = 4;                  // pieces per thread per round
+  constexpr int kG = kTileN / kPer;          // threads per tile (bf16: 16, fp32: 32)
   const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int V = p.V, nT = p.n_tiles;
-  int rho = -1;
+  int used = p.n_rows;
   if (p.row_offset != nullptr) {
-    int used = p.row_offset[p.R];
+    used = p.row_offset[p.R];
     if (used > p.n_rows) {
       if (row == 0 && c == 0 && tid == 0) flag_error(p.err, kErrLength);
       used = p.n_rows;
     }
-    if (row >= used) return;
-    int lo = 0, hi = p.R;  // request of the row: the last rho with row_offset[rho] <= row
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
-    }
-    const int base = p.row_offset[lo];
-    if (p.row_offset[lo + 1] - 1 == row) {
-      rho = lo;  // the last row of its request: the bonus position keeps tile partials
-    } else if (c == 0 && tid < 32) {
-      // a verified draft (k <= ell): its entry of the compact-row map and its
-      // transition row W1[x_{k-1}] for the verify pass
-      const int k = row - base + 1, i = row - lo;
-      if (k >= 1 && k <= p.gamma && i >= 0 && i < p.R * p.gamma) {
-        int prev = k == 1 ? p.x0[lo] : p.x[(int64_t)lo * p.gamma + k - 2];
-        if (prev < 0 || prev >= V) {
-          if (tid == 0) flag_error(p.err, kErrToken);
-          prev = prev < 0 ? 0 : V - 1;
-        }
-        if (tid == 0) p.row_map[i] = make_int4(lo, k, prev, row);
-        constexpr int kPerA = 16 / (int)sizeof(T);
-        if (tid < p.r * (int)sizeof(T) / 16)
-          *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r + tid * kPerA) =
-              *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
-                                               (int64_t)prev * p.r + tid * kPerA);
-      } else if (tid == 0) {
-        flag_error(p.err, kErrLength);
-      }
-    }
   }
+  if (row >= used) return;
   const int tpc = (nT + kChunks - 1) / kChunks;
   const int tb = min(c * tpc, nT), te = min(tb + tpc, nT);
   const int vb = tb * kTileN, ve = min(te * kTileN, V);
-  const T *X = reinterpret_cast<const T *>(p.X) + (int64_t)row * V;
-  constexpr int kPer = Elem<T>::kPerVec;
-  float M = -INFINITY, S = 0.0f;
+  const int npc = (ve - vb + kPer - 1) / kPer;  // pieces in the chunk (V % kPer == 0)
+  const T *X = reinterpret_cast<const T *>(p.X) + (int64_t)row * V + vb;
+  const float cl = p.invT * kLog2e;
 
-  if (rho < 0) {
-    // online statistics, eight 16-byte loads in flight per thread
-    constexpr int kUnroll = 8;
-    for (int v0 = vb + tid * kPer; v0 < ve; v0 += kBlock * kPer * kUnroll) {
-      float x[kUnroll][kPer];
+  float M = -INFINITY, S = 0.0f;  // running (max of x, sum of 2^((x - M) cl))
+  int rho = -1;                   // set for the last row of a request
+  bool looked_up = false;
+  for (int p0 = 0; p0 < npc; p0 += kBatch * kBlock) {
+    u32x4 raw[kBatch];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int v = v0 + u * kBlock * kPer;
-        if (v < ve) {
-          Elem<T>::vec(X, v, x[u]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < kPer; ++q) x[u][q] = -INFINITY;
+    for (int j = 0; j < kBatch; ++j)
+      raw[j] = ld_stream4(X + (int64_t)min(p0 + j * kBlock + tid, npc - 1) * kPer);
+    if (!looked_up) {
+      looked_up = true;
+      if (p.row_offset != nullptr) {
+        // request of the row: the last rho with row_offset[rho] <= row
+        int lo = 0, hi = p.R;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
         }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float lm = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          if (x[u][q] != -INFINITY) x[u][q] *= p.invT;
-          lm = fmaxf(lm, x[u][q]);
+        const int base = p.row_offset[lo];
+        if (p.row_offset[lo + 1] - 1 == row) {
+          rho = lo;  // the bonus position keeps tile partials
+        } else if (c == 0 && tid < 32) {
+          // a verified draft (k <= ell): its entry of the compact-row map and
+          // its transition row W1[x_{k-1}] for the verify pass
+          const int k = row - base + 1, i = row - lo;
+          if (k >= 1 && k <= p.gamma && i >= 0 && i < p.R * p.gamma) {
+            int prev = k == 1 ? p.x0[lo] : p.x[(int64_t)lo * p.gamma + k - 2];
+            if (prev < 0 || prev >= V) {
+              if (tid == 0) flag_error(p.err, kErrToken);
+              prev = prev < 0 ? 0 : V - 1;
+            }
+            if (tid == 0) p.row_map[i] = make_int4(lo, k, prev, row);
+            constexpr int kPerA = 16 / (int)sizeof(T);
+            if (tid < p.r * (int)sizeof(T) / 16)
+              *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r +
+                                         tid * kPerA) =
+                  *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
+                                                   (int64_t)prev * p.r + tid * kPerA);
+          } else if (tid == 0) {
+            flag_error(p.err, kErrLength);
+          }
         }
-        if (lm == -INFINITY) continue;
-        if (lm > M) {
-          S = S * fexp(M - lm);
-          M = lm;
-        }
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) S += fexp(x[u][q] - M);
       }
     }
-  } else {
-    // per-tile partials (kept for the bonus draw), merged into the chunk
-    constexpr int kG = kTileN / kPer;              // threads per tile
-    constexpr int kTilesPerIt = kBlock / kG;
-    for (int t0 = tb; t0 < te; t0 += kTilesPerIt) {
-      const int t = t0 + tid / kG;
-      const int v = t * kTileN + (tid % kG) * kPer;
-      float x[kPer];
-      if (t < te && v < V) {
-        Elem<T>::vec(X, v, x);
+    if (rho < 0) {
+      float bm = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) x[q] *= p.invT;
-      } else {
+      for (int j = 0; j < kBatch; ++j) {
+        float x[kPer];
+        unpack16(raw[j], (T *)nullptr, x);
+        const bool in = p0 + j * kBlock + tid < npc;
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) x[q] = -INFINITY;
+        for (int q = 0; q < kPer; ++q) bm = fmaxf(bm, in ? x[q] : -INFINITY);
       }
-      float lm = -INFINITY;
+      if (bm != -INFINITY) {
+        const float mn = fmaxf(M, bm);
+        float sb = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) lm = fmaxf(lm, x[q]);
-      const float mt = group_max<kG>(lm);
-      float ls = 0.0f;
-      if (mt != -INFINITY) {
+        for (int j = 0; j < kBatch; ++j) {
+          float x[kPer];
+          unpack16(raw[j], (T *)nullptr, x);
+          const bool in = p0 + j * kBlock + tid < npc;
+          float e = 0.0f;
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) ls += fexp(x[q] - mt);
+          for (int q = 0; q < kPer; ++q) e += exp2_fast((x[q] - mn) * cl);
+          sb += in ? e : 0.0f;
+        }
+        S = fmaf(S, exp2_fast((M - mn) * cl), sb);
+        M = mn;
       }
-      const float st = group_sum<kG>(ls);
-      if (t < te && (tid % kG) == 0) {
-        p.bonus_tiles[(int64_t)rho * nT + t] = make_float2(mt, st);
-        online_merge(M, S, mt, st);
+    } else {
+      // tile of piece (p0 + j kBlock + tid): kG consecutive threads share one
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int pc = p0 + j * kBlock + tid;
+        const bool in = pc < npc;
+        if (p0 + j * kBlock >= npc) continue;  // uniform: no piece of this round left
+        float x[kPer];
+        unpack16(raw[j], (T *)nullptr, x);
+        float lm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) lm = fmaxf(lm, in ? x[q] : -INFINITY);
+        const float mt = group_max<kG>(lm);
+        float ls = 0.0f;
+        if (in) {
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) ls += exp2_fast((x[q] - mt) * cl);
+        }
+        const float st = group_sum<kG>(ls);
+        const int t = tb + pc / kG;
+        if (in && (tid % kG) == 0) {
+          p.bonus_tiles[(int64_t)rho * nT + t] = make_float2(mt * p.invT, st);
+          if (mt > M) {
+            S = S * exp2_fast((M - mt) * cl) + st;
+            M = mt;
+          } else {
+            S += st * exp2_fast((mt - M) * cl);
+          }
+        }
       }
     }
   }
-  const float m = block_max(M, red);
-  const float s = block_sum(M == -INFINITY ? 0.0f : S * fexp(M - m), red);
+  // workgroup (max, sum): x-units, then m = x_max / T
+  const float mx = block_max(M, red);
+  const float sx = block_sum(M == -INFINITY ? 0.0f : S * exp2_fast((M - mx) * cl), red);
   if (tid == 0) {
-    p.chunks[(int64_t)row * kChunks + c] = make_float2(m, s);
-    if (vb < ve && !(isfinite(m) && isfinite(s))) flag_error(p.err, kErrNonFinite);
+    const float m = mx * p.invT;
+    p.chunks[(int64_t)row * kChunks + c] = make_float2(m, sx);
+    if (vb < ve && !(isfinite(m) && isfinite(sx))) flag_error(p.err, kErrNonFinite);
   }
 }
 
