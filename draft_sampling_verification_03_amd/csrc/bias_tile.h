@@ -308,8 +308,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
 #pragma unroll
       for (int i = 0; i < kSegV; ++i) {
         const int col = min(cb * kBlockCols + ec0 + i * kPer, V - kPer);
-        ur.u[i] = ld_stream4(Urow + col);
-        if constexpr (kVerify) ur.t[i] = ld_stream4(Prow + col);
+        // plain loads: a 128-byte line serves two consecutive blocks of a row,
+        // so it must stay in L2 until the next block's load
+        ur.u[i] = *reinterpret_cast<const u32x4 *>(Urow + col);
+        if constexpr (kVerify) ur.t[i] = *reinterpret_cast<const u32x4 *>(Prow + col);
       }
     };
 
