@@ -192,13 +192,14 @@ __device__ __forceinline__ float log2_prob(float x, float invT, float m, float l
   return fmaf(fmaf(x, invT, -m), kLog2e, -log2S);
 }
 
-// NW waves per workgroup (a row group of 32 NW product rows); one workgroup
-// per compute unit.
-template <typename T, Epi E, int KS, int NW>
+// NW waves per workgroup, each with RB blocks of 32 product rows: a row group
+// of 32 NW RB rows shares every W2 block it loads.  One workgroup per compute
+// unit (a wave may use up to 512 registers).
+template <typename T, Epi E, int KS, int NW, int RB>
 __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTileParams p) {
   constexpr bool kVerify = E == Epi::kVerify;
   constexpr int kThreads = NW * kWave;
-  constexpr int kRowGroup = NW * kRowsPerWave;
+  constexpr int kRowGroup = NW * RB * kRowsPerWave;
   constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int kSegV = 16 / kPer;            // pieces per 16-column row segment
   constexpr int kTpc = kThreads / kBlockCols;  // threads per W2 column of a block
@@ -236,9 +237,19 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
   const T *U = reinterpret_cast<const T *>(p.U);
   const T *P = reinterpret_cast<const T *>(p.P);
   float *ws = scratch[wave];
-  const int erow_w = lane >> 1;          // epilogue row within the wave
+  const int erow_w = lane >> 1;          // epilogue row within a 32-row block
   const int ec0 = (lane & 1) * 16;       // first epilogue column within the block
   bool bad_entry = false;
+
+  // per row block of this wave: block b = rb * NW + wave of the row group
+  struct RowState {
+    bool live, wave_live;
+    int slot;                  // row of the group, for pbuf and pout
+    const T *Urow, *Prow;
+    float mq, lq, mp, lp;      // (m, log2 S) of q and p (verify)
+    float run_m, run_s;        // draft: max of acc + u, sum of exp over the tile
+    float run_min, run_res;    // verify: sum min(p, q), sum (p - q)_+
+  };
 
   while (t0 < t1) {
     __syncthreads();  // the previous range's flush is done with pbuf and pout
@@ -248,43 +259,50 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
     const int nblk = ntile * kBlocksPerTile;
     const int cb0 = tile0 * kBlocksPerTile;  // first column block
 
-    // ---- the wave's A rows (product row = lane % 32 of the wave's 32)
-    AFrag<T> af;
-    load_afrag(Ab, r, min(rg * kRowGroup + wave * 32 + (lane & 31), n_rows - 1), af, KS);
-
-    // ---- this lane's epilogue row: source rows and statistics
-    const int erow = rg * kRowGroup + wave * 32 + erow_w;
-    bool live = erow < n_rows;
-    int rho = 0, k = 1, prow = 0;
-    if constexpr (kVerify) {
-      const int4 e = p.row_map[live ? erow : 0];  // written by the target-row statistics pass
-      const bool bad = e.x < 0 || e.x >= p.R || e.y < 1 || e.y > p.gamma || e.w < 0 ||
-                       e.w >= p.rows_capacity;
-      bad_entry |= live && bad;
-      live = live && !bad;
-      if (live) { rho = e.x; k = e.y; prow = e.w; }
-    } else {
-      if (live) { rho = erow; k = p.k; }
+    AFrag<T> af[RB];
+    RowState rs[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rbase = rg * kRowGroup + (rb * NW + wave) * kRowsPerWave;
+      // the A rows (product row = lane % 32 of the block)
+      load_afrag(Ab, r, min(rbase + (lane & 31), n_rows - 1), af[rb], KS);
+      // this lane's epilogue row: source rows and statistics
+      RowState &s = rs[rb];
+      const int erow = rbase + erow_w;
+      s.slot = (rb * NW + wave) * kRowsPerWave + erow_w;
+      s.live = erow < n_rows;
+      s.wave_live = rbase < n_rows;  // uniform per wave
+      int rho = 0, k = 1, prow = 0;
+      if constexpr (kVerify) {
+        const int4 e = p.row_map[s.live ? erow : 0];  // written by the target-row statistics pass
+        const bool bad = e.x < 0 || e.x >= p.R || e.y < 1 || e.y > p.gamma || e.w < 0 ||
+                         e.w >= p.rows_capacity;
+        bad_entry |= s.live && bad;
+        s.live = s.live && !bad;
+        if (s.live) { rho = e.x; k = e.y; prow = e.w; }
+      } else {
+        if (s.live) { rho = erow; k = p.k; }
+      }
+      if ((lane & 1) == 0) pout[s.slot] = s.live ? erow : -1;
+      s.Urow = U + ((int64_t)rho * p.gamma + (k - 1)) * V;
+      s.Prow = P + (int64_t)prow * V;
+      s.mq = s.lq = s.mp = s.lp = 0.0f;
+      if constexpr (kVerify) {
+        const int64_t qi = (int64_t)rho * p.gamma + k - 1;
+        s.mq = p.q_stats[2 * qi];
+        s.lq = log2_fast(p.q_stats[2 * qi + 1]);
+        const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)prow * kChunks);
+        s.mp = ps.x;
+        s.lp = log2_fast(ps.y);
+      }
+      s.run_m = -INFINITY;
+      s.run_s = s.run_min = s.run_res = 0.0f;
     }
-    if ((lane & 1) == 0) pout[wave * 32 + erow_w] = live ? erow : -1;
-    const bool wave_live = rg * kRowGroup + wave * 32 < n_rows;  // uniform per wave
-    const T *Urow = U + ((int64_t)rho * p.gamma + (k - 1)) * V;
-    const T *Prow = P + (int64_t)prow * V;
-    float mq = 0.0f, lq = 0.0f, mp = 0.0f, lp = 0.0f;  // (m, log2 S) of q and p
-    if constexpr (kVerify) {
-      const int64_t qi = (int64_t)rho * p.gamma + k - 1;
-      mq = p.q_stats[2 * qi];
-      lq = log2_fast(p.q_stats[2 * qi + 1]);
-      const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)prow * kChunks);
-      mp = ps.x;
-      lp = log2_fast(ps.y);
-    }
-    float2 *out = kVerify ? p.pair_partials : p.tile_stats;
 
     // ---- loads of block j (clamped past the range)
     // native vectors, so that the stages stay in registers
     struct WRegs { u32x4 w[kWPieces]; };
-    struct URegs { u32x4 u[kSegV]; u32x4 t[kVerify ? kSegV : 1]; };
+    struct URegs { u32x4 u[RB][kSegV]; u32x4 t[RB][kVerify ? kSegV : 1]; };
     // W2 pieces of a block: thread t takes column t / kTpc and pieces
     // (t % kTpc) + kTpc i (pieces past the column's npieces repeat its last)
     const int wc = tid / kTpc, wp = tid % kTpc;
@@ -304,49 +322,50 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
     };
     auto load_u = [&](URegs &ur, int j) __attribute__((always_inline)) {
       const int cb = cb0 + min(j, nblk - 1);
-      // a 16-byte piece is all in or all out of [0, V) (V % 8 == 0)
+      // a 16-byte piece is all in or all out of [0, V) (V % 8 == 0).  Plain
+      // loads: a 128-byte line serves two consecutive blocks of a row, so it
+      // must stay in L2 until the next block's load.
 #pragma unroll
-      for (int i = 0; i < kSegV; ++i) {
-        const int col = min(cb * kBlockCols + ec0 + i * kPer, V - kPer);
-        // plain loads: a 128-byte line serves two consecutive blocks of a row,
-        // so it must stay in L2 until the next block's load
-        ur.u[i] = *reinterpret_cast<const u32x4 *>(Urow + col);
-        if constexpr (kVerify) ur.t[i] = *reinterpret_cast<const u32x4 *>(Prow + col);
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < kSegV; ++i) {
+          const int col = min(cb * kBlockCols + ec0 + i * kPer, V - kPer);
+          ur.u[rb][i] = *reinterpret_cast<const u32x4 *>(rs[rb].Urow + col);
+          if constexpr (kVerify) ur.t[rb][i] = *reinterpret_cast<const u32x4 *>(rs[rb].Prow + col);
+        }
     };
 
-    // running sums of the current tile
-    float run_m = -INFINITY, run_s = 0.0f;  // draft: max of acc + u, sum of exp
-    float run_min = 0.0f, run_res = 0.0f;   // verify: sum min(p, q), sum (p - q)_+
-
-    // ---- one block: product, transpose, epilogue
-    auto block = [&](int j, const URegs &ur, auto mask_tag) __attribute__((always_inline)) {
+    // ---- epilogue of block j for row block rb: transpose the product
+    //      through the wave's scratch, add U, fold into the running sums
+    auto epilogue = [&](int j, int rb, const floatx16 &acc, const URegs &ur,
+                        auto mask_tag) __attribute__((always_inline)) {
       constexpr bool kMask = decltype(mask_tag)::value;
-      floatx16 acc;
-      mma_block<KS>(af, w2s[j & 1], r, acc);
+      RowState &s = rs[rb];
+      wave_sync();  // the previous block's reads of the scratch are done
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         ws[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * kScratchPitch + (lane & 31)] = acc[e];
       wave_sync();  // the other lanes' accumulators are in the scratch
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const floatx4 c4 = *reinterpret_cast<const floatx4 *>(ws + erow_w * kScratchPitch + ec0 + 4 * q);
-        v[4 * q] = c4[0]; v[4 * q + 1] = c4[1]; v[4 * q + 2] = c4[2]; v[4 * q + 3] = c4[3];
-      }
       const int col0 = (cb0 + j) * kBlockCols + ec0;
-#pragma unroll
-      for (int i = 0; i < kSegV; ++i) {
-        float u[kPer];
-        unpack16(ur.u[i], (T *)nullptr, u);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) v[i * kPer + q] += u[q];  // v = acc + u
-      }
+      const float *srow = ws + erow_w * kScratchPitch + ec0;
       if constexpr (!kVerify) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const floatx4 c4 = *reinterpret_cast<const floatx4 *>(srow + 4 * q);
+          v[4 * q] = c4[0]; v[4 * q + 1] = c4[1]; v[4 * q + 2] = c4[2]; v[4 * q + 3] = c4[3];
+        }
+#pragma unroll
+        for (int i = 0; i < kSegV; ++i) {
+          float u[kPer];
+          unpack16(ur.u[rb][i], (T *)nullptr, u);
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) v[i * kPer + q] += u[q];  // v = acc + u
+        }
         float bm = -INFINITY;
 #pragma unroll
         for (int c = 0; c < 16; ++c) bm = fmaxf(bm, (kMask && col0 + c >= V) ? -INFINITY : v[c]);
-        const float mn = fmaxf(run_m, bm);
+        const float mn = fmaxf(s.run_m, bm);
         if (!kMask || mn != -INFINITY) {
           // exp(z - z_max) = 2^((v - v_max) log2(e) / T): v - v_max keeps the
           // precision of the terms near the maximum
@@ -356,47 +375,61 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
             const float e = exp2_fast((v[c] - mn) * cl);
             sb += (kMask && col0 + c >= V) ? 0.0f : e;
           }
-          run_s = fmaf(run_s, exp2_fast((run_m - mn) * cl), sb);
-          run_m = mn;
+          s.run_s = fmaf(s.run_s, exp2_fast((s.run_m - mn) * cl), sb);
+          s.run_m = mn;
         }
       } else {
-        float t[16];
+        // one 16-byte piece (kPer columns) of U and P at a time
 #pragma unroll
-        for (int i = 0; i < kSegV; ++i) unpack16(ur.t[i], (T *)nullptr, t + i * kPer);
+        for (int i = 0; i < kSegV; ++i) {
+          float u[kPer], t[kPer];
+          unpack16(ur.u[rb][i], (T *)nullptr, u);
+          unpack16(ur.t[rb][i], (T *)nullptr, t);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const float a = log2_prob(t[c], invT, mp, lp);  // log2 p
-          const float b = log2_prob(v[c], invT, mq, lq);  // log2 q
-          const float mn = exp2_fast(fminf(a, b));
-          const float pe = exp2_fast(a);
-          const bool in = !kMask || col0 + c < V;
-          run_min += in ? mn : 0.0f;
-          run_res += in ? pe - mn : 0.0f;
+          for (int q4 = 0; q4 < kPer; q4 += 4) {
+            const floatx4 c4 = *reinterpret_cast<const floatx4 *>(srow + i * kPer + q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q = q4 + e, c = i * kPer + q;
+              const float a = log2_prob(t[q], invT, s.mp, s.lp);          // log2 p
+              const float b = log2_prob(c4[e] + u[q], invT, s.mq, s.lq);  // log2 q, v = acc + u
+              const float mn = exp2_fast(fminf(a, b));
+              const float pe = exp2_fast(a);
+              const bool in = !kMask || col0 + c < V;
+              s.run_min += in ? mn : 0.0f;
+              s.run_res += in ? pe - mn : 0.0f;
+            }
+          }
         }
       }
     };
     // ---- end of a tile: combine the lane pair of each row into the LDS
     //      partial buffer, reset; every kFlushTiles tiles the buffer goes out
     auto tile_end = [&](int tl) __attribute__((always_inline)) {
-      float2 o;
-      if constexpr (!kVerify) {
-        const float om = pair_swap(run_m), os = pair_swap(run_s);
-        const float M = fmaxf(run_m, om);
-        float S = 0.0f;
-        if (M != -INFINITY)
-          S = run_s * exp2_fast((run_m - M) * cl) + os * exp2_fast((om - M) * cl);
-        o = make_float2(M * invT, S);  // max z = (max of acc + u) / T, exactly
-        run_m = -INFINITY;
-        run_s = 0.0f;
-      } else {
-        o = make_float2(run_min + pair_swap(run_min), run_res + pair_swap(run_res));
-        run_min = run_res = 0.0f;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        RowState &s = rs[rb];
+        float2 o;
+        if constexpr (!kVerify) {
+          const float om = pair_swap(s.run_m), os = pair_swap(s.run_s);
+          const float M = fmaxf(s.run_m, om);
+          float S = 0.0f;
+          if (M != -INFINITY)
+            S = s.run_s * exp2_fast((s.run_m - M) * cl) + os * exp2_fast((om - M) * cl);
+          o = make_float2(M * invT, S);  // max z = (max of acc + u) / T, exactly
+          s.run_m = -INFINITY;
+          s.run_s = 0.0f;
+        } else {
+          o = make_float2(s.run_min + pair_swap(s.run_min), s.run_res + pair_swap(s.run_res));
+          s.run_min = s.run_res = 0.0f;
+        }
+        if ((lane & 1) == 0) pbuf[s.slot][tl % kFlushTiles] = o;
       }
-      if ((lane & 1) == 0) pbuf[wave * 32 + erow_w][tl % kFlushTiles] = o;
     };
     auto flush = [&](int tl) __attribute__((always_inline)) {
       __syncthreads();
       const int n = tl % kFlushTiles + 1, ft = tile0 + tl + 1 - n;
+      float2 *out = kVerify ? p.pair_partials : p.tile_stats;
       for (int i = tid; i < kRowGroup * n; i += kThreads) {
         const int row = i / n, t = i - row * n;
         const int orow = pout[row];
@@ -404,40 +437,55 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
       }
     };
 
-    // ---- pipeline: W2 of block j+1 goes to LDS during block j; loads run two
-    //      blocks ahead of their use
-    // two register sets each: W2 of block j + 1 goes to LDS during block j and
-    // its set is refilled with block j + 3; U (P) of block j is used in block j
-    // and its set refilled with block j + 2
+    // ---- pipeline.  The product of block j + 1 is issued before the
+    //      epilogue of block j, so the matrix cores work while the vector ALU
+    //      reduces: at step j block j + 1 is in LDS stage (j + 1) & 1, W2 of
+    //      block j + 2 is in registers and goes to stage j & 1 (free since the
+    //      product of block j), and that register set is refilled with block
+    //      j + 4; U (P) of block j is used and its set refilled with j + 2.
     WRegs wr0, wr1;
     URegs ur0, ur1;
+    floatx16 acc0[RB], acc1[RB];
     __syncthreads();  // the previous range is done with both LDS stages
     load_w(wr0, 0);
     load_w(wr1, 1);
     load_u(ur0, 0);
     load_u(ur1, 1);
     store_w(0, wr0);
+    store_w(1, wr1);
     load_w(wr0, 2);
-    auto step = [&](int j, bool masked, WRegs &wnext, URegs &ucur) __attribute__((always_inline)) {
-      __syncthreads();  // block j in LDS stage j & 1; stage (j + 1) & 1 is free
-      if (!wave_live) {
-      } else if (masked) {
-        block(j, ucur, std::true_type{});
-      } else {
-        block(j, ucur, std::false_type{});
+    load_w(wr1, 3);
+    __syncthreads();  // blocks 0 and 1 in LDS
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      if (rs[rb].wave_live) mma_block<KS>(af[rb], w2s[0], r, acc0[rb]);
+    auto step = [&](int j, bool masked, WRegs &wst, URegs &ucur, floatx16 (&acc_j)[RB],
+                    floatx16 (&acc_n)[RB]) __attribute__((always_inline)) {
+      __syncthreads();  // block j + 1 in stage (j + 1) & 1; stage j & 1 is free
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (rs[rb].wave_live) mma_block<KS>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
+      store_w(j & 1, wst);  // block j + 2
+      load_w(wst, j + 4);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (!rs[rb].wave_live) {
+        } else if (masked) {
+          epilogue(j, rb, acc_j[rb], ucur, std::true_type{});
+        } else {
+          epilogue(j, rb, acc_j[rb], ucur, std::false_type{});
+        }
       }
-      store_w((j + 1) & 1, wnext);
-      load_w(wnext, j + 3);
       load_u(ucur, j + 2);
     };
     const bool mask_last = (int64_t)(tile0 + ntile) * kTileN > V;
     for (int tl = 0; tl < ntile; ++tl) {
       const bool masked = mask_last && tl == ntile - 1;
       const int j = tl * kBlocksPerTile;
-      step(j, masked, wr1, ur0);
-      step(j + 1, masked, wr0, ur1);
-      step(j + 2, masked, wr1, ur0);
-      step(j + 3, masked, wr0, ur1);
+      step(j, masked, wr0, ur0, acc0, acc1);
+      step(j + 1, masked, wr1, ur1, acc1, acc0);
+      step(j + 2, masked, wr0, ur0, acc0, acc1);
+      step(j + 3, masked, wr1, ur1, acc1, acc0);
       tile_end(tl);
       if (tl % kFlushTiles == kFlushTiles - 1 || tl == ntile - 1) flush(tl);
     }

@@ -249,10 +249,10 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
     if (wide) {
       DSPARK_LAUNCH("bias_tile_draft", stream,
-                    (stream_tile_kernel<T, Epi::kDraft, KS, 8><<<grid, 8 * kWave, 0, stream>>>(bp)));
+                    (stream_tile_kernel<T, Epi::kDraft, KS, 8, 1><<<grid, 8 * kWave, 0, stream>>>(bp)));
     } else {
       DSPARK_LAUNCH("bias_tile_draft", stream,
-                    (stream_tile_kernel<T, Epi::kDraft, KS, 4><<<grid, 4 * kWave, 0, stream>>>(bp)));
+                    (stream_tile_kernel<T, Epi::kDraft, KS, 4, 1><<<grid, 4 * kWave, 0, stream>>>(bp)));
     }
     DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp));
   }
