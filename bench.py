@@ -239,7 +239,7 @@ def main():
     roof["kernel"] = dom
     roof["mfma_frac"] = round(dk["tflops"] / PEAK_BF16_TFLOPS, 4)
     roof["traffic"] = None
-    traffic_file = os.path.join(PROFILE_DIR, f"traffic_{dom}_config{cfg.cid}.json")
+    traffic_file = os.path.join(PROFILE_DIR, f"traffic_{dom}_{cfg.name.replace('-', '_')}.json")
     if os.path.exists(traffic_file):
         with open(traffic_file) as f:
             tr = json.load(f)
