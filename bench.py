@@ -45,11 +45,15 @@ def parse():
 
 
 def source_hash():
+    """Hash of the library's code (comments and blank lines dropped), to tell
+    whether hardware counters collected earlier still describe its kernels."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_sampling_verification_03_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            code = [re.sub(r"//.*", "", line).rstrip() for line in fh]
+        h.update(f.encode() + "\n".join(line for line in code if line).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,26 +1,16 @@
-// Fused Markov-bias tile kernel: gather W1 rows -> matrix-core product with W2
-// -> add U_k and scale by 1/T -> per-(row, vocabulary tile) reduction.
+// Fused Markov-bias product: matrix-core product of W1 rows with W2 -> add U_k
+// and scale by 1/T -> per-(row, vocabulary tile) reduction.
 //
 // The Markov head (Blog, "Markov sequential head"; KB section 2) adds the bias
 // row W1[x_{k-1}, :] W2 to the backbone logits U_k.  For a batch of rows this is
 // an [M, r] x [r, V] product whose only consumer is a vocabulary-wide
-// reduction, so z never goes to HBM: a workgroup owns one 128-column
-// vocabulary tile, keeps it on chip and emits one partial per row.
+// reduction, so z never goes to HBM: per row and 128-column vocabulary tile the
+// kernel emits one partial.
 //
 //   Draft epilogue  (m_t, s_t) = (max_v z, sum_v exp(z - m_t)) of the tile
 //   Verify epilogue (sum_v min(p, q), sum_v (p - q)_+) of the tile, with
 //                   q = exp(z - m_q)/S_q from the draft's statistics and
 //                   p = exp(t/T - m_p)/S_p from the target row statistics
-//
-// Work split.  Each of the 4 waves owns 32 of the 128 columns; it loads the r
-// coefficients of its 32 W2 columns into registers once (all K at a time, so
-// one memory round trip) and keeps them for every row tile the workgroup
-// visits: W2 crosses HBM once per launch.  Row tiles of TM rows (all requests
-// for the draft, the compacted verified drafts for verification) are walked
-// in a loop; per row tile the gathered W1 rows go to LDS, every wave multiplies
-// all TM rows by its columns, the accumulators are transposed through the same
-// LDS for a row-wise epilogue, and the U (and P) row segments that epilogue
-// reads are prefetched into registers before the matrix-core work starts.
 #pragma once
 #include <type_traits>
 
@@ -72,22 +62,21 @@ enum class Epi { kDraft, kVerify };
 // ------------------------------------------------------------------------
 // Row-stationary streaming tile kernel.
 //
-// A workgroup of 4 waves takes a row group of 128 product rows (wave w: rows
-// 32w..32w+31) and a contiguous range of vocabulary tiles.  Each wave keeps
-// the A operand of its 32 rows (all of K) in registers for the whole range;
-// W2 streams through in blocks of 32 columns: loaded into registers two
-// blocks ahead, written to one half of a double-buffered LDS stage (pieces
-// XOR-swizzled per column so the operand reads are free of bank conflicts),
-// and read by all four waves.  U (and P) row segments stream into a register
-// ring two blocks ahead.  After the product a wave transposes its 32x32
-// accumulator through its own LDS scratch so that each lane holds 16
-// consecutive columns of one row, adds U, and folds the block into running
-// per-row sums that are written once per 128-column tile.
+// A workgroup of NW waves takes a row group of product rows (each wave RB
+// blocks of 32 rows) and a contiguous range of vocabulary tiles.  Each wave
+// keeps the A operand of its rows (all of K) in registers for the whole range;
+// W2 streams through in blocks of 32 columns: loaded into registers ahead of
+// use, written to one half of a double-buffered LDS stage (a padded column
+// pitch keeps the operand reads free of bank conflicts), and read by all
+// waves.  U (and P) row segments stream into a register ring two blocks
+// ahead.  After the product a wave transposes its 32x32 accumulator through
+// its own LDS scratch so that each lane holds 16 consecutive columns of one
+// row, adds U, and folds the block into running per-row sums; the partials of
+// finished tiles are buffered in LDS and written every kFlushTiles tiles.
 //
 // The loop body covers one tile (4 blocks) with a fixed instruction sequence
-// (loads past the range are clamped, stores of lanes without an output go to
-// a sink), so every wait the compiler inserts counts exactly the loads it
-// needs.
+// (loads past the range are clamped), so the waits the compiler inserts count
+// only the loads they need.
 constexpr int kRowsPerWave = 32;                        // product rows of one wave
 constexpr int kBlockCols = 32;                          // W2 columns per block
 constexpr int kBlocksPerTile = kTileN / kBlockCols;     // 4

@@ -65,10 +65,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld_stream4(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
-__device__ __forceinline__ uint4 ld_stream(const void *p) {
-  const u32x4 v = ld_stream4(p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // e^x on the transcendental unit: 2^(x log2 e).  Every kernel uses this one
 // function, so equal arguments give equal results everywhere.

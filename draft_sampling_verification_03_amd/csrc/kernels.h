@@ -10,8 +10,7 @@ namespace dspark {
 
 constexpr int kComputeUnits = 256;  // MI355X
 
-// bytes 0..3 of every workspace hold the sticky error word; bytes 128..255 are
-// a write-only sink for lanes that have no output
+// bytes 0..3 of every workspace hold the sticky error word
 constexpr size_t kWsHeader = 256;
 
 struct DraftLaunch {
