@@ -38,13 +38,12 @@ struct SampleParams {
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
-  __shared__ float wbuf[kMaxTiles];
-  __shared__ float2 pbuf[kMaxTiles];
+  constexpr int kCpt = kMaxTiles / kBlock;  // tiles per thread, at most
   __shared__ float zbuf[kTileN];
   __shared__ __align__(16) T arow[kMaxRank + 16];
-  __shared__ float fred[8];
-  __shared__ int ired[8];
-  __shared__ float s_before;
+  __shared__ float red_max[4], red_sum[4];
+  __shared__ int red_found[4], red_last[4];
+  __shared__ float s_before, s_mt;
   __shared__ int s_token;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -53,78 +52,98 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   constexpr int kPer = 16 / (int)sizeof(T);
   const int pieces = r * (int)sizeof(T) / 16;
 
-  // 1. stage the row's tile partials and W1[x_{k-1}] (= A_k[rho]) in LDS, one
-  //    round trip; then the row maximum and tile masses w_t = s_t exp(m_t - m)
+  // 1. W1[x_{k-1}] (= A_k[rho]) to LDS; this thread's contiguous tiles
+  //    [t0, t1) of the row's partials into registers, one round trip
+  const int cpt = (nT + kBlock - 1) / kBlock;
+  const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
+  float2 pt[kCpt];
   {
     const T *Acur = reinterpret_cast<const T *>(p.A_cur) + (int64_t)rho * r;
     uint4 a = make_uint4(0, 0, 0, 0);
     if (tid < pieces) a = *reinterpret_cast<const uint4 *>(Acur + tid * kPer);
-    stage_to_lds<kMaxTiles / kBlock>(p.tile_stats + (int64_t)rho * nT, nT, pbuf);
+    const float2 *ts = p.tile_stats + (int64_t)rho * nT;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) pt[j] = t0 + j < t1 ? ts[t0 + j] : make_float2(-INFINITY, 0.0f);
     if (tid < pieces) *reinterpret_cast<uint4 *>(arow + tid * kPer) = a;
   }
-  __syncthreads();
-  const float2 *part = pbuf;
-  const int cpt = (nT + kBlock - 1) / kBlock;
-  const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
+  // 2. row maximum, then tile masses w_t = s_t exp(m_t - m) and their
+  //    exclusive scan in tile order (one barrier each)
   float lm = -INFINITY;
-  for (int t = t0; t < t1; ++t) lm = fmaxf(lm, part[t].x);
-  const float m = block_max(lm, fred);
+#pragma unroll
+  for (int j = 0; j < kCpt; ++j) lm = fmaxf(lm, pt[j].x);
+  lm = wave_max(lm);
+  if (lane == 0) red_max[wave] = lm;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+  float w[kCpt];
   float ls = 0.0f;
-  for (int t = t0; t < t1; ++t) {
-    const float w = part[t].y * fexp(part[t].x - m);
-    wbuf[t] = w;
-    ls += w;
+#pragma unroll
+  for (int j = 0; j < kCpt; ++j) {
+    w[j] = t0 + j < t1 ? pt[j].y * fexp(pt[j].x - m) : 0.0f;
+    ls += w[j];
   }
-  float S;
-  const float base = block_exclusive_scan(ls, fred, &S);
+  const float inc = wave_inclusive_scan(ls);
+  if (lane == kWave - 1) red_sum[wave] = inc;
+  __syncthreads();
+  float before_wave = 0.0f;
+  for (int i = 0; i < wave; ++i) before_wave += red_sum[i];
+  const float S = ((red_sum[0] + red_sum[1]) + red_sum[2]) + red_sum[3];
+  const float base = before_wave + (inc - ls);
   const bool finite = isfinite(m) && isfinite(S) && S > 0.0f;
 
-  // 2. the tile holding the draw
+  // 3. the tile holding the draw: the first tile whose cumulative mass
+  //    exceeds u * S (else, rounding having left no crossing, the last tile
+  //    with mass)
   const float u = uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamDraft);
   const float target = u * S;
-  int found = 0x7fffffff;
+  int found = 0x7fffffff, lastpos = -1;
   {
     float run = base;
-    for (int t = t0; t < t1; ++t) {
-      const float nx = run + wbuf[t];
-      if (found == 0x7fffffff && target < nx && wbuf[t] > 0.0f) found = t;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const float nx = run + w[j];
+      if (found == 0x7fffffff && target < nx && w[j] > 0.0f) found = t0 + j;
+      if (w[j] > 0.0f) lastpos = t0 + j;
       run = nx;
     }
   }
-  int tstar = block_min_int(found, ired);
-  if (tstar == 0x7fffffff) {  // rounding left no crossing: last tile with mass
-    int lastpos = -1;
-    for (int t = t0; t < t1; ++t)
-      if (wbuf[t] > 0.0f) lastpos = t;
-    tstar = block_max_int(lastpos, ired);
-  }
+  found = wave_min_int(found);
+  lastpos = wave_max_int(lastpos);
+  if (lane == 0) { red_found[wave] = found; red_last[wave] = lastpos; }
+  __syncthreads();
+  int tstar = min(min(red_found[0], red_found[1]), min(red_found[2], red_found[3]));
+  if (tstar == 0x7fffffff) tstar = max(max(red_last[0], red_last[1]), max(red_last[2], red_last[3]));
   if (tstar < 0 || !finite) {
     if (tid == 0) flag_error(p.err, kErrNonFinite);
     tstar = 0;
   }
-  if (tid == 0) s_before = 0.0f;
-  __syncthreads();
-  if (t0 <= tstar && tstar < t1) {
+  if (t0 <= tstar && tstar < t1) {  // the owner of the tile: mass before it, its max
     float run = base;
-    for (int t = t0; t < tstar; ++t) run += wbuf[t];
+    float mt = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      if (t0 + j < tstar) run += w[j];
+      if (t0 + j == tstar) mt = pt[j].x;
+    }
     s_before = run;
+    s_mt = mt;
   }
 
-  // 3. recompute z of that tile, bit-identical to the fused kernel
+  // 4. recompute z of that tile, bit-identical to the fused kernel
   __syncthreads();
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
   recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31, zbuf);
   __syncthreads();
-  if (tid < kTileN) zbuf[tid] *= p.invT;  // z = (acc + u) / T, the draft's exact arithmetic
-  __syncthreads();
 
-  // 4. scan inside the tile (wave 0, two columns per lane, left to right)
+  // 5. scan inside the tile (wave 0, two columns per lane, left to right);
+  //    z = (acc + u) / T, the draft's exact arithmetic
   if (wave == 0) {
-    const float mt = part[tstar].x;
+    const float mt = s_mt;
     const float scale = fexp(mt - m);
-    const float e0 = fexp(zbuf[2 * lane] - mt), e1 = fexp(zbuf[2 * lane + 1] - mt);
-    const float inc = wave_inclusive_scan(e0 + e1);
-    float exc = __shfl_up(inc, 1);
+    const float z0 = zbuf[2 * lane] * p.invT, z1 = zbuf[2 * lane + 1] * p.invT;
+    const float e0 = fexp(z0 - mt), e1 = fexp(z1 - mt);
+    const float incl = wave_inclusive_scan(e0 + e1);
+    float exc = __shfl_up(incl, 1);
     if (lane == 0) exc = 0.0f;
     const float cdf0 = s_before + scale * (exc + e0);
     const float cdf1 = s_before + scale * ((exc + e0) + e1);
@@ -139,17 +158,18 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       pick = wave_max_int(lp);
       if (pick < 0) pick = 0;
     }
+    const float zp = __shfl(pick & 1 ? z1 : z0, pick >> 1);
     if (lane == 0) {
       const int xk = tstar * kTileN + pick;
       p.x[slot] = finite ? xk : -1;
       p.q_stats[2 * slot] = m;
       p.q_stats[2 * slot + 1] = S;
-      p.q_x[slot] = fexp(zbuf[pick] - m) / S;
+      p.q_x[slot] = fexp(zp - m) / S;
       s_token = xk;  // in [0, V): a picked column always has positive mass
     }
   }
 
-  // 5. confidence head on [h_k ; W1[x_{k-1}]] (wave 1)
+  // 6. confidence head on [h_k ; W1[x_{k-1}]] (wave 1)
   if (p.sh != nullptr && wave == 1) {
     float acc = 0.0f;
     for (int i = lane; i < r; i += kWave) acc = fmaf(p.w_e[i], Elem<T>::at(arow, i), acc);
@@ -160,7 +180,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     }
   }
 
-  // 6. the next step's transition row: A_{k+1}[rho] = W1[x_k]
+  // 7. the next step's transition row: A_{k+1}[rho] = W1[x_k]
   if (p.A_next != nullptr) {
     __syncthreads();
     const int xk = min(max(s_token, 0), V - 1);
