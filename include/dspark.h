@@ -147,7 +147,7 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
  *   c_prev2 [R][gamma] confidences of round t-2, ASYNC_TOPK only (else ignored)
  *   SPS     [B_max + 1] target steps per second indexed by verify batch size B,
  *           fp64; B_max >= R * (1 + gamma).  May be NULL in OFF mode.
- *   R * gamma <= 16384.
+ *   R * gamma <= 8192, gamma <= 64.
  * Outputs
  *   ell [R], row_offset [R + 1] int32; a [R][gamma] fp32 (may be NULL);
  *   n_admitted [1] int32; theta [1] fp64 (theta_{n*}; NaN when c is NULL).
