@@ -38,6 +38,7 @@ struct SchedShared {
   union {
     float conf[kConfSlots];       // confidences, then survival (in place)
     int ell[kMaxCandidates];      // admitted depth per request
+    uint64_t keys2[kMaxCandidates];  // second exchange buffer of the sort
   };
   int64_t wave_i64[kSchedWaves];
   double wave_d[kSchedWaves];
@@ -224,42 +225,72 @@ __device__ __forceinline__ void reg_stage(uint64_t (&k)[E], int base, int size) 
       }
   }
 }
-// The whole network is unrolled (P2 is a constant): no branches or loop
-// control per stage, which would otherwise queue all 16 waves on the scalar unit.
+// Strides across waves: position p = e + E (lane + 64 wave) in the blocked
+// layout.  For the levels that have such strides the keys are transposed
+// through LDS into a layout where the wave bits of p are lane bits (lane =
+// l0 + 4 wave_p, wave = l_hi, with l0 and l_hi the low two and high four lane
+// bits of p), the cross-wave strides run as lane shuffles, and the keys go
+// back for the rest of the level: two barriers per level (alternating LDS
+// buffers) instead of two per stride.
 template <int E>
-__device__ __forceinline__ void sort_keys(uint64_t (&k)[E], SchedShared &sh) {
-  constexpr int P2 = kSchedThreads * E;
-  const int base = (int)threadIdx.x * E;
+__device__ __forceinline__ int transposed_base() {
+  constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : 3;
+  const int lane = (int)(threadIdx.x & (kWave - 1)), wave = (int)threadIdx.x / kWave;
+  return ((lane & 3) << LE) | (wave << (LE + 2)) | ((lane >> 2) << (LE + 6));
+}
+template <int E>
+__device__ __forceinline__ void exchange(uint64_t (&k)[E], uint64_t *buf, int from, int to) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) buf[from + e] = k[e];
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) k[e] = buf[to + e];
+}
+template <int E>
+__device__ __forceinline__ void local_stage(uint64_t (&k)[E], int base, int size, int s) {
+  const bool keep_min = ((base & s) == 0) == ((base & size) == 0);
+  if (s >= E) {
+    switch (s / E) {
+      case 1: lane_stage<E, 1>(k, keep_min); break;
+      case 2: lane_stage<E, 2>(k, keep_min); break;
+      case 4: lane_stage<E, 4>(k, keep_min); break;
+      case 8: lane_stage<E, 8>(k, keep_min); break;
+      case 16: lane_stage<E, 16>(k, keep_min); break;
+      default: lane_stage<E, 32>(k, keep_min); break;
+    }
+  } else if (s == 4) {
+    reg_stage<E, 4>(k, base, size);
+  } else if (s == 2) {
+    reg_stage<E, 2>(k, base, size);
+  } else {
+    reg_stage<E, 1>(k, base, size);
+  }
+}
+// The whole network is unrolled (P2 is a constant): no branches or loop
+// control per stage, which would otherwise queue all 16 waves on the scalar
+// unit.  buf0 and buf1 hold P2 keys each.
+template <int E>
+__device__ __forceinline__ void sort_keys(uint64_t (&k)[E], uint64_t *buf0, uint64_t *buf1) {
+  constexpr int P2 = kSchedThreads * E, kCross = kWave * E;
+  const int base = (int)threadIdx.x * E, tbase = transposed_base<E>();
 #pragma unroll
   for (int size = 2; size <= P2; size <<= 1) {
+    if (size > kCross) {
+      exchange<E>(k, buf0, base, tbase);
 #pragma unroll
-    for (int s = size >> 1; s > 0; s >>= 1) {
-      // above the in-thread bits both s and size give one direction per thread
-      const bool keep_min = ((base & s) == 0) == ((base & size) == 0);
-      if (s >= kWave * E) {
-        __syncthreads();  // the previous exchange's reads are done
-#pragma unroll
-        for (int e = 0; e < E; ++e) sh.keys[base + e] = k[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) k[e] = keep_of(k[e], sh.keys[(base + e) ^ s], keep_min);
-      } else if (s >= E) {
-        switch (s / E) {
-          case 1: lane_stage<E, 1>(k, keep_min); break;
-          case 2: lane_stage<E, 2>(k, keep_min); break;
-          case 4: lane_stage<E, 4>(k, keep_min); break;
-          case 8: lane_stage<E, 8>(k, keep_min); break;
-          case 16: lane_stage<E, 16>(k, keep_min); break;
+      for (int s = size >> 1; s >= kCross; s >>= 1) {
+        const bool keep_min = ((tbase & s) == 0) == ((tbase & size) == 0);
+        switch (s / kCross) {
+          case 1: lane_stage<E, 4>(k, keep_min); break;
+          case 2: lane_stage<E, 8>(k, keep_min); break;
+          case 4: lane_stage<E, 16>(k, keep_min); break;
           default: lane_stage<E, 32>(k, keep_min); break;
         }
-      } else if (s == 4) {
-        reg_stage<E, 4>(k, base, size);
-      } else if (s == 2) {
-        reg_stage<E, 2>(k, base, size);
-      } else {
-        reg_stage<E, 1>(k, base, size);
       }
+      exchange<E>(k, buf1, tbase, base);
     }
+#pragma unroll
+    for (int s = (size > kCross ? kCross : size) >> 1; s > 0; s >>= 1) local_stage<E>(k, base, size, s);
   }
 }
 
@@ -282,7 +313,7 @@ __device__ __forceinline__ int scheduler_pass(const ScheduleLaunch L, const floa
   if (a_out) write_survival(a_out, N, gamma, gs, sh);
 #pragma unroll
   for (int e = 0; e < E; ++e) k[e] = base + e < N ? sh.keys[base + e] : ~(uint64_t)0;
-  sort_keys<E>(k, sh);
+  sort_keys<E>(k, sh.keys, sh.keys2);
 
   // fixed-point path: A_i = sum of the weights before sorted position i
   int64_t wgt[E], lsum = 0;
