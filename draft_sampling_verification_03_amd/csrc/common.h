@@ -20,6 +20,7 @@ constexpr int kBlock = 256;          // threads of every workgroup
 constexpr int kTileN = 128;          // vocabulary columns per tile
 constexpr int kMaxTiles = 2048;      // V <= 262144
 constexpr int kMaxRank = 256;
+constexpr int kMaxGamma = 64;       // draft positions per request
 
 // sticky device error bits (mirrors dspark.h)
 constexpr int kErrToken = 1, kErrConfidence = 2, kErrLength = 4, kErrNonFinite = 8;

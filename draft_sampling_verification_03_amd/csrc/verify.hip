@@ -269,110 +269,143 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   __shared__ float fred[8];
   __shared__ int ired[8];
   __shared__ float s_before;
-  __shared__ int s_bad;
+  __shared__ float2 s_ps[kMaxGamma + 1];  // (m_p, S_p) of the request's target rows
+  __shared__ int s_x[kMaxGamma];          // its draft tokens
 
+  constexpr int kTpt = kMaxTiles / kBlock;  // tiles per thread, at most
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rho = blockIdx.x, gamma = p.gamma, V = p.V, nT = p.n_tiles;
   int32_t *yrow = p.y + (int64_t)rho * (gamma + 1);
   float *crow = p.c_star + (int64_t)rho * gamma;
 
-  // ---- validate this request's slice of the ragged batch
-  const int ell = p.ell[rho];
-  const int base = p.row_offset[rho];
-  if (tid == 0) {
-    const int64_t d_off = (int64_t)base - rho;
-    const bool ok = ell >= 0 && ell <= gamma && base >= 0 &&
-                    p.row_offset[rho + 1] == base + 1 + ell && base + ell < p.rows_capacity &&
-                    p.row_offset[p.R] <= p.rows_capacity && d_off >= 0 &&
-                    d_off + ell <= (int64_t)p.R * gamma;
-    s_bad = ok ? 0 : 1;
-    if (!ok) flag_error(p.err, kErrLength);
-  }
-  __syncthreads();
-  if (s_bad) {
-    for (int i = tid; i <= gamma; i += kBlock) yrow[i] = -1;
-    for (int i = tid; i < gamma; i += kBlock) crow[i] = NAN;
-    if (tid == 0) p.n_acc[rho] = 0;
-    return;
-  }
-  const int64_t d_off = (int64_t)base - rho;  // compact index of (rho, k = 1)
+  // ---- loads that need only rho, all in flight together: the request's
+  //      slice of the ragged batch (every thread validates the same values),
+  //      the draft token and q(x_k) of position k = tid + 1, and the bonus
+  //      row's tile partials
+  const int ell_in = p.ell[rho];
+  const int base_in = p.row_offset[rho];
+  const int next = p.row_offset[rho + 1], rows_used = p.row_offset[p.R];
   const int32_t *xr = p.x + (int64_t)rho * gamma;
-
-  // ---- c*_k = sum over tiles of sum_v min(p, q), fixed order per k
-  for (int k = 1 + wave; k <= gamma; k += kBlock / kWave) {
-    float v = NAN;
-    if (k <= ell) {
-      const float2 *pp = p.pair_partials + (d_off + k - 1) * nT;
-      float acc = 0.0f;
+  // (unconditional loads at clamped positions: a load under a condition
+  // would be waited for inside its branch)
+  const int xk_raw = xr[min(tid, gamma - 1)];
+  const float qk = p.q_x[(int64_t)rho * gamma + min(tid, gamma - 1)];
+  const int x0 = p.x0[rho];
+  float2 bt[kTpt];
 #pragma unroll
-      for (int j = 0; j < kMaxTiles / kWave; ++j) {  // all loads in flight, fixed order
-        const int t = lane + j * kWave;
-        if (t < nT) acc += pp[t].x;
-      }
-      v = wave_sum(acc);
+  for (int i = 0; i < kTpt; ++i)
+    bt[i] = p.bonus_tiles[(int64_t)rho * nT + min(tid + i * kBlock, nT - 1)];
+  const bool ok = ell_in >= 0 && ell_in <= gamma && base_in >= 0 && next == base_in + 1 + ell_in &&
+                  base_in + ell_in < p.rows_capacity && rows_used <= p.rows_capacity &&
+                  base_in >= rho && (int64_t)base_in - rho + ell_in <= (int64_t)p.R * gamma;
+  // an invalid slice runs as an empty one (every address stays in bounds, so
+  // the loads above need not wait for the check) and is reported at the end
+  const int ell = ok ? ell_in : 0, base = ok ? base_in : 0;
+  const int64_t d_off = ok ? (int64_t)base - rho : 0;  // compact index of (rho, k = 1)
+
+  // ---- target-row inputs of position k = tid + 1 <= ell + 1 (the row after
+  //      the drafts is the bonus row): chunk statistics, and p(x_k)
+  const bool own_row = tid <= ell;
+  const int prow = base + (own_row ? tid : 0);
+  float2 cs[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) cs[c] = p.p_chunks[(int64_t)prow * kChunks + c];
+  const bool test = tid < ell;
+  const int xk = xk_raw < 0 ? 0 : (xk_raw >= V ? V - 1 : xk_raw);
+  const float tx = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)prow * V,
+                               test ? xk : 0);
+
+  // ---- c*_k = sum over tiles of sum_v min(p, q) in tile order: wave w takes
+  //      k = w + 1, w + 5, ... two at a time, every tile load in flight
+  //      (clamped past n_tiles, masked in the sum)
+  constexpr int kTpl = kMaxTiles / kWave;  // tiles per lane, at most
+  for (int ka = 1 + wave; ka <= ell; ka += 2 * (kBlock / kWave)) {
+    const int kb = ka + kBlock / kWave;
+    const float2 *pa = p.pair_partials + (d_off + ka - 1) * nT;
+    const float2 *pb = p.pair_partials + (d_off + min(kb, ell) - 1) * nT;
+    float va[kTpl], vb[kTpl];
+#pragma unroll
+    for (int i = 0; i < kTpl; ++i) {
+      const int t = min(lane + i * kWave, nT - 1);
+      va[i] = pa[t].x;
+      vb[i] = pb[t].x;
     }
-    if (lane == 0) crow[k - 1] = v;
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTpl; ++i)
+      if (lane + i * kWave < nT) {
+        sa += va[i];
+        sb += vb[i];
+      }
+    sa = wave_sum(sa);
+    sb = wave_sum(sb);
+    if (lane == 0) {
+      crow[ka - 1] = sa;
+      if (kb <= ell) crow[kb - 1] = sb;
+    }
   }
+  for (int k = ell + 1 + tid; k <= gamma; k += kBlock) crow[k - 1] = NAN;
 
   // ---- accept tests: u * q(x_k) < p(x_k), first rejection
-  int rej = 0x7fffffff;
-  for (int k = 1 + tid; k <= ell; k += kBlock) {
-    int xk = xr[k - 1];
-    if (xk < 0 || xk >= V) {
-      flag_error(p.err, kErrToken);
-      xk = xk < 0 ? 0 : V - 1;
-    }
-    const int row = base + k - 1;
-    const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)row * kChunks);
-    const float t = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)row * V, xk) * p.invT;
-    const double pk = exp((double)t - (double)ps.x) / (double)ps.y;
-    const double qk = (double)p.q_x[(int64_t)rho * gamma + k - 1];
-    const double u = (double)uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamAccept);
-    if (!(u * qk < pk)) rej = min(rej, k);
+  float2 ps_own = make_float2(0.0f, 0.0f);
+  if (own_row) {
+    ps_own = combine_chunk_stats(cs);
+    s_ps[tid] = ps_own;
   }
-  rej = block_min_int(rej, ired);
+  if (tid < gamma) s_x[tid] = xk;
+  int rej = 0x7fffffff;
+  if (test) {
+    if (xk_raw != xk) flag_error(p.err, kErrToken);
+    const int k = tid + 1;
+    const double pk = exp((double)(tx * p.invT) - (double)ps_own.x) / (double)ps_own.y;
+    const double u = (double)uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamAccept);
+    if (!(u * (double)qk < pk)) rej = k;
+  }
+  rej = block_min_int(rej, ired);  // its barriers also publish s_ps and s_x
   const int n = rej == 0x7fffffff ? ell : rej - 1;
   const int j = n + 1;             // position of the final token
   const int frow = base + n;       // its target row
-  const float2 ps = combine_chunk_stats(p.p_chunks + (int64_t)frow * kChunks);
+  const float2 ps = s_ps[n];
   const float uf = uniform01(p.seed, p.round, (uint64_t)j, (uint64_t)rho, kStreamFinal);
   const T *Prow = reinterpret_cast<const T *>(p.P) + (int64_t)frow * V;
   int final_token = 0;
 
   bool residual = n < ell;
   if (residual) {
-    // residual masses per tile from the verify pass
+    // residual masses per tile from the verify pass; the transition row and
+    // q statistics of position j load meanwhile
     const float2 *pp = p.pair_partials + (d_off + j - 1) * nT;
+    float w[kTpt];
 #pragma unroll
-    for (int j = 0; j < kMaxTiles / kBlock; ++j) {
-      const int t = tid + j * kBlock;
-      if (t < nT) wbuf[t] = pp[t].y;
-    }
+    for (int i = 0; i < kTpt; ++i) w[i] = pp[min(tid + i * kBlock, nT - 1)].y;
+    const int prev = j == 1 ? min(max(x0, 0), V - 1) : s_x[j - 2];
+    const T *W1 = reinterpret_cast<const T *>(p.W1);
+    const int pieces = p.r * (int)sizeof(T) / 16;
+    uint4 arow_piece = make_uint4(0, 0, 0, 0);
+    if (tid < pieces)
+      arow_piece = *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * p.r + tid * (16 / sizeof(T)));
+    const int64_t qi = (int64_t)rho * gamma + j - 1;
+    const float mq = p.q_stats[2 * qi], sq = p.q_stats[2 * qi + 1];
+#pragma unroll
+    for (int i = 0; i < kTpt; ++i)
+      if (tid + i * kBlock < nT) wbuf[tid + i * kBlock] = w[i];
+    if (tid < pieces) *reinterpret_cast<uint4 *>(arow + tid * (16 / sizeof(T))) = arow_piece;
     __syncthreads();
     float total, target;
     const int tstar = pick_tile(wbuf, nT, uf, fred, ired, &s_before, &total, &target);
     if (total > 0.0f) {
-      int prev = j == 1 ? p.x0[rho] : xr[j - 2];
-      if (prev < 0 || prev >= V) prev = prev < 0 ? 0 : V - 1;
-      const T *W1 = reinterpret_cast<const T *>(p.W1);
-      const int pieces = p.r * (int)sizeof(T) / 16;
-      if (tid < pieces)
-        *reinterpret_cast<uint4 *>(arow + tid * (16 / sizeof(T))) =
-            *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * p.r + tid * (16 / sizeof(T)));
-      __syncthreads();
+      const int col = tstar * kTileN + tid;
+      const float tcol = tid < kTileN && col < V ? Elem<T>::at(Prow, col) : 0.0f;
       const T *Urow = reinterpret_cast<const T *>(p.U) + ((int64_t)rho * gamma + j - 1) * V;
       recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
                           (int)((d_off + j - 1) & 31), zbuf);
       __syncthreads();
       if (tid < kTileN) {
         // (p - q)_+ = p - min(p, q), each term formed as in the verify pass
-        const int64_t qi = (int64_t)rho * gamma + j - 1;
-        const float mq = p.q_stats[2 * qi], lq = log2_fast(p.q_stats[2 * qi + 1]);
-        const float lp = log2_fast(ps.y);
-        const int col = tstar * kTileN + tid;
+        const float lq = log2_fast(sq), lp = log2_fast(ps.y);
         float e = 0.0f;
         if (col < V) {
-          const float a = log2_prob(Elem<T>::at(Prow, col), p.invT, ps.x, lp);
+          const float a = log2_prob(tcol, p.invT, ps.x, lp);
           const float b = log2_prob(zbuf[tid], p.invT, mq, lq);
           e = exp2_fast(a) - exp2_fast(fminf(a, b));
         }
@@ -394,11 +427,10 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
     // gets its tile masses by one pass over the row
     const bool bonus = n == ell;
     if (bonus) {
-      const float2 *bt = p.bonus_tiles + (int64_t)rho * nT;
 #pragma unroll
-      for (int j = 0; j < kMaxTiles / kBlock; ++j) {
-        const int t = tid + j * kBlock;
-        if (t < nT) wbuf[t] = bt[t].y * fexp(bt[t].x - ps.x);
+      for (int i = 0; i < kTpt; ++i) {
+        const int t = tid + i * kBlock;
+        if (t < nT) wbuf[t] = bt[i].y * fexp(bt[i].x - ps.x);
       }
     } else {
       for (int t = wave; t < nT; t += kBlock / kWave) {
@@ -428,6 +460,12 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   }
 
   // ---- outputs
+  if (!ok) {  // uniform
+    if (tid == 0) flag_error(p.err, kErrLength);
+    for (int i = tid; i <= gamma; i += kBlock) yrow[i] = -1;
+    if (tid == 0) p.n_acc[rho] = 0;
+    return;
+  }
   for (int i = tid; i <= gamma; i += kBlock) {
     int v = -1;
     if (i < n) v = xr[i];
