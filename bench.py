@@ -217,7 +217,6 @@ def main():
         "row_chunk_stats": dict(bytes=rows_used * V * s_el + rows_used * 32, flops=0.0, bound="hbm"),
         "bias_tile_verify": dict(bytes=2 * sum_ell * V * s_el + r * V * s_el + sum_ell * nT * 8,
                                  flops=2.0 * sum_ell * r * V, bound="hbm"),
-        "gather_rows": dict(bytes=2 * R * r * s_el, flops=0.0, bound="hbm"),
         "verify_finalize": dict(bytes=sum_ell * nT * 8 + R * nT * 8, flops=0.0, bound="hbm"),
         "overlap_chunk": dict(bytes=2 * n_ov * V * s_el, flops=0.0, bound="hbm"),
         "overlap_combine": dict(bytes=n_ov * 20, flops=0.0, bound="hbm"),

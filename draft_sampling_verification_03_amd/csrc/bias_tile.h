@@ -53,8 +53,10 @@ struct BiasTileParams {
   float2 *pair_partials;    // [R*gamma][n_tiles] (sum min, sum residual)
   const int4 *row_map;      // [R*gamma] (rho, k, x_{k-1}, target row) of compact row i
   // transition rows W1[x_{k-1}] of the product's rows, contiguous: [R][r]
-  // (draft, row = request) or [R*gamma][r] (verify, row = compact row)
+  // (draft, row = request) or [R*gamma][r] (verify, row = compact row);
+  // or, where a_tokens is set (draft), row i is W1[a_tokens[i]] read in place
   const void *A;
+  const int32_t *a_tokens;
 };
 
 enum class Epi { kDraft, kVerify };
@@ -99,10 +101,10 @@ template <> struct AFrag<float> {
 
 // Rows past the last real row read a clamped real row (finite values whose
 // outputs are discarded).
-__device__ __forceinline__ void load_afrag(const bf16_t *A, int r, int row, AFrag<bf16_t> &a,
+__device__ __forceinline__ void load_afrag(const bf16_t *Arow, int r, AFrag<bf16_t> &a,
                                            int ks_static) {
   const int lane = threadIdx.x & (kWave - 1);
-  const bf16_t *ptr = A + (int64_t)row * r + (lane >> 5) * 8;
+  const bf16_t *ptr = Arow + (lane >> 5) * 8;
   const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int ks = 0; ks < AFrag<bf16_t>::kSteps; ++ks) {
@@ -112,10 +114,10 @@ __device__ __forceinline__ void load_afrag(const bf16_t *A, int r, int row, AFra
     a.v[ks] = in ? t : zero;
   }
 }
-__device__ __forceinline__ void load_afrag(const float *A, int r, int row, AFrag<float> &a,
+__device__ __forceinline__ void load_afrag(const float *Arow, int r, AFrag<float> &a,
                                            int ks_static) {
   const int lane = threadIdx.x & (kWave - 1);
-  const float *ptr = A + (int64_t)row * r + (lane >> 5);
+  const float *ptr = Arow + (lane >> 5);
 #pragma unroll
   for (int ks = 0; ks < AFrag<float>::kSteps; ++ks) {
     const bool in = ks_static > 0 ? ks < ks_static : ks * 2 < r;
@@ -254,7 +256,17 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
     for (int rb = 0; rb < RB; ++rb) {
       const int rbase = rg * kRowGroup + (rb * NW + wave) * kRowsPerWave;
       // the A rows (product row = lane % 32 of the block)
-      load_afrag(Ab, r, min(rbase + (lane & 31), n_rows - 1), af[rb], KS);
+      const int arow = min(rbase + (lane & 31), n_rows - 1);
+      const T *aptr = Ab + (int64_t)arow * r;
+      if (p.a_tokens != nullptr) {
+        int tok = p.a_tokens[arow];
+        if (tok < 0 || tok >= V) {
+          flag_error(p.err, kErrToken);
+          tok = tok < 0 ? 0 : V - 1;
+        }
+        aptr = reinterpret_cast<const T *>(p.W1) + (int64_t)tok * r;
+      }
+      load_afrag(aptr, r, af[rb], KS);
       // this lane's epilogue row: source rows and statistics
       RowState &s = rs[rb];
       const int erow = rbase + erow_w;
@@ -503,6 +515,8 @@ __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, 
                                                  int V, int r, int tile, int row_in_block,
                                                  float *vout) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int col = tile * kTileN + wave * 32 + (lane & 31);
+  const float u = Elem<T>::at(Urow, min(col, V - 1));  // in flight with the W2 loads
   BFrag<T> bfr;
   load_bfrag(W2, V, r, tile * kTileN + wave * 32, bfr);
   floatx16 acc[1];
@@ -513,9 +527,8 @@ __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, 
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (e == reg) a = acc[0][e];
-    const int col = tile * kTileN + wave * 32 + (lane & 31);
     float v = -INFINITY;
-    if (col < V) v = a + Elem<T>::at(Urow, col);
+    if (col < V) v = a + u;
     vout[wave * 32 + (lane & 31)] = v;
   }
 }

@@ -8,10 +8,11 @@
 // (bit-identical to the fused kernel), and scans inside the tile.  Only the
 // 128-column tile is re-read, never the row.
 //
-// The transition rows W1[x_{k-1}] of step k sit in a contiguous [R][r] buffer
-// (A_k) written by the sampler of step k-1 (by a gather kernel for k = 1), so
-// the tile kernel loads them together with its W2 columns and U rows, with no
-// dependent token lookup in between.
+// The transition rows W1[x_{k-1}] of step k > 1 sit in a contiguous [R][r]
+// buffer (A_k) written by the sampler of step k-1, so the tile kernel loads
+// them together with its W2 columns and U rows, with no dependent token lookup
+// in between; step 1 reads W1[x0] in place (the anchors are known before the
+// launch, and the first launch saves a gather kernel).
 #include "bias_tile.h"
 #include "kernels.h"
 #include "trace.h"
@@ -23,6 +24,7 @@ struct SampleParams {
   float invT;
   const void *U, *W1, *W2;
   const void *A_cur;         // [R][r]: W1[x_{k-1}] of every request
+  const int32_t *a_tokens;   // or, if set, x_{k-1} (A_cur row rho = W1[a_tokens[rho]])
   void *A_next;              // [R][r]: receives W1[x_k] (NULL at the last step)
   int32_t *x;
   float *q_stats, *q_x;
@@ -59,6 +61,8 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   float2 pt[kCpt];
   {
     const T *Acur = reinterpret_cast<const T *>(p.A_cur) + (int64_t)rho * r;
+    if (p.a_tokens != nullptr)  // validated (and flagged) by the product kernel
+      Acur = reinterpret_cast<const T *>(p.W1) + (int64_t)min(max(p.a_tokens[rho], 0), V - 1) * r;
     uint4 a = make_uint4(0, 0, 0, 0);
     if (tid < pieces) a = *reinterpret_cast<const uint4 *>(Acur + tid * kPer);
     const float2 *ts = p.tile_stats + (int64_t)rho * nT;
@@ -191,26 +195,6 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   }
 }
 
-// rows[i] = W1[tokens[i]] for i < n (r elements each); tokens outside [0, V)
-// are flagged and clamped.  8 rows per workgroup, 32 threads per row.
-template <typename T>
-__global__ __launch_bounds__(kBlock) void gather_rows_kernel(int n, int V, int r, const T *W1,
-                                                             const int32_t *tokens, T *rows,
-                                                             int32_t *err) {
-  constexpr int kPer = 16 / (int)sizeof(T);
-  const int i = blockIdx.x * 8 + threadIdx.x / 32, pc = threadIdx.x & 31;
-  const int pieces = r * (int)sizeof(T) / 16;
-  if (i >= n) return;
-  int t = tokens[i];
-  if (t < 0 || t >= V) {
-    if (pc == 0) flag_error(err, kErrToken);
-    t = t < 0 ? 0 : V - 1;
-  }
-  if (pc < pieces)
-    *reinterpret_cast<uint4 *>(rows + (int64_t)i * r + pc * kPer) =
-        *reinterpret_cast<const uint4 *>(W1 + (int64_t)t * r + pc * kPer);
-}
-
 // sh[rho][k] = sum_j w[j] h[rho][k][j]: one wave per (rho, k), 16-byte loads.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, int d,
@@ -251,11 +235,9 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
                       n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh));
     sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
   }
+  // the first step reads its transition rows W1[x0] in place; the sampler of
+  // step k writes W1[x_k] contiguously for step k + 1
   void *A[2] = {L.A0, L.A1};
-  DSPARK_LAUNCH("gather_rows", stream,
-                gather_rows_kernel<T><<<(L.R + 7) / 8, kBlock, 0, stream>>>(
-                    L.R, L.V, L.r, reinterpret_cast<const T *>(L.W1), L.x0,
-                    reinterpret_cast<T *>(A[0]), L.err));
   // row groups of 32 NW requests x vocabulary tiles, in equal contiguous ranges
   // over one workgroup per compute unit: 4 waves up to 128 requests, else 8
   const bool wide = L.R > 4 * kRowsPerWave;
@@ -264,8 +246,10 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   for (int k = 1; k <= L.gamma; ++k) {
     bp.k = k;
     bp.A = A[(k - 1) & 1];
+    bp.a_tokens = k == 1 ? L.x0 : nullptr;
     sp.k = k;
     sp.A_cur = A[(k - 1) & 1];
+    sp.a_tokens = k == 1 ? L.x0 : nullptr;
     sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
     if (wide) {
       DSPARK_LAUNCH("bias_tile_draft", stream,
