@@ -498,15 +498,16 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   // compute unit) takes an equal share of the (row group, tile) items it
   // finds there
   const int grid = kComputeUnits;
-  // row groups of 128 rows (4 waves x 1 row block; measured faster than
-  // 8 waves or 3 row blocks per wave)
+  // row groups of 256 rows (8 waves x 1 row block: each W2 block in LDS serves
+  // twice the rows of a 4-wave group; measured faster than 4 waves and than 2
+  // or 3 row blocks per wave)
   if (L.r == (L.bf16 ? kMaxRank : 128)) {
     DSPARK_LAUNCH("bias_tile_verify", stream,
-                  (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64, 4, 1>
-                   <<<grid, 4 * kWave, 0, stream>>>(bp)));
+                  (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64, 8, 1>
+                   <<<grid, 8 * kWave, 0, stream>>>(bp)));
   } else {
     DSPARK_LAUNCH("bias_tile_verify", stream,
-                  (stream_tile_kernel<T, Epi::kVerify, 0, 4, 1><<<grid, 4 * kWave, 0, stream>>>(bp)));
+                  (stream_tile_kernel<T, Epi::kVerify, 0, 8, 1><<<grid, 8 * kWave, 0, stream>>>(bp)));
   }
 
   FinalizeParams fp{};
