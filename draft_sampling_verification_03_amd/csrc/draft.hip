@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   __shared__ __align__(16) T arow[kMaxRank + 16];
   __shared__ float red_max[4], red_sum[4];
   __shared__ int red_found[4], red_last[4];
-  __shared__ float s_before, s_mt;
+  __shared__ float s_before, s_mt, s_u;
   __shared__ int s_token;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -68,6 +68,9 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     const float2 *ts = p.tile_stats + (int64_t)rho * nT;
 #pragma unroll
     for (int j = 0; j < kCpt; ++j) pt[j] = t0 + j < t1 ? ts[t0 + j] : make_float2(-INFINITY, 0.0f);
+    // the draw's uniform (a scalar Philox chain) is formed while the loads
+    // are in flight: the LDS store keeps it ahead of the first barrier
+    if (tid == 0) s_u = uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamDraft);
     if (tid < pieces) *reinterpret_cast<uint4 *>(arow + tid * kPer) = a;
   }
   // 2. row maximum, then tile masses w_t = s_t exp(m_t - m) and their
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   // 3. the tile holding the draw: the first tile whose cumulative mass
   //    exceeds u * S (else, rounding having left no crossing, the last tile
   //    with mass)
-  const float u = uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamDraft);
+  const float u = s_u;
   const float target = u * S;
   int found = 0x7fffffff, lastpos = -1;
   {

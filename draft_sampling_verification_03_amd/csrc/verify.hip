@@ -271,6 +271,7 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   __shared__ float s_before;
   __shared__ float2 s_ps[kMaxGamma + 1];  // (m_p, S_p) of the request's target rows
   __shared__ int s_x[kMaxGamma];          // its draft tokens
+  __shared__ float s_ufin[kMaxGamma + 1];  // final-token uniform of each position
 
   constexpr int kTpt = kMaxTiles / kBlock;  // tiles per thread, at most
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -315,6 +316,13 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   const float tx = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)prow * V,
                                test ? xk : 0);
 
+  // ---- the Philox uniforms (long integer chains) while the loads are in
+  //      flight: the accept test of position k = tid + 1, and the final draw
+  //      at each position it could land on (the LDS store keeps it here)
+  const float u_acc = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamAccept);
+  if (tid <= gamma)
+    s_ufin[tid] = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamFinal);
+
   // ---- c*_k = sum over tiles of sum_v min(p, q) in tile order: wave w takes
   //      k = w + 1, w + 5, ... two at a time, every tile load in flight
   //      (clamped past n_tiles, masked in the sum)
@@ -358,15 +366,14 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
     if (xk_raw != xk) flag_error(p.err, kErrToken);
     const int k = tid + 1;
     const double pk = exp((double)(tx * p.invT) - (double)ps_own.x) / (double)ps_own.y;
-    const double u = (double)uniform01(p.seed, p.round, (uint64_t)k, (uint64_t)rho, kStreamAccept);
-    if (!(u * (double)qk < pk)) rej = k;
+    if (!((double)u_acc * (double)qk < pk)) rej = k;
   }
   rej = block_min_int(rej, ired);  // its barriers also publish s_ps and s_x
   const int n = rej == 0x7fffffff ? ell : rej - 1;
   const int j = n + 1;             // position of the final token
   const int frow = base + n;       // its target row
   const float2 ps = s_ps[n];
-  const float uf = uniform01(p.seed, p.round, (uint64_t)j, (uint64_t)rho, kStreamFinal);
+  const float uf = s_ufin[n];  // position j = n + 1
   const T *Prow = reinterpret_cast<const T *>(p.P) + (int64_t)frow * V;
   int final_token = 0;
 
