@@ -75,6 +75,8 @@ def test_tiny_config_other_rounds(rnd):
     dict(R=6, gamma=4, V=2048, dtype=synth.BF16, r=32, target_sd=3.0, weight_sd=0.05),
     dict(R=4, gamma=5, V=1024, dtype=synth.BF16, r=256, weight_sd=0.05),
     dict(R=4, gamma=4, V=1024, r=128),              # fp32 rank limit
+    dict(R=5, gamma=64, V=1024),                    # the longest block
+    dict(R=128, gamma=64, V=264),                   # the largest candidate count, 8192
 ])
 def test_edge_shapes(over):
     cfg = synth.make_config(1, cid=50 + len(_cache), **over)
