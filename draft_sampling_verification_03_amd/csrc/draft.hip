@@ -46,7 +46,6 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   __shared__ float red_max[4], red_sum[4];
   __shared__ int red_found[4], red_last[4];
   __shared__ float s_before, s_mt, s_u;
-  __shared__ int s_token;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rho = blockIdx.x, k = p.k, V = p.V, r = p.r, nT = p.n_tiles;
@@ -166,13 +165,20 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       if (pick < 0) pick = 0;
     }
     const float zp = __shfl(pick & 1 ? z1 : z0, pick >> 1);
+    const int xk = tstar * kTileN + pick;  // in [0, V): a picked column has positive mass
     if (lane == 0) {
-      const int xk = tstar * kTileN + pick;
       p.x[slot] = finite ? xk : -1;
       p.q_stats[2 * slot] = m;
       p.q_stats[2 * slot + 1] = S;
       p.q_x[slot] = fexp(zp - m) / S;
-      s_token = xk;  // in [0, V): a picked column always has positive mass
+    }
+    // 7. the next step's transition row A_{k+1}[rho] = W1[x_k], by this wave
+    //    (no barrier: the token is in its registers)
+    if (p.A_next != nullptr && lane < pieces) {
+      const int xc = min(max(xk, 0), V - 1);
+      *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_next) + (int64_t)rho * r + lane * kPer) =
+          *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) + (int64_t)xc * r +
+                                           lane * kPer);
     }
   }
 
@@ -185,16 +191,6 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       const float s = p.sh[slot] + acc + p.b_conf;
       p.c[slot] = 1.0f / (1.0f + expf(-s));
     }
-  }
-
-  // 7. the next step's transition row: A_{k+1}[rho] = W1[x_k]
-  if (p.A_next != nullptr) {
-    __syncthreads();
-    const int xk = min(max(s_token, 0), V - 1);
-    if (tid < pieces)
-      *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_next) + (int64_t)rho * r + tid * kPer) =
-          *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) + (int64_t)xk * r +
-                                           tid * kPer);
   }
 }
 
