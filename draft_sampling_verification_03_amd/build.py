@@ -17,8 +17,12 @@ ARCH = os.environ.get("DSPARK_OFFLOAD_ARCH", "gfx950")
 
 
 def _flags():
+    # -amdgpu-mfma-vgpr-form: matrix-core results land in ordinary vector
+    # registers, so the epilogue of one block need not wait for a copy out of
+    # the accumulation registers of the next block's product
     return ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-parameter", "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -142,13 +142,27 @@ __device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned
   const int c = lane & 31;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  if constexpr (KS > 0) {
+    // every B operand read first, then the products: with the reads
+    // interleaved two at a time the LDS latency was exposed between pairs
+    u16x8 b[KS];
 #pragma unroll
-  for (int ks = 0; ks < (KS > 0 ? KS : AFrag<bf16_t>::kSteps); ++ks) {
-    if (KS > 0 || ks * 16 < r) {
-      const u16x8 b = *reinterpret_cast<const u16x8 *>(
-          stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
+    for (int ks = 0; ks < KS; ++ks)
+      b[ks] = *reinterpret_cast<const u16x8 *>(stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
-                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+                                                    __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < AFrag<bf16_t>::kSteps; ++ks) {
+      if (ks * 16 < r) {
+        const u16x8 b = *reinterpret_cast<const u16x8 *>(
+            stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      }
     }
   }
 }
