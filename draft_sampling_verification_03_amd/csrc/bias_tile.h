@@ -134,15 +134,17 @@ __device__ __forceinline__ int w2_slot(int c, int pc) { return c * kColPitch + p
 // Product of one wave's 32 rows with one W2 block from LDS.  K advances in
 // increasing order from a zero accumulator with the same instruction as
 // mma_rows, the A operand in registers and the B operand in LDS: the same
-// element comes out of the same instruction sequence.
-template <int KS>
+// element comes out of the same instruction sequence.  kInterleave keeps each
+// B read next to its product (the verify pass, whose eight waves per
+// workgroup hide the LDS latency themselves, runs faster that way).
+template <int KS, bool kInterleave = false>
 __device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned char *stage,
                                           int r, floatx16 &acc) {
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane & 31;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  if constexpr (KS > 0) {
+  if constexpr (KS > 0 && !kInterleave) {
     // every B operand read first, then the products: with the reads
     // interleaved two at a time the LDS latency was exposed between pairs
     u16x8 b[KS];
@@ -156,8 +158,8 @@ __device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned
                                                     __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
   } else {
 #pragma unroll
-    for (int ks = 0; ks < AFrag<bf16_t>::kSteps; ++ks) {
-      if (ks * 16 < r) {
+    for (int ks = 0; ks < (KS > 0 ? KS : AFrag<bf16_t>::kSteps); ++ks) {
+      if (KS > 0 || ks * 16 < r) {
         const u16x8 b = *reinterpret_cast<const u16x8 *>(
             stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
@@ -166,7 +168,7 @@ __device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned
     }
   }
 }
-template <int KS>
+template <int KS, bool kInterleave = false>
 __device__ __forceinline__ void mma_block(const AFrag<float> &a, const unsigned char *stage,
                                           int r, floatx16 &acc) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -473,13 +475,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
     __syncthreads();  // blocks 0 and 1 in LDS
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      if (rs[rb].wave_live) mma_block<KS>(af[rb], w2s[0], r, acc0[rb]);
+      if (rs[rb].wave_live) mma_block<KS, kVerify>(af[rb], w2s[0], r, acc0[rb]);
     auto step = [&](int j, bool masked, WRegs &wst, URegs &ucur, floatx16 (&acc_j)[RB],
                     floatx16 (&acc_n)[RB]) __attribute__((always_inline)) {
       __syncthreads();  // block j + 1 in stage (j + 1) & 1; stage j & 1 is free
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (rs[rb].wave_live) mma_block<KS>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
+        if (rs[rb].wave_live) mma_block<KS, kVerify>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
       store_w(j & 1, wst);  // block j + 2
       load_w(wst, j + 4);
 #pragma unroll
