@@ -71,10 +71,13 @@ enum class Epi { kDraft, kVerify };
 // use, written to one half of a double-buffered LDS stage (a padded column
 // pitch keeps the operand reads free of bank conflicts), and read by all
 // waves.  U (and P) row segments stream into a register ring two blocks
-// ahead.  After the product a wave transposes its 32x32 accumulator through
-// its own LDS scratch so that each lane holds 16 consecutive columns of one
-// row, adds U, and folds the block into running per-row sums; the partials of
-// finished tiles are buffered in LDS and written every kFlushTiles tiles.
+// ahead.  The epilogue works on 16 consecutive columns of one row per lane:
+// the draft step puts W2 first in the product (columns in the order
+// block_col_of_m), so each lane's accumulator already holds them; the verify
+// pass puts the rows first and transposes its accumulator through the wave's
+// own LDS scratch (its longer epilogue ran faster that way).  U is added, the
+// block is folded into running per-row sums, and the partials of finished
+// tiles are buffered in LDS and written every kFlushTiles tiles.
 //
 // The loop body covers one tile (4 blocks) with a fixed instruction sequence
 // (loads past the range are clamped), so the waits the compiler inserts count
@@ -85,7 +88,7 @@ constexpr int kBlocksPerTile = kTileN / kBlockCols;     // 4
 constexpr int kColPieces = kMaxRank * 2 / 16;           // 16-byte pieces per W2 column (max)
 constexpr int kColPitch = kColPieces + 1;               // pieces per LDS column: one of padding
 constexpr int kStageBytes = kBlockCols * kColPitch * 16;  // one W2 block in LDS: 16.5 KB
-constexpr int kScratchPitch = 36;                       // floats per scratch row
+constexpr int kScratchPitch = 36;                       // floats per scratch row (rows first)
 constexpr int kFlushTiles = 8;                          // tile partials kept in LDS
 
 // the A operand of one wave's 32 rows, all K
@@ -126,61 +129,76 @@ __device__ __forceinline__ void load_afrag(const float *Arow, int r, AFrag<float
   }
 }
 
-// 16-byte piece pc of column c of a W2 block in LDS.  The column pitch of
-// kColPitch (odd) pieces puts the same piece of 16 consecutive columns in 16
-// different bank groups, and keeps every offset within a column affine.
-__device__ __forceinline__ int w2_slot(int c, int pc) { return c * kColPitch + pc; }
+// 16-byte piece pc of the W2 column in LDS slot m of a block.  Lane l reads
+// slot l % 32 for its operand: with W2 first a block is stored in matrix-row
+// order (column c in slot block_m_of_col(c)), rows first in column order.  The
+// pitch of kColPitch (odd) pieces puts the same piece of 16 consecutive slots
+// in 16 different bank groups, and keeps every offset within a column affine.
+__device__ __forceinline__ int w2_slot(int m, int pc) { return m * kColPitch + pc; }
+template <bool kW2First> __device__ __forceinline__ int w2_slot_of_col(int c) {
+  return kW2First ? block_m_of_col(c) : c;
+}
 
-// Product of one wave's 32 rows with one W2 block from LDS.  K advances in
-// increasing order from a zero accumulator with the same instruction as
-// mma_rows, the A operand in registers and the B operand in LDS: the same
-// element comes out of the same instruction sequence.  kInterleave keeps each
-// B read next to its product (the verify pass, whose eight waves per
-// workgroup hide the LDS latency themselves, runs faster that way).
-template <int KS, bool kInterleave = false>
+template <bool kW2First>
+__device__ __forceinline__ floatx16 mfma16(const u16x8 &w2, const u16x8 &rows, const floatx16 &c) {
+  if constexpr (kW2First)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w2),
+                                                   __builtin_bit_cast(bf16x8, rows), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, rows),
+                                                   __builtin_bit_cast(bf16x8, w2), c, 0, 0, 0);
+}
+
+// Product of one W2 block from LDS with one wave's 32 rows (A operand in
+// registers).  K advances in increasing order from a zero accumulator with the
+// same instruction and operand order as mma_rows<kW2First>: the same element
+// comes out of the same instruction sequence.  With W2 first (the draft step)
+// every W2 read of the block is issued before the products: interleaved two
+// at a time, the LDS latency was exposed between pairs.  Rows first (the
+// verify pass, eight waves per workgroup) keeps each read next to its product,
+// which measured faster there.
+template <int KS, bool kW2First>
 __device__ __forceinline__ void mma_block(const AFrag<bf16_t> &a, const unsigned char *stage,
                                           int r, floatx16 &acc) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int c = lane & 31;
+  const int m = lane & 31;  // LDS slot of this lane's W2 column
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  if constexpr (KS > 0 && !kInterleave) {
-    // every B operand read first, then the products: with the reads
-    // interleaved two at a time the LDS latency was exposed between pairs
+  if constexpr (KS > 0 && kW2First) {
     u16x8 b[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      b[ks] = *reinterpret_cast<const u16x8 *>(stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
+      b[ks] = *reinterpret_cast<const u16x8 *>(stage + 16 * w2_slot(m, 2 * ks + (lane >> 5)));
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
-                                                    __builtin_bit_cast(bf16x8, b[ks]), acc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16<kW2First>(b[ks], a.v[ks], acc);
   } else {
 #pragma unroll
     for (int ks = 0; ks < (KS > 0 ? KS : AFrag<bf16_t>::kSteps); ++ks) {
       if (KS > 0 || ks * 16 < r) {
         const u16x8 b = *reinterpret_cast<const u16x8 *>(
-            stage + 16 * w2_slot(c, 2 * ks + (lane >> 5)));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[ks]),
-                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+            stage + 16 * w2_slot(m, 2 * ks + (lane >> 5)));
+        acc = mfma16<kW2First>(b, a.v[ks], acc);
       }
     }
   }
 }
-template <int KS, bool kInterleave = false>
+template <int KS, bool kW2First>
 __device__ __forceinline__ void mma_block(const AFrag<float> &a, const unsigned char *stage,
                                           int r, floatx16 &acc) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int c = lane & 31;
+  const int m = lane & 31;  // LDS slot of this lane's W2 column
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < (KS > 0 ? KS : AFrag<float>::kSteps); ++ks) {
     if (KS > 0 || ks * 2 < r) {
       const int k = 2 * ks + (lane >> 5);
-      const float b = *reinterpret_cast<const float *>(stage + 16 * w2_slot(c, 0) + 4 * k);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[ks], b, acc, 0, 0, 0);
+      const float b = *reinterpret_cast<const float *>(stage + 16 * w2_slot(m, 0) + 4 * k);
+      if constexpr (kW2First)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(b, a.v[ks], acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[ks], b, acc, 0, 0, 0);
     }
   }
 }
@@ -188,6 +206,11 @@ __device__ __forceinline__ void mma_block(const AFrag<float> &a, const unsigned 
 // exchange with the neighbouring lane (l ^ 1)
 __device__ __forceinline__ float pair_swap(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+// exchange with the lane holding the other half of the row (l ^ 32)
+__device__ __forceinline__ float half_swap(float x) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(x)));
 }
 
 // log2 of a probability exp(x / T - m) / S from a logit x before the
@@ -205,6 +228,7 @@ __device__ __forceinline__ float log2_prob(float x, float invT, float m, float l
 template <typename T, Epi E, int KS, int NW, int RB>
 __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTileParams p) {
   constexpr bool kVerify = E == Epi::kVerify;
+  constexpr bool kW2First = !kVerify;  // operand order of the product
   constexpr int kThreads = NW * kWave;
   constexpr int kRowGroup = NW * RB * kRowsPerWave;
   constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte piece
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
   constexpr int kTpc = kThreads / kBlockCols;  // threads per W2 column of a block
   constexpr int kWPieces = kColPieces / kTpc;  // W2 pieces per thread per block
   __shared__ __align__(16) unsigned char w2s[2][kStageBytes];
-  __shared__ __align__(16) float scratch[NW][32 * kScratchPitch];
+  __shared__ __align__(16) float scratch[kW2First ? 1 : NW][kW2First ? 1 : 32 * kScratchPitch];
   __shared__ float2 pbuf[kRowGroup][kFlushTiles];  // partials of the last tiles, by row
   __shared__ int pout[kRowGroup];                  // output row of each row, -1 for none
 
@@ -243,9 +267,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
   const T *W2 = reinterpret_cast<const T *>(p.W2);
   const T *U = reinterpret_cast<const T *>(p.U);
   const T *P = reinterpret_cast<const T *>(p.P);
-  float *ws = scratch[wave];
-  const int erow_w = lane >> 1;          // epilogue row within a 32-row block
-  const int ec0 = (lane & 1) * 16;       // first epilogue column within the block
+  float *ws = scratch[kW2First ? 0 : wave];
+  // epilogue row within a 32-row block, its first column within the block, and
+  // whether this lane is the first of the two that hold the row
+  const int erow_w = kW2First ? lane & 31 : lane >> 1;
+  const int ec0 = kW2First ? (lane >> 5) * 16 : (lane & 1) * 16;
+  const bool row_lead = kW2First ? (lane >> 5) == 0 : (lane & 1) == 0;
   bool bad_entry = false;
 
   // per row block of this wave: block b = rb * NW + wave of the row group
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
       } else {
         if (s.live) { rho = erow; k = p.k; }
       }
-      if ((lane & 1) == 0) pout[s.slot] = s.live ? erow : -1;
+      if (row_lead) pout[s.slot] = s.live ? erow : -1;
       s.Urow = U + ((int64_t)rho * p.gamma + (k - 1)) * V;
       s.Prow = P + (int64_t)prow * V;
       s.mq = s.lq = s.mp = s.lp = 0.0f;
@@ -331,7 +358,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
         wr.w[i] = *reinterpret_cast<const u32x4 *>(src + min(wp + kTpc * i, npieces - 1) * kPer);
     };
     auto store_w = [&](int stage, const WRegs &wr) __attribute__((always_inline)) {
-      unsigned char *dst = w2s[stage] + 16 * w2_slot(wc, wp);
+      unsigned char *dst = w2s[stage] + 16 * w2_slot(w2_slot_of_col<kW2First>(wc), wp);
 #pragma unroll
       for (int i = 0; i < kWPieces; ++i)
         if (KS > 0 ? kTpc * i < npieces : wp + kTpc * i < npieces)
@@ -352,24 +379,37 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
         }
     };
 
-    // ---- epilogue of block j for row block rb: transpose the product
-    //      through the wave's scratch, add U, fold into the running sums
+    // ---- epilogue of block j for row block rb: (rows first: transpose the
+    //      product through the wave's scratch), add U, fold into the running
+    //      sums
     auto epilogue = [&](int j, int rb, const floatx16 &acc, const URegs &ur,
                         auto mask_tag) __attribute__((always_inline)) {
       constexpr bool kMask = decltype(mask_tag)::value;
       RowState &s = rs[rb];
-      wave_sync();  // the previous block's reads of the scratch are done
+      if constexpr (!kW2First) {
+        wave_sync();  // the previous block's reads of the scratch are done
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        ws[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * kScratchPitch + (lane & 31)] = acc[e];
-      wave_sync();  // the other lanes' accumulators are in the scratch
-      const int col0 = (cb0 + j) * kBlockCols + ec0;
+        for (int e = 0; e < 16; ++e)
+          ws[(8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * kScratchPitch + (lane & 31)] = acc[e];
+        wave_sync();  // the other lanes' accumulators are in the scratch
+      }
       const float *srow = ws + erow_w * kScratchPitch + ec0;
+      // product values of columns c..c+3 of this lane's row
+      auto prod4 = [&](int c) __attribute__((always_inline)) {
+        if constexpr (kW2First) {
+          floatx4 c4;
+          c4[0] = acc[c]; c4[1] = acc[c + 1]; c4[2] = acc[c + 2]; c4[3] = acc[c + 3];
+          return c4;
+        } else {
+          return *reinterpret_cast<const floatx4 *>(srow + c);
+        }
+      };
+      const int col0 = (cb0 + j) * kBlockCols + ec0;
       if constexpr (!kVerify) {
         float v[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const floatx4 c4 = *reinterpret_cast<const floatx4 *>(srow + 4 * q);
+          const floatx4 c4 = prod4(4 * q);
           v[4 * q] = c4[0]; v[4 * q + 1] = c4[1]; v[4 * q + 2] = c4[2]; v[4 * q + 3] = c4[3];
         }
 #pragma unroll
@@ -404,7 +444,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
           unpack16(ur.t[rb][i], (T *)nullptr, t);
 #pragma unroll
           for (int q4 = 0; q4 < kPer; q4 += 4) {
-            const floatx4 c4 = *reinterpret_cast<const floatx4 *>(srow + i * kPer + q4);
+            const floatx4 c4 = prod4(i * kPer + q4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int q = q4 + e, c = i * kPer + q;
@@ -420,7 +460,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
         }
       }
     };
-    // ---- end of a tile: combine the lane pair of each row into the LDS
+    // ---- end of a tile: combine the two lanes of each row into the LDS
     //      partial buffer, reset; every kFlushTiles tiles the buffer goes out
     auto tile_end = [&](int tl) __attribute__((always_inline)) {
 #pragma unroll
@@ -428,7 +468,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
         RowState &s = rs[rb];
         float2 o;
         if constexpr (!kVerify) {
-          const float om = pair_swap(s.run_m), os = pair_swap(s.run_s);
+          const float om = kW2First ? half_swap(s.run_m) : pair_swap(s.run_m);
+          const float os = kW2First ? half_swap(s.run_s) : pair_swap(s.run_s);
           const float M = fmaxf(s.run_m, om);
           float S = 0.0f;
           if (M != -INFINITY)
@@ -437,10 +478,12 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
           s.run_m = -INFINITY;
           s.run_s = 0.0f;
         } else {
-          o = make_float2(s.run_min + pair_swap(s.run_min), s.run_res + pair_swap(s.run_res));
+          const float omin = kW2First ? half_swap(s.run_min) : pair_swap(s.run_min);
+          const float ores = kW2First ? half_swap(s.run_res) : pair_swap(s.run_res);
+          o = make_float2(s.run_min + omin, s.run_res + ores);
           s.run_min = s.run_res = 0.0f;
         }
-        if ((lane & 1) == 0) pbuf[s.slot][tl % kFlushTiles] = o;
+        if (row_lead) pbuf[s.slot][tl % kFlushTiles] = o;
       }
     };
     auto flush = [&](int tl) __attribute__((always_inline)) {
@@ -475,13 +518,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
     __syncthreads();  // blocks 0 and 1 in LDS
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
-      if (rs[rb].wave_live) mma_block<KS, kVerify>(af[rb], w2s[0], r, acc0[rb]);
+      if (rs[rb].wave_live) mma_block<KS, kW2First>(af[rb], w2s[0], r, acc0[rb]);
     auto step = [&](int j, bool masked, WRegs &wst, URegs &ucur, floatx16 (&acc_j)[RB],
                     floatx16 (&acc_n)[RB]) __attribute__((always_inline)) {
       __syncthreads();  // block j + 1 in stage (j + 1) & 1; stage j & 1 is free
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        if (rs[rb].wave_live) mma_block<KS, kVerify>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
+        if (rs[rb].wave_live) mma_block<KS, kW2First>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
       store_w(j & 1, wst);  // block j + 2
       load_w(wst, j + 4);
 #pragma unroll
@@ -539,33 +582,63 @@ inline int stream_tile_grid(int total_items, int max_groups) {
 }
 
 // v = acc + U (before the temperature) of one row over one vocabulary tile,
-// formed by the same instruction sequence as stream_tile_kernel: the row's A
-// operand from LDS (ldsArow: r elements; every position of the 32-row block
-// reads it, and the row is taken from position row_in_block = its row index
-// mod 32, where stream_tile_kernel had it), W2 columns from global memory, K in
+// formed by the same instruction sequence as stream_tile_kernel with the same
+// operand order: W2 columns from global memory (W2 first: in the order
+// block_col_of_m), the row's A operand from LDS (ldsArow: r elements) read by
+// every row position of the block, the result taken from position
+// row_in_block = the row's index mod 32, where stream_tile_kernel had it; K in
 // increasing order from a zero accumulator.  Called by all 256 threads; wave w
 // produces columns 32w..32w+31 of the tile.  Writes v (or -inf past V) to
 // vout[0..127].
-template <typename T>
+template <typename T, bool kW2First>
 __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, const T *Urow,
                                                  int V, int r, int tile, int row_in_block,
                                                  float *vout) {
+  constexpr int kPer = 16 / (int)sizeof(T);  // elements per 16-byte piece
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int col = tile * kTileN + wave * 32 + (lane & 31);
-  const float u = Elem<T>::at(Urow, min(col, V - 1));  // in flight with the W2 loads
-  BFrag<T> bfr;
-  load_bfrag(W2, V, r, tile * kTileN + wave * 32, bfr);
-  floatx16 acc[1];
-  mma_rows<1>(ldsArow, 0, 0, r, bfr, acc);
-  const int reg = acc_reg_of_row(row_in_block);
-  if ((lane >> 5) == acc_half_of_row(row_in_block)) {
-    float a = 0.0f;
+  const int b0 = tile * kTileN + wave * 32;  // first column of this wave's block
+  if constexpr (kW2First) {
+    // lanes row_in_block and row_in_block + 32 end with columns
+    // b0 + 16 (l / 32) .. +15; their U pieces (a 16-byte piece is all in or
+    // all out of [0, V)) are in flight with the W2 loads
+    const int c0 = b0 + (lane >> 5) * 16;
+    u32x4 ur[16 / kPer];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (e == reg) a = acc[0][e];
-    float v = -INFINITY;
-    if (col < V) v = a + u;
-    vout[wave * 32 + (lane & 31)] = v;
+    for (int i = 0; i < 16 / kPer; ++i)
+      ur[i] = *reinterpret_cast<const u32x4 *>(Urow + min(c0 + i * kPer, V - kPer));
+    BFrag<T> bfr;
+    load_bfrag(W2, V, r, b0 + block_col_of_m(lane & 31), bfr);
+    floatx16 acc[1];
+    mma_rows<true, 1>(ldsArow, 0, 0, r, bfr, acc);
+    if ((lane & 31) == row_in_block) {
+#pragma unroll
+      for (int i = 0; i < 16 / kPer; ++i) {
+        float u[kPer];
+        unpack16(ur[i], (T *)nullptr, u);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int c = i * kPer + q;
+          vout[wave * 32 + (lane >> 5) * 16 + c] = c0 + c < V ? acc[0][c] + u[q] : -INFINITY;
+        }
+      }
+    }
+  } else {
+    // lane l (l % 32 = the column) holds the row in register
+    // acc_reg_of_row(row_in_block) of lane half acc_half_of_row(row_in_block)
+    const int col = b0 + (lane & 31);
+    const float u = Elem<T>::at(Urow, min(col, V - 1));  // in flight with the W2 loads
+    BFrag<T> bfr;
+    load_bfrag(W2, V, r, col, bfr);
+    floatx16 acc[1];
+    mma_rows<false, 1>(ldsArow, 0, 0, r, bfr, acc);
+    const int reg = acc_reg_of_row(row_in_block);
+    if ((lane >> 5) == acc_half_of_row(row_in_block)) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e == reg) a = acc[0][e];
+      vout[wave * 32 + (lane & 31)] = col < V ? a + u : -INFINITY;
+    }
   }
 }
 

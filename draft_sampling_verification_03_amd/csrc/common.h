@@ -226,16 +226,32 @@ template <typename T> __host__ __device__ constexpr int lds_pitch(int r) {
   return r + 16 / (int)sizeof(T);
 }
 
-// Matrix-core bias product.  A wave owns one 32-column block of a vocabulary
-// tile: its B operand (the r coefficients of each of the 32 W2 columns) is
-// loaded once into registers, all K at a time, and reused for every 32-row
-// block of A.  A rows come from LDS: row (a_row0 + 32 mb + lane % 32) at pitch
-// a_pitch (a_pitch = 0 makes every row read the same data).  K advances in
-// increasing order (bf16: one 32x32x16 MFMA per 16; fp32: one 32x32x2 MFMA per
-// 2) from a zero accumulator.  Every kernel that forms z uses these two
-// functions, so the same element always comes out of the same instruction
-// sequence.  Output element (row i, column j) of a 32x32 block is in lane
-// (j + 32 * ((i / 4) % 2)), register 4 * (i / 8) + i % 4.
+// Matrix-core bias product of a block of 32 A rows with 32 W2 columns, K
+// advancing in increasing order (bf16: one 32x32x16 MFMA per 16; fp32: one
+// 32x32x2 MFMA per 2) from a zero accumulator.  Output element (M index i,
+// N index j) of a 32x32 block is in lane j + 32 ((i / 4) % 2), register
+// 4 (i / 8) + i % 4.  Two operand orders are used:
+//   W2 first (kW2First): the columns are the M index, entered in the order
+//     block_col_of_m, the rows the N index; lane l then holds columns
+//     16 (l / 32) .. +15 of row l % 32 in registers 0..15, ready for a
+//     reduction over the row (the draft step);
+//   rows first: the rows are the M index, the columns the N index in natural
+//     order; lane l holds 16 rows of column l % 32 (the verify pass, which
+//     transposes through LDS).
+// Each product kernel and the recompute of its tiles issue the same sequence
+// with the same operand order, so the same element always comes out of the
+// same instructions.
+__host__ __device__ constexpr int block_col_of_m(int m) {
+  return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+}
+// its inverse: the matrix row that column c of a block feeds
+__host__ __device__ constexpr int block_m_of_col(int c) {
+  return 8 * ((c >> 2) & 3) + 4 * (c >> 4) + (c & 3);
+}
+// Rows first: row i (0..31) of a 32x32 accumulator block, lane half and register.
+__device__ __forceinline__ int acc_half_of_row(int i) { return (i >> 2) & 1; }
+__device__ __forceinline__ int acc_reg_of_row(int i) { return 4 * (i >> 3) + (i & 3); }
+
 template <typename T> struct BFrag;
 template <> struct BFrag<bf16_t> {
   static constexpr int kSteps = kMaxRank / 16;  // K = 16 per step
@@ -246,14 +262,15 @@ template <> struct BFrag<float> {
   float v[kSteps];
 };
 
-// Columns >= V read as zero.  Every load is issued unconditionally from a
-// clamped in-bounds address (no branches between them) and masked afterwards.
-__device__ __forceinline__ void load_bfrag(const bf16_t *W2, int V, int r, int b_col0,
+// The r coefficients of W2 column col (this lane's column) as an operand;
+// a column >= V reads as zero.  Every load is issued unconditionally
+// from a clamped in-bounds address (no branches between them) and masked
+// afterwards.
+__device__ __forceinline__ void load_bfrag(const bf16_t *W2, int V, int r, int col,
                                            BFrag<bf16_t> &b) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int v = b_col0 + (lane & 31);
-  const bool ok = v < V;
-  const bf16_t *ptr = W2 + (int64_t)(ok ? v : 0) * r + (lane >> 5) * 8;
+  const bool ok = col < V;
+  const bf16_t *ptr = W2 + (int64_t)(ok ? col : 0) * r + (lane >> 5) * 8;
   const u16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int ks = 0; ks < BFrag<bf16_t>::kSteps; ++ks) {
@@ -262,12 +279,11 @@ __device__ __forceinline__ void load_bfrag(const bf16_t *W2, int V, int r, int b
     b.v[ks] = (ok && ks * 16 < r) ? t : zero;
   }
 }
-__device__ __forceinline__ void load_bfrag(const float *W2, int V, int r, int b_col0,
+__device__ __forceinline__ void load_bfrag(const float *W2, int V, int r, int col,
                                            BFrag<float> &b) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int v = b_col0 + (lane & 31);
-  const bool ok = v < V;
-  const float *ptr = W2 + (int64_t)(ok ? v : 0) * r + (lane >> 5);
+  const bool ok = col < V;
+  const float *ptr = W2 + (int64_t)(ok ? col : 0) * r + (lane >> 5);
 #pragma unroll
   for (int ks = 0; ks < BFrag<float>::kSteps; ++ks) {
     const int kk = ks * 2 < r ? ks * 2 : r - 2;
@@ -280,7 +296,7 @@ __device__ __forceinline__ void load_bfrag(const float *W2, int V, int r, int b_
 // for fp32: no branch between the matrix-core instructions, so the LDS reads
 // of later steps are issued early); KS = 0 takes r at run time.  Both forms
 // issue the same instructions in the same order for the same r.
-template <int WMB, int KS = 0>
+template <bool kW2First, int WMB, int KS = 0>
 __device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_row0, int r,
                                          const BFrag<bf16_t> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -296,13 +312,17 @@ __device__ __forceinline__ void mma_rows(const bf16_t *ldsA, int a_pitch, int a_
       for (int mb = 0; mb < WMB; ++mb) {
         const u16x8 a = *reinterpret_cast<const u16x8 *>(
             ldsA + (a_row0 + 32 * mb + (lane & 31)) * a_pitch + ks * 16 + kq);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b.v[ks]), acc[mb], 0, 0, 0);
+        if constexpr (kW2First)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, b.v[ks]), __builtin_bit_cast(bf16x8, a), acc[mb], 0, 0, 0);
+        else
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b.v[ks]), acc[mb], 0, 0, 0);
       }
     }
   }
 }
-template <int WMB, int KS = 0>
+template <bool kW2First, int WMB, int KS = 0>
 __device__ __forceinline__ void mma_rows(const float *ldsA, int a_pitch, int a_row0, int r,
                                          const BFrag<float> &b, floatx16 (&acc)[WMB]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -317,7 +337,10 @@ __device__ __forceinline__ void mma_rows(const float *ldsA, int a_pitch, int a_r
 #pragma unroll
       for (int mb = 0; mb < WMB; ++mb) {
         const float a = ldsA[(a_row0 + 32 * mb + (lane & 31)) * a_pitch + ks * 2 + kq];
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b.v[ks], acc[mb], 0, 0, 0);
+        if constexpr (kW2First)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(b.v[ks], a, acc[mb], 0, 0, 0);
+        else
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b.v[ks], acc[mb], 0, 0, 0);
       }
     }
   }
@@ -366,9 +389,5 @@ __device__ __forceinline__ void stage_to_lds(const E *__restrict__ src, int n, E
     if (i < n) dst[i] = v[j];
   }
 }
-
-// Row i (0..31) of a 32x32 accumulator block: which lane half and register.
-__device__ __forceinline__ int acc_half_of_row(int i) { return (i >> 2) & 1; }
-__device__ __forceinline__ int acc_reg_of_row(int i) { return 4 * (i >> 3) + (i & 3); }
 
 }  // namespace dspark

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   // 4. recompute z of that tile, bit-identical to the fused kernel
   __syncthreads();
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
-  recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31, zbuf);
+  recompute_tile_v<T, true>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
+                            zbuf);
   __syncthreads();
 
   // 5. scan inside the tile (wave 0, two columns per lane, left to right);

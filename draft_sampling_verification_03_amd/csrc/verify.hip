@@ -404,8 +404,8 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
       const int col = tstar * kTileN + tid;
       const float tcol = tid < kTileN && col < V ? Elem<T>::at(Prow, col) : 0.0f;
       const T *Urow = reinterpret_cast<const T *>(p.U) + ((int64_t)rho * gamma + j - 1) * V;
-      recompute_tile_v<T>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
-                          (int)((d_off + j - 1) & 31), zbuf);
+      recompute_tile_v<T, false>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, p.r, tstar,
+                                 (int)((d_off + j - 1) & 31), zbuf);
       __syncthreads();
       if (tid < kTileN) {
         // (p - q)_+ = p - min(p, q), each term formed as in the verify pass
