@@ -538,6 +538,28 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
       }
       load_u(ucur, j + 2);
     };
+    // draft: no branch between the product of block j + 1 and the epilogue of
+    // block j (every wave runs both; a wave without live rows works on
+    // clamped rows and its results are dropped), so the scheduler can put a
+    // few epilogue instructions after each matrix instruction: they issue
+    // while the matrix core works (25.0 vs 26.4 us per draft step)
+    auto step_d = [&](int j, auto mask_tag, WRegs &wst, URegs &ucur, floatx16 (&acc_j)[RB],
+                      floatx16 (&acc_n)[RB]) __attribute__((always_inline)) {
+      __syncthreads();  // block j + 1 in stage (j + 1) & 1; stage j & 1 is free
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        mma_block<KS, kW2First>(af[rb], w2s[(j + 1) & 1], r, acc_n[rb]);
+      store_w(j & 1, wst);  // block j + 2
+      load_w(wst, j + 4);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) epilogue(j, rb, acc_j[rb], ucur, mask_tag);
+      load_u(ucur, j + 2);
+#pragma unroll
+      for (int i = 0; i < 16 * RB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector ALU
+      }
+    };
     if constexpr (kVerify) {
       // blocks in pairs (the register sets alternate with the block's parity)
       // with the tile's end checked after each block: half the code of the
@@ -557,16 +579,26 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
         }
       }
     } else {
+      // full tiles, then the range's last tile alone where it passes V
       const bool mask_last = (int64_t)(tile0 + ntile) * kTileN > V;
-      for (int tl = 0; tl < ntile; ++tl) {
-        const bool masked = mask_last && tl == ntile - 1;
+      const int nfull = ntile - (mask_last ? 1 : 0);
+      for (int tl = 0; tl < nfull; ++tl) {
         const int j = tl * kBlocksPerTile;
-        step(j, masked, wr0, ur0, acc0, acc1);
-        step(j + 1, masked, wr1, ur1, acc1, acc0);
-        step(j + 2, masked, wr0, ur0, acc0, acc1);
-        step(j + 3, masked, wr1, ur1, acc1, acc0);
+        step_d(j, std::false_type{}, wr0, ur0, acc0, acc1);
+        step_d(j + 1, std::false_type{}, wr1, ur1, acc1, acc0);
+        step_d(j + 2, std::false_type{}, wr0, ur0, acc0, acc1);
+        step_d(j + 3, std::false_type{}, wr1, ur1, acc1, acc0);
         tile_end(tl);
         if (tl % kFlushTiles == kFlushTiles - 1 || tl == ntile - 1) flush(tl);
+      }
+      if (mask_last) {
+        const int tl = ntile - 1, j = tl * kBlocksPerTile;
+        step_d(j, std::true_type{}, wr0, ur0, acc0, acc1);
+        step_d(j + 1, std::true_type{}, wr1, ur1, acc1, acc0);
+        step_d(j + 2, std::true_type{}, wr0, ur0, acc0, acc1);
+        step_d(j + 3, std::true_type{}, wr1, ur1, acc1, acc0);
+        tile_end(tl);
+        flush(tl);
       }
     }
   }
