@@ -253,10 +253,28 @@ __global__ __launch_bounds__(NW * kWave, 1) void stream_tile_kernel(BiasTilePara
   }
   if (n_rows <= 0) return;
   const int n_rg = (n_rows + kRowGroup - 1) / kRowGroup;
-  // Work: (row group, vocabulary tile) items in equal contiguous ranges,
-  // row-group major; one workgroup per compute unit.
+  // Work: (row group, vocabulary tile) items; one workgroup per compute unit.
   int t0, t1;
-  {
+  if (kVerify && n_rg > 1 && n_rg <= (int)gridDim.x / kXcds && gridDim.x % kXcds == 0) {
+    // Workgroups are dealt to the XCDs in turn (workgroup b on XCD b % 8), and
+    // each XCD has its own L2.  Groups of n_rg workgroups on one XCD take the
+    // same tile range, one row group each, so each W2 block comes from HBM
+    // about once per group rather than once per row group (fetched bytes
+    // 639 -> 539 MB on a long-block round); workgroups left over on an XCD
+    // stay idle.
+    const int per_xcd = (int)gridDim.x / kXcds;
+    const int x = (int)blockIdx.x % kXcds, li = (int)blockIdx.x / kXcds;
+    const int groups = per_xcd / n_rg;
+    const int g = li / n_rg, rg = li - g * n_rg;
+    if (g >= groups) {
+      t0 = t1 = 0;
+    } else {
+      const int nr = kXcds * groups, ri = g * kXcds + x;  // tile range of the group
+      t0 = rg * n_tiles + (int)((int64_t)ri * n_tiles / nr);
+      t1 = rg * n_tiles + (int)((int64_t)(ri + 1) * n_tiles / nr);
+    }
+  } else {
+    // equal contiguous ranges, row-group major
     const int total = n_rg * n_tiles;
     const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
     t0 = (int)blockIdx.x * per;

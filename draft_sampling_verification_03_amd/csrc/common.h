@@ -18,6 +18,7 @@ namespace dspark {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;          // threads of every workgroup
 constexpr int kTileN = 128;          // vocabulary columns per tile
+constexpr int kXcds = 8;             // accelerator complex dies, each with its own L2
 constexpr int kMaxTiles = 2048;      // V <= 262144
 constexpr int kMaxRank = 256;
 constexpr int kMaxGamma = 64;       // draft positions per request
