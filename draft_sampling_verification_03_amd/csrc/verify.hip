@@ -72,47 +72,62 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
 
   float M = -INFINITY, S = 0.0f;  // running (max of x, sum of 2^((x - M) cl))
   int rho = -1;                   // set for the last row of a request
-  bool looked_up = false;
-  for (int p0 = 0; p0 < npc; p0 += kBatch * kBlock) {
-    u32x4 raw[kBatch];
+  // rounds of kBatch pieces per thread, double-buffered: the loads of round
+  // i + 1 are in flight while round i is reduced (past the chunk they read
+  // its last piece again, and the results are not used)
+  constexpr int kRound = kBatch * kBlock;
+  auto issue = [&](u32x4 (&raw)[kBatch], int p0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
       raw[j] = ld_stream4(X + (int64_t)min(p0 + j * kBlock + tid, npc - 1) * kPer);
-    if (!looked_up) {
-      looked_up = true;
-      if (p.row_offset != nullptr) {
-        // request of the row: the last rho with row_offset[rho] <= row
-        int lo = 0, hi = p.R;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (p.row_offset[mid] <= row) lo = mid; else hi = mid;
+  };
+  u32x4 cur[kBatch], nxt[kBatch];
+  issue(cur, 0);
+  issue(nxt, kRound);
+  if (p.row_offset != nullptr) {
+    // request of the row: the last rho with row_offset[rho] <= row, as the
+    // number of rho in [1, R) with row_offset[rho] <= row (the offsets are
+    // nondecreasing), counted by every wave with ballots over loads that are
+    // all in flight at once (a binary search took one round trip per step)
+    const int lane = tid & (kWave - 1);
+    int lo = 0;
+    for (int t0 = 1; t0 < p.R; t0 += 4 * kWave) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u * kWave + lane;
+        const int o = p.row_offset[min(t, p.R)];
+        v[u] = t < p.R ? o : INT_MAX;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lo += __popcll(__ballot(v[u] <= row));
+    }
+    const int base = p.row_offset[lo];
+    if (p.row_offset[lo + 1] - 1 == row) {
+      rho = lo;  // the bonus position keeps tile partials
+    } else if (c == 0 && tid < 32) {
+      // a verified draft (k <= ell): its entry of the compact-row map and
+      // its transition row W1[x_{k-1}] for the verify pass
+      const int k = row - base + 1, i = row - lo;
+      if (k >= 1 && k <= p.gamma && i >= 0 && i < p.R * p.gamma) {
+        int prev = k == 1 ? p.x0[lo] : p.x[(int64_t)lo * p.gamma + k - 2];
+        if (prev < 0 || prev >= V) {
+          if (tid == 0) flag_error(p.err, kErrToken);
+          prev = prev < 0 ? 0 : V - 1;
         }
-        const int base = p.row_offset[lo];
-        if (p.row_offset[lo + 1] - 1 == row) {
-          rho = lo;  // the bonus position keeps tile partials
-        } else if (c == 0 && tid < 32) {
-          // a verified draft (k <= ell): its entry of the compact-row map and
-          // its transition row W1[x_{k-1}] for the verify pass
-          const int k = row - base + 1, i = row - lo;
-          if (k >= 1 && k <= p.gamma && i >= 0 && i < p.R * p.gamma) {
-            int prev = k == 1 ? p.x0[lo] : p.x[(int64_t)lo * p.gamma + k - 2];
-            if (prev < 0 || prev >= V) {
-              if (tid == 0) flag_error(p.err, kErrToken);
-              prev = prev < 0 ? 0 : V - 1;
-            }
-            if (tid == 0) p.row_map[i] = make_int4(lo, k, prev, row);
-            constexpr int kPerA = 16 / (int)sizeof(T);
-            if (tid < p.r * (int)sizeof(T) / 16)
-              *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r +
-                                         tid * kPerA) =
-                  *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
-                                                   (int64_t)prev * p.r + tid * kPerA);
-          } else if (tid == 0) {
-            flag_error(p.err, kErrLength);
-          }
-        }
+        if (tid == 0) p.row_map[i] = make_int4(lo, k, prev, row);
+        constexpr int kPerA = 16 / (int)sizeof(T);
+        if (tid < p.r * (int)sizeof(T) / 16)
+          *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r +
+                                     tid * kPerA) =
+              *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
+                                               (int64_t)prev * p.r + tid * kPerA);
+      } else if (tid == 0) {
+        flag_error(p.err, kErrLength);
       }
     }
+  }
+  auto reduce = [&](const u32x4 (&raw)[kBatch], int p0) __attribute__((always_inline)) {
     if (rho < 0) {
       float bm = -INFINITY;
 #pragma unroll
@@ -170,6 +185,12 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
         }
       }
     }
+  };
+  for (int p0 = 0; p0 < npc; p0 += 2 * kRound) {
+    reduce(cur, p0);
+    issue(cur, p0 + 2 * kRound);
+    if (p0 + kRound < npc) reduce(nxt, p0 + kRound);
+    issue(nxt, p0 + 3 * kRound);
   }
   // workgroup (max, sum): x-units, then m = x_max / T
   const float mx = block_max(M, red);
