@@ -89,10 +89,23 @@ __device__ __forceinline__ void flag_error(int32_t *err, int bits) {
 }
 
 // ------------------------------------------------------------------ reductions
+// Max and min over the wave: DPP steps within each row of 16 lanes (xor 1,
+// xor 2, then the mirrors within 8 and 16 lanes pair every lane with one of
+// the other half), after which each row is uniform; the four rows are read
+// back as scalars.  Exact in any order, and no LDS round trip per step.
+template <typename Op> __device__ __forceinline__ int dpp_rows_reduce(int v, Op op) {
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return op(op(a, b), op(c, d));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return __int_as_float(dpp_rows_reduce(__float_as_int(v), [](int x, int y) {
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  }));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -100,14 +113,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 __device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return dpp_rows_reduce(v, [](int x, int y) { return min(x, y); });
 }
 __device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  return dpp_rows_reduce(v, [](int x, int y) { return max(x, y); });
 }
 // reductions over groups of G consecutive lanes (G a power of two <= 64)
 template <int G> __device__ __forceinline__ float group_max(float v) {

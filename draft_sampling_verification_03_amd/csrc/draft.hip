@@ -131,12 +131,11 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       if (t0 + j < tstar) run += w[j];
       if (t0 + j == tstar) mt = pt[j].x;
     }
-    s_before = run;
+    s_before = run;  // read after the barrier that follows the recompute
     s_mt = mt;
   }
 
   // 4. recompute z of that tile, bit-identical to the fused kernel
-  __syncthreads();
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
   recompute_tile_v<T, true>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
                             zbuf);
