@@ -130,16 +130,24 @@ template <int G> __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// inclusive scan over the wave, lane order
+// inclusive scan over the wave, lane order: Hillis-Steele steps within each
+// row of 16 lanes by DPP row shifts (a lane without a source adds 0), then
+// the totals of rows 0 and 2 are added to rows 1 and 3 and the total of rows
+// 0-1 to rows 2 and 3 (DPP row broadcasts).  Fixed order: deterministic.
+template <int kCtrl, int kRowMask> __device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, true));
+}
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    float t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v += dpp_or_zero<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or_zero<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or_zero<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or_zero<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
+// the value of the previous lane (0 in lane 0): DPP wave_shr:1
+__device__ __forceinline__ float wave_prev_lane(float v) { return dpp_or_zero<0x138, 0xF>(v); }
 
 // Workgroup-wide reductions (kBlock threads); `scratch` holds >= 4 floats.
 __device__ __forceinline__ float block_max(float v, float *scratch) {

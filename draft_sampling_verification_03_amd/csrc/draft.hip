@@ -149,8 +149,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     const float z0 = zbuf[2 * lane] * p.invT, z1 = zbuf[2 * lane + 1] * p.invT;
     const float e0 = fexp(z0 - mt), e1 = fexp(z1 - mt);
     const float incl = wave_inclusive_scan(e0 + e1);
-    float exc = __shfl_up(incl, 1);
-    if (lane == 0) exc = 0.0f;
+    const float exc = wave_prev_lane(incl);
     const float cdf0 = s_before + scale * (exc + e0);
     const float cdf1 = s_before + scale * ((exc + e0) + e1);
     int pick = 0x7fffffff;

@@ -263,8 +263,7 @@ __device__ int pick_in_tile(const float *ebuf, float before, float scale, float 
   const int lane = threadIdx.x & (kWave - 1);
   const float e0 = ebuf[2 * lane], e1 = ebuf[2 * lane + 1];
   const float inc = wave_inclusive_scan(e0 + e1);
-  float exc = __shfl_up(inc, 1);
-  if (lane == 0) exc = 0.0f;
+  const float exc = wave_prev_lane(inc);
   const float cdf0 = before + scale * (exc + e0);
   const float cdf1 = before + scale * ((exc + e0) + e1);
   int pick = 0x7fffffff;
