@@ -127,7 +127,6 @@ def main():
     idx = np.concatenate([rho * (gamma + 1) + np.arange(int(ell[rho]) + 1) for rho in range(R)])
     P = torch.zeros((cfg.rows_capacity, V), dtype=dT.dtype, device=dev)
     P[: idx.size] = dT.index_select(0, torch.from_numpy(idx).to(dev))
-    del dT
     vout = None
 
     def schedule():
@@ -181,6 +180,37 @@ def main():
     assert np.array_equal(sout["ell"].cpu().numpy(), ell), "schedule changed during timing"
     errs = (wsd.error_code(), wss.error_code(), wsv.error_code())
     assert errs == (0, 0, 0), f"device error words {errs}"
+
+    # ---- the same workload with the scheduler off (ell = gamma for every request:
+    #      R * (1 + gamma) target rows, the flattened layout of all positions),
+    #      a figure that does not depend on the schedule; separate timed pass
+    wss_off, wsv_off = ds.Workspace(), ds.Workspace()
+    sout_off = ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off,
+                           stream=stream)
+    vout_off = None
+
+    def step_off():
+        nonlocal vout_off
+        draft()
+        ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off, stream=stream,
+                    out=sout_off)
+        vout_off = ds.verify(sout_off["ell"], sout_off["row_offset"], dT, dU, dW1, dW2, dx0,
+                             dout["x"], dout["q_stats"], dout["q_x"], temp=cfg.temp,
+                             seed=cfg.seed, round=cfg.round, ws=wsv_off, stream=stream,
+                             out=vout_off)
+
+    step_off()
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_off = max(1, args.steps // 2)
+    e2.record(stream)
+    for _ in range(n_off):
+        step_off()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    ms_off = e2.elapsed_time(e3) / n_off
+    rows_off = R * (gamma + 1)
+    assert wsv_off.error_code() == 0, "device error word set in the scheduler-off pass"
 
     # ---- per-kernel launch durations (HIP events on the launch stream, separate pass)
     ds.dspark_trace_enable(True)
@@ -305,6 +335,14 @@ def main():
                    "verify_rows": rows_used},
         "achieved_hbm_gbps": round(round_bytes / (ms_step / 1e3) / 1e9, 1),
         "round_bytes": int(round_bytes),
+        "draft_positions_per_s": round(positions / (t_draft / 1e3), 1),
+        "verify_rows_per_s": round(rows_used / (t_ver / 1e3), 1),
+        "scheduler_off": {"ms_per_step": round(ms_off, 4),
+                          "positions_per_s": round(positions / (ms_off / 1e3), 1),
+                          "verify_rows": rows_off,
+                          "achieved_hbm_gbps": round(
+                              (s_el * V * (R * gamma + R * gamma + rows_off) + 2 * s_el * r * V
+                               + (R * gamma * cfg.d * s_el if cfg.d else 0)) / (ms_off / 1e3) / 1e9, 1)},
         "breakdown_ms": {"draft": round(t_draft, 4), "schedule": round(t_sched, 4),
                          "verify": round(t_ver, 4)},
         "roofline": roof,
