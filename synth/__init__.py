@@ -250,3 +250,100 @@ def generate(cfg: Config, workers: int = 8, requests=None):
     with ThreadPoolExecutor(max(1, workers)) as ex:
         list(ex.map(one, range(len(reqs))))
     return U, T
+
+
+# ------------------------------------------------------------ multi-round loop
+# A prefix-dependent synthetic target for many rounds of decoding: a low-rank
+# Markov model whose next-token logits given the previous token are
+#     t(prev) = B + Wt1[prev, :] Wt2        (B [V], Wt1 [V][r], Wt2 r x V)
+# and a draft that resembles it: the draft head's factors are the target's
+# plus noise, and the draft backbone rows U_k of every round are B plus noise.
+# The target forward is the environment of the method, not part of it; it is
+# given here (fp32, numpy) so that the host can lay out the target rows that a
+# round's verify reads.
+_T_MB, _T_MW1, _T_MW2, _T_MD1, _T_MD2, _T_MU, _T_MC, _T_MX0 = range(100, 108)
+
+
+@dataclass
+class MarkovLoop:
+    R: int = 8
+    gamma: int = 4
+    V: int = 64
+    r: int = 16
+    dtype: int = F32
+    base_sd: float = 1.5       # B
+    factor_sd: float = 0.6     # Wt1, Wt2 entries
+    head_noise: float = 0.15   # draft head factors = target's + this * N(0, 1)
+    u_noise: float = 0.6       # U_k = B + this * N(0, 1)
+    conf: str = "beta:4:1"
+    sps: str = "tiny"
+    mode: int = SCHED_EARLY_STOP
+    temp: float = 1.0
+    seed: int = 7              # Philox key of the method's own draws
+    key: int = 0               # seed of the synthetic inputs
+
+    @property
+    def B_max(self):
+        return self.R * (1 + self.gamma)
+
+
+def _mrng(m: MarkovLoop, *ids):
+    return np.random.default_rng(np.random.SeedSequence([7000 + m.key, m.V, m.R, m.r, *ids]))
+
+
+def _mstore(m: MarkovLoop, x32: np.ndarray) -> np.ndarray:
+    return to_bf16_bits(x32) if m.dtype == BF16 else np.ascontiguousarray(x32, np.float32)
+
+
+def markov_target(m: MarkovLoop):
+    """(B [V], Wt1 [V][r], Wt2 stored [V][r] = r x V column-major), float32."""
+    B = m.base_sd * _mrng(m, _T_MB).standard_normal(m.V, dtype=np.float32)
+    W1t = m.factor_sd * _mrng(m, _T_MW1).standard_normal((m.V, m.r), dtype=np.float32)
+    W2t = m.factor_sd * _mrng(m, _T_MW2).standard_normal((m.V, m.r), dtype=np.float32)
+    return B, W1t, W2t
+
+
+def markov_target_rows(m: MarkovLoop, target, prev: np.ndarray) -> np.ndarray:
+    """Stored target rows t(prev[i]) for a list of previous tokens."""
+    B, W1t, W2t = target
+    prev = np.asarray(prev, dtype=np.int64)
+    t32 = B[None, :] + W1t[prev] @ W2t.T
+    return _mstore(m, t32.astype(np.float32))
+
+
+def markov_draft_head(m: MarkovLoop, target):
+    """Stored draft factors (W1 [V][r], W2 [V][r]): the target's plus noise."""
+    _, W1t, W2t = target
+    n1 = _mrng(m, _T_MD1).standard_normal((m.V, m.r), dtype=np.float32)
+    n2 = _mrng(m, _T_MD2).standard_normal((m.V, m.r), dtype=np.float32)
+    return _mstore(m, W1t + m.head_noise * n1), _mstore(m, W2t + m.head_noise * n2)
+
+
+def markov_U(m: MarkovLoop, target, t: int) -> np.ndarray:
+    """Draft backbone rows of round t: [R][gamma][V], B + noise."""
+    B = target[0]
+    n = _mrng(m, _T_MU, t).standard_normal((m.R, m.gamma, m.V), dtype=np.float32)
+    return _mstore(m, B[None, None, :] + m.u_noise * n)
+
+
+def markov_confidences(m: MarkovLoop, t: int) -> np.ndarray:
+    """[R][gamma] conditional confidences of round t (t < 0: an earlier history)."""
+    g = _mrng(m, _T_MC, t + 1000)
+    kind, *par = m.conf.split(":")
+    if kind == "beta":
+        c = g.beta(float(par[0]), float(par[1]), (m.R, m.gamma))
+    else:
+        mu, sd = float(par[0]), float(par[1])
+        c = 1.0 / (1.0 + np.exp(-(mu + sd * g.standard_normal((m.R, m.gamma)))))
+    return c.astype(np.float32)
+
+
+def markov_anchors(m: MarkovLoop) -> np.ndarray:
+    return _mrng(m, _T_MX0).integers(0, m.V, m.R).astype(np.int32)
+
+
+def markov_sps(m: MarkovLoop) -> np.ndarray:
+    B = np.arange(m.B_max + 1, dtype=np.float64)
+    if m.sps == "tiny":
+        return 100.0 / (1.0 + B / 8.0)
+    return 60.0 * 1024.0 / (1024.0 + B)
