@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 DSPARK_F32, DSPARK_BF16 = 0, 1
-DSPARK_SCHED_OFF, DSPARK_SCHED_EARLY_STOP, DSPARK_SCHED_FULL_SEARCH, DSPARK_SCHED_ASYNC_TOPK = range(4)
+(DSPARK_SCHED_OFF, DSPARK_SCHED_EARLY_STOP, DSPARK_SCHED_FULL_SEARCH, DSPARK_SCHED_ASYNC_TOPK,
+ DSPARK_SCHED_THRESHOLD) = range(5)
 STATUS_NAMES = ["DSPARK_OK", "DSPARK_ERR_NULL", "DSPARK_ERR_SHAPE", "DSPARK_ERR_DTYPE",
                 "DSPARK_ERR_VALUE", "DSPARK_ERR_WORKSPACE", "DSPARK_ERR_SPS_TABLE",
                 "DSPARK_ERR_MODE", "DSPARK_ERR_ALIGN", "DSPARK_ERR_HIP"]
@@ -41,11 +42,11 @@ def library():
         L.dspark_status_string.restype = C.c_char_p
         L.dspark_draft_workspace.argtypes = [_i, _i, _i, _i, _i]
         L.dspark_draft_workspace.restype = _sz
-        L.dspark_draft.argtypes = ([_i] * 5 + [_f] + [_vp] * 5 + [_i, _vp, _f, _u64, _u64]
+        L.dspark_draft.argtypes = ([_i] * 5 + [_f] + [_vp] * 5 + [_i, _vp, _f, _vp, _u64, _u64]
                                    + [_vp] * 5 + [_sz, _vp])
         L.dspark_schedule_workspace.argtypes = [_i, _i]
         L.dspark_schedule_workspace.restype = _sz
-        L.dspark_schedule.argtypes = [_i, _i, _i, _vp, _vp, _vp, _i] + [_vp] * 6 + [_sz, _vp]
+        L.dspark_schedule.argtypes = [_i, _i, _i, _f, _vp, _vp, _vp, _i] + [_vp] * 6 + [_sz, _vp]
         L.dspark_verify_workspace.argtypes = [_i, _i, _i, _i]
         L.dspark_verify_workspace.restype = _sz
         L.dspark_verify.argtypes = ([_i] * 5 + [_f, _vp, _vp, _i] + [_vp] * 8 + [_u64, _u64]
@@ -91,20 +92,21 @@ def dspark_draft_workspace(R, gamma, V, r, dt):
     return library().dspark_draft_workspace(R, gamma, V, r, dt)
 
 
-def dspark_draft(R, gamma, V, r, dt, temp, U, W1, W2, x0, h, d, w_conf, b_conf, seed, round_,
-                 x, q_stats, q_x, c, ws, ws_bytes, stream):
+def dspark_draft(R, gamma, V, r, dt, temp, U, W1, W2, x0, h, d, w_conf, b_conf, conf_temp, seed,
+                 round_, x, q_stats, q_x, c, ws, ws_bytes, stream):
     return library().dspark_draft(R, gamma, V, r, dt, temp, _p(U), _p(W1), _p(W2), _p(x0), _p(h),
-                                  d, _p(w_conf), b_conf, seed, round_, _p(x), _p(q_stats), _p(q_x),
-                                  _p(c), _p(ws), ws_bytes, _s(stream))
+                                  d, _p(w_conf), b_conf, _p(conf_temp), seed, round_, _p(x),
+                                  _p(q_stats), _p(q_x), _p(c), _p(ws), ws_bytes, _s(stream))
 
 
 def dspark_schedule_workspace(R, gamma):
     return library().dspark_schedule_workspace(R, gamma)
 
 
-def dspark_schedule(R, gamma, mode, c, c_prev2, SPS, B_max, ell, row_offset, a, n_admitted, theta,
-                    ws, ws_bytes, stream):
-    return library().dspark_schedule(R, gamma, mode, _p(c), _p(c_prev2), _p(SPS), B_max, _p(ell),
+def dspark_schedule(R, gamma, mode, threshold, c, c_prev2, SPS, B_max, ell, row_offset, a,
+                    n_admitted, theta, ws, ws_bytes, stream):
+    return library().dspark_schedule(R, gamma, mode, threshold, _p(c), _p(c_prev2), _p(SPS), B_max,
+                                     _p(ell),
                                      _p(row_offset), _p(a), _p(n_admitted), _p(theta), _p(ws),
                                      ws_bytes, _s(stream))
 

@@ -46,8 +46,9 @@ class Workspace:
 
 
 def draft(U, W1, W2, x0, *, temp=1.0, seed=0, round=0, h=None, w_conf=None, b_conf=0.0,
-          ws=None, stream=None, out=None):
-    """U [R][gamma][V], W1 [V][r], W2 column-major ([V][r] storage), x0 [R] int32."""
+          conf_temp=None, ws=None, stream=None, out=None):
+    """U [R][gamma][V], W1 [V][r], W2 column-major ([V][r] storage), x0 [R] int32;
+    conf_temp [gamma] fp32 per-position temperatures of the confidence head."""
     R, gamma, V = U.shape
     r = W1.shape[1]
     dt = _dt(U)
@@ -62,15 +63,17 @@ def draft(U, W1, W2, x0, *, temp=1.0, seed=0, round=0, h=None, w_conf=None, b_co
     buf = ws.get(nbytes)
     d = 0 if h is None else h.shape[-1]
     st = A.dspark_draft(R, gamma, V, r, dt, float(temp), U, W1, W2, x0, h, d, w_conf, float(b_conf),
-                        int(seed), int(round), out["x"], out["q_stats"], out["q_x"], out["c"], buf,
+                        conf_temp, int(seed), int(round), out["x"], out["q_stats"], out["q_x"],
+                        out["c"], buf,
                         buf.numel(), _stream(stream))
     _check(st, "dspark_draft")
     return out
 
 
 def schedule(c, SPS, mode, *, c_prev2=None, R=None, gamma=None, ws=None, stream=None, out=None,
-             want_a=True):
-    """c [R][gamma] fp32 (None in OFF mode with R, gamma given); SPS fp64 table."""
+             want_a=True, threshold=0.0):
+    """c [R][gamma] fp32 (None in OFF mode with R, gamma given); SPS fp64 table;
+    threshold: the THRESHOLD mode's cutoff."""
     if c is not None:
         R, gamma = c.shape
         dev = c.device
@@ -86,7 +89,7 @@ def schedule(c, SPS, mode, *, c_prev2=None, R=None, gamma=None, ws=None, stream=
     ws = ws or Workspace(dev)
     buf = ws.get(A.dspark_schedule_workspace(R, gamma))
     B_max = 0 if SPS is None else SPS.numel() - 1
-    st = A.dspark_schedule(R, gamma, int(mode), c, c_prev2, SPS, B_max, out["ell"],
+    st = A.dspark_schedule(R, gamma, int(mode), float(threshold), c, c_prev2, SPS, B_max, out["ell"],
                            out["row_offset"], out["a"], out["n_admitted"], out["theta"], buf,
                            buf.numel(), _stream(stream))
     _check(st, "dspark_schedule")

@@ -61,7 +61,8 @@ size_t dspark_draft_workspace(int R, int gamma, int V, int r, dspark_dtype dt) {
 dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
                            const void *U, const void *W1, const void *W2, const int32_t *x0,
                            const void *h, int d, const float *w_conf, float b_conf,
-                           uint64_t seed, uint64_t round, int32_t *x, float *q_stats, float *q_x,
+                           const float *conf_temp, uint64_t seed, uint64_t round, int32_t *x,
+                           float *q_stats, float *q_x,
                            float *c, void *ws, size_t ws_bytes, hipStream_t stream) {
   dspark_status s = check_common(R, gamma, V, r, dt, temp);
   if (s != DSPARK_OK) return s;
@@ -83,7 +84,8 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
-  L.b_conf = b_conf; L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
+  L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
+  L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
   L.c = c;
   return from_hip(launch_draft(L, stream));
 }
@@ -93,22 +95,25 @@ size_t dspark_schedule_workspace(int R, int gamma) {
   return schedule_ws_bytes(R, gamma);
 }
 
-dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode, const float *c,
-                              const float *c_prev2, const double *SPS, int B_max, int32_t *ell,
+dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode, float threshold,
+                              const float *c, const float *c_prev2, const double *SPS, int B_max,
+                              int32_t *ell,
                               int32_t *row_offset, float *a, int32_t *n_admitted, double *theta,
                               void *ws, size_t ws_bytes, hipStream_t stream) {
   if (R < 1 || gamma < 1 || gamma > 64 || (int64_t)R * gamma > 8192) return DSPARK_ERR_SHAPE;
-  if ((int)mode < 0 || (int)mode > 3) return DSPARK_ERR_MODE;
+  if ((int)mode < 0 || (int)mode > 4) return DSPARK_ERR_MODE;
   if (!ell || !row_offset || !n_admitted || !theta || !ws) return DSPARK_ERR_NULL;
   if (mode != DSPARK_SCHED_OFF && !c) return DSPARK_ERR_MODE;
   if (mode == DSPARK_SCHED_ASYNC_TOPK && !c_prev2) return DSPARK_ERR_MODE;
-  const bool need_sps = mode != DSPARK_SCHED_OFF || (c != nullptr && SPS != nullptr);
-  if (mode != DSPARK_SCHED_OFF && !SPS) return DSPARK_ERR_SPS_TABLE;
+  if (mode == DSPARK_SCHED_THRESHOLD && !isfinite(threshold)) return DSPARK_ERR_VALUE;
+  const bool sps_optional = mode == DSPARK_SCHED_OFF || mode == DSPARK_SCHED_THRESHOLD;
+  const bool need_sps = !sps_optional || (c != nullptr && SPS != nullptr);
+  if (!sps_optional && !SPS) return DSPARK_ERR_SPS_TABLE;
   if (need_sps && (int64_t)B_max < (int64_t)R * (1 + gamma)) return DSPARK_ERR_SPS_TABLE;
   if (!aligned16(ws)) return DSPARK_ERR_ALIGN;
   if (ws_bytes < schedule_ws_bytes(R, gamma)) return DSPARK_ERR_WORKSPACE;
   ScheduleLaunch L{};
-  L.R = R; L.gamma = gamma; L.mode = (int)mode; L.c = c;
+  L.R = R; L.gamma = gamma; L.mode = (int)mode; L.threshold = threshold; L.c = c;
   L.c_prev2 = mode == DSPARK_SCHED_ASYNC_TOPK ? c_prev2 : nullptr;
   L.SPS = need_sps ? SPS : nullptr; L.ell = ell; L.row_offset = row_offset;
   L.a = c ? a : nullptr; L.n_admitted = n_admitted; L.theta = theta; L.err = (int32_t *)ws;

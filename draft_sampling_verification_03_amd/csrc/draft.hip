@@ -30,10 +30,12 @@ struct SampleParams {
   float *q_stats, *q_x;
   const float2 *tile_stats;  // [R][n_tiles]
   uint64_t seed, round;
-  // confidence head (Bangkok 4.2.1): c_k = sigmoid(sh[rho][k] + w_e . W1[x_{k-1}] + b)
+  // confidence head (Bangkok 4.2.1): c_k = sigmoid((sh[rho][k] + w_e . W1[x_{k-1}] + b) / T_k)
+  // with sequential temperature scaling's T_k (Blog "Sequential temperature scaling")
   const float *sh;           // [R][gamma] = w_h . h_k, or NULL
   const float *w_e;          // [r] (the last r weights of w_conf)
   float b_conf;
+  const float *conf_temp;    // [gamma] T_k, or NULL (1)
   float *c;
   int32_t *err;
 };
@@ -181,14 +183,19 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     }
   }
 
-  // 6. confidence head on [h_k ; W1[x_{k-1}]] (wave 1)
+  // 6. confidence head on [h_k ; W1[x_{k-1}]], at the position's temperature (wave 1)
   if (p.sh != nullptr && wave == 1) {
+    float tk = p.conf_temp != nullptr ? p.conf_temp[k - 1] : 1.0f;  // in flight with the dot
     float acc = 0.0f;
     for (int i = lane; i < r; i += kWave) acc = fmaf(p.w_e[i], Elem<T>::at(arow, i), acc);
     acc = wave_sum(acc);
     if (lane == 0) {
+      if (!(tk > 0.0f) || !isfinite(tk)) {
+        flag_error(p.err, kErrConfidence);
+        tk = 1.0f;
+      }
       const float s = p.sh[slot] + acc + p.b_conf;
-      p.c[slot] = 1.0f / (1.0f + expf(-s));
+      p.c[slot] = 1.0f / (1.0f + expf(-s / tk));
     }
   }
 }
@@ -232,6 +239,7 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
                   head_hidden_dot_kernel<T><<<(n_slots + 3) / 4, kBlock, 0, stream>>>(
                       n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh));
     sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
+    sp.conf_temp = L.conf_temp;
   }
   // the first step reads its transition rows W1[x0] in place; the sampler of
   // step k writes W1[x_k] contiguously for step k + 1

@@ -22,6 +22,7 @@ struct DraftLaunch {
   const void *h;
   const float *w_conf;
   float b_conf;
+  const float *conf_temp;  // [gamma] or NULL
   uint64_t seed, round;
   int32_t *x;
   float *q_stats, *q_x, *c;
@@ -34,6 +35,7 @@ struct DraftLaunch {
 
 struct ScheduleLaunch {
   int R, gamma, mode;
+  float threshold;  // THRESHOLD mode
   const float *c, *c_prev2;
   const double *SPS;
   int32_t *ell, *row_offset;

@@ -390,13 +390,65 @@ __device__ __forceinline__ void prefetch_sps(const ScheduleLaunch L, double (&sp
   for (int e = 0; e <= E; ++e) sps[e] = base + e <= N ? L.SPS[L.R + base + e] : 0.0;
 }
 
+// THRESHOLD mode: survival in place (as for the sort) and, per request, the
+// number of leading positions with c >= threshold and the fixed-point weight
+// of those positions; returns the thread's weight sum, lengths in len[].
+constexpr int kMaxReqPerThread = kMaxCandidates / kSchedThreads;
+__device__ __forceinline__ int64_t threshold_survival(int R, int gamma, int gs, float thr,
+                                                      int32_t *err, SchedShared &sh,
+                                                      int (&len)[kMaxReqPerThread]) {
+  bool bad = false;
+  int64_t wsum = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxReqPerThread; ++q) {
+    len[q] = 0;
+    const int rho = (int)threadIdx.x + q * kSchedThreads;
+    if (rho >= R) continue;
+    float run = 1.0f;
+    float *row = sh.conf + rho * gs;
+    bool kept = true;
+    for (int j = 1; j <= gamma; ++j) {
+      float c = row[j - 1];
+      if (!(c >= 0.0f && c <= 1.0f)) {
+        bad = true;
+        c = 0.0f;
+      }
+      run = run * c;
+      row[j - 1] = run;
+      kept = kept && c >= thr;
+      if (kept) {
+        len[q] = j;
+        wsum += fixed_weight(run);
+      }
+    }
+  }
+  if (bad) flag_error(err, kErrConfidence);
+  return wsum;
+}
+
 template <int E>
 __device__ __forceinline__ void schedule_body(const ScheduleLaunch L, SchedShared &sh, double *s_theta) {
   const int R = L.R, gamma = L.gamma, N = R * gamma;
   int n_star = N;
   double theta = NAN;
   uint64_t k[E];
-  if (L.mode == 0) {
+  int len[kMaxReqPerThread];  // THRESHOLD mode: kept lengths of requests tid + q 1024
+  if (L.mode == 4) {
+    const int gs = gamma | 1;
+    stage_confidences(L.c, N, gamma, gs, sh);
+    const int64_t wsum = threshold_survival(R, gamma, gs, L.threshold, L.err, sh, len);
+    __syncthreads();
+    if (L.a) write_survival(L.a, N, gamma, gs, sh);
+    int64_t nl = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxReqPerThread; ++q) nl += len[q];
+    int64_t A, n_total;
+    sched_exclusive_scan_i64(wsum, sh, &A);
+    sched_exclusive_scan_i64(nl, sh, &n_total);
+    n_star = (int)n_total;
+    if (threadIdx.x == 0 && L.SPS != nullptr)
+      theta = ((double)R + (double)A * (1.0 / 4294967296.0)) * L.SPS[R + n_star];
+  } else if (L.mode == 0) {
     if (L.c != nullptr) {
       const int gs = gamma | 1;
       stage_confidences(L.c, N, gamma, gs, sh);
@@ -422,9 +474,17 @@ __device__ __forceinline__ void schedule_body(const ScheduleLaunch L, SchedShare
   }
   __syncthreads();  // done with sh.conf: it becomes sh.ell
   if (!isnan(theta)) *s_theta = theta;  // exactly one thread holds it
-  for (int rho = threadIdx.x; rho < R; rho += kSchedThreads) sh.ell[rho] = L.mode == 0 ? gamma : 0;
+  if (L.mode == 4) {
+#pragma unroll
+    for (int q = 0; q < kMaxReqPerThread; ++q) {
+      const int rho = (int)threadIdx.x + q * kSchedThreads;
+      if (rho < R) sh.ell[rho] = len[q];
+    }
+  } else {
+    for (int rho = threadIdx.x; rho < R; rho += kSchedThreads) sh.ell[rho] = L.mode == 0 ? gamma : 0;
+  }
   __syncthreads();
-  if (L.mode != 0) {
+  if (L.mode != 0 && L.mode != 4) {
     // admitted candidates are a prefix of each request (keys increase with
     // depth along a request): its admitted count is its deepest admitted j
     const int base = (int)threadIdx.x * E;

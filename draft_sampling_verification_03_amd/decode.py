@@ -17,7 +17,7 @@ from . import _abi as A
 from . import api
 
 
-def decode(rounds, x0, W1, W2, U_of_round, target_rows, *, SPS=None, mode=0,
+def decode(rounds, x0, W1, W2, U_of_round, target_rows, *, SPS=None, mode=0, threshold=0.0,
            conf_of_round=None, temp=1.0, seed=0, first_round=0, stream=None):
     """Run `rounds` rounds for R requests.
 
@@ -27,7 +27,8 @@ def decode(rounds, x0, W1, W2, U_of_round, target_rows, *, SPS=None, mode=0,
     target_rows   prev (host int64 array of previous tokens) -> [len(prev)][V]
                   device tensor: the target logits after each given token
     conf_of_round t -> c [R][gamma] float32 device tensor (None: scheduler off)
-    mode          scheduler mode (ASYNC_TOPK reads the confidences of round t - 2)
+    mode          scheduler mode (ASYNC_TOPK reads the confidences of round t - 2;
+                  THRESHOLD keeps each request's leading drafts with c >= threshold)
 
     Returns a dict of per-round host arrays (ell, n_acc, y, theta, n_admitted)
     and the emitted token stream of every request (anchors excluded)."""
@@ -47,7 +48,7 @@ def decode(rounds, x0, W1, W2, U_of_round, target_rows, *, SPS=None, mode=0,
         # the first rounds the callable supplies an earlier history)
         cp = conf_of_round(t - 2) if (c is not None and mode == A.DSPARK_SCHED_ASYNC_TOPK) else None
         s = api.schedule(c, SPS, mode if c is not None else 0, c_prev2=cp, R=R, gamma=gamma,
-                         ws=ws_s, stream=stream)
+                         ws=ws_s, stream=stream, threshold=threshold)
         ell = s["ell"].cpu().numpy()
         x = d["x"].cpu().numpy()
         a = anchors.cpu().numpy()

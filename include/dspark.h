@@ -74,7 +74,8 @@ typedef enum {
   DSPARK_SCHED_OFF = 0,
   DSPARK_SCHED_EARLY_STOP = 1,
   DSPARK_SCHED_FULL_SEARCH = 2,
-  DSPARK_SCHED_ASYNC_TOPK = 3
+  DSPARK_SCHED_ASYNC_TOPK = 3,
+  DSPARK_SCHED_THRESHOLD = 4
 } dspark_sched_mode;
 
 typedef enum {
@@ -106,8 +107,10 @@ typedef enum {
  *            u = uniform(position k, rho, stream 0, round)
  * The bias row W1[x_{k-1}] W2 is a [R, r] x [r, V] product on bf16 matrix
  * cores with fp32 accumulation.  Optional confidence head (Bangkok 4.2.1; KB
- * section 4): c_k = sigmoid(sum_j w_conf[j] h[rho][k-1][j]
- *                          + sum_i w_conf[d+i] W1[x_{k-1}][i] + b_conf).
+ * section 4): c_k = sigmoid(z_k / T_k),
+ *   z_k = sum_j w_conf[j] h[rho][k-1][j] + sum_i w_conf[d+i] W1[x_{k-1}][i] + b_conf,
+ * with T_k the position's temperature of sequential temperature scaling (Blog
+ * "Sequential temperature scaling"; Bangkok 4.2.1), 1 when conf_temp is NULL.
  *
  * Inputs
  *   U      [R][gamma][V]  draft base logits U_k of the parallel backbone (dt)
@@ -118,6 +121,9 @@ typedef enum {
  *   h      [R][gamma][d]  backbone hidden states for the confidence head (dt), or NULL
  *   d      width of h (d % 8 == 0, 8 <= d <= 65536); ignored when h == NULL
  *   w_conf [d + r] fp32 head weights; b_conf fp32 bias; ignored when h == NULL
+ *   conf_temp [gamma] fp32 per-position temperatures T_k > 0, or NULL (all 1);
+ *          ignored when h == NULL.  A T_k that is not a finite positive number
+ *          sets DSPARK_DEVERR_CONFIDENCE and is taken as 1.
  *   seed, round           Philox key and round counter
  * Outputs
  *   x       [R][gamma]    drafted tokens x_1..x_gamma, int32
@@ -129,7 +135,7 @@ size_t dspark_draft_workspace(int R, int gamma, int V, int r, dspark_dtype dt);
 dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
                            const void *U, const void *W1, const void *W2, const int32_t *x0,
                            const void *h, int d, const float *w_conf, float b_conf,
-                           uint64_t seed, uint64_t round,
+                           const float *conf_temp, uint64_t seed, uint64_t round,
                            int32_t *x, float *q_stats, float *q_x, float *c,
                            void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -142,18 +148,24 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
  *   tau_n = R + A_n * 2^-32,  B_n = R + n,  theta_n = tau_n * SPS[B_n]   (fp64)
  *   n* by mode; ell[rho] = admitted candidates of rho (a prefix by the order);
  *   row_offset = exclusive scan of (1 + ell).
+ * THRESHOLD mode (the static confidence cutoff the pages test before the
+ * scheduler, Bangkok 5.3; KB section 7): no sort; request rho keeps its
+ * leading positions with c[rho][j] >= threshold, up to the first one below it;
+ * n* = sum ell and theta = tau * SPS[R + n*] over the kept positions.
  * Inputs
  *   c       [R][gamma] conditional confidences in [0, 1], fp32 (may be NULL in OFF mode)
  *   c_prev2 [R][gamma] confidences of round t-2, ASYNC_TOPK only (else ignored)
  *   SPS     [B_max + 1] target steps per second indexed by verify batch size B,
- *           fp64; B_max >= R * (1 + gamma).  May be NULL in OFF mode.
+ *           fp64; B_max >= R * (1 + gamma).  May be NULL in OFF and THRESHOLD
+ *           modes (theta is then NaN).
+ *   threshold  THRESHOLD mode's cutoff (finite; ignored in other modes)
  *   R * gamma <= 8192, gamma <= 64.
  * Outputs
  *   ell [R], row_offset [R + 1] int32; a [R][gamma] fp32 (may be NULL);
  *   n_admitted [1] int32; theta [1] fp64 (theta_{n*}; NaN when c is NULL).
  * Workspace: dspark_schedule_workspace(R, gamma) bytes. */
 size_t dspark_schedule_workspace(int R, int gamma);
-dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode,
+dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode, float threshold,
                               const float *c, const float *c_prev2,
                               const double *SPS, int B_max,
                               int32_t *ell, int32_t *row_offset, float *a,

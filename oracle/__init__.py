@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 STREAM_DRAFT, STREAM_ACCEPT, STREAM_FINAL = 0, 1, 2
-SCHED_OFF, SCHED_EARLY_STOP, SCHED_FULL_SEARCH, SCHED_ASYNC_TOPK = 0, 1, 2, 3
+SCHED_OFF, SCHED_EARLY_STOP, SCHED_FULL_SEARCH, SCHED_ASYNC_TOPK, SCHED_THRESHOLD = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -49,16 +49,17 @@ def _declare(L):
     L.orc_inverse_cdf.argtypes = [C.c_int, _dp, C.c_double, _dp]
     L.orc_draft_position.argtypes = [C.c_int, C.c_int, C.c_int, C.c_double, _vp, _vp, _vp, C.c_int,
                                      C.c_double, _dp, _dp, _dp, _dp, _dp]
-    L.orc_conf_head.argtypes = [C.c_int, C.c_int, C.c_int, _vp, _f32p, C.c_float, _vp, C.c_int]
+    L.orc_conf_head.argtypes = [C.c_int, C.c_int, C.c_int, _vp, _f32p, C.c_float, C.c_double, _vp,
+                                C.c_int]
     L.orc_conf_head.restype = C.c_double
     L.orc_draft_request.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_double, _vp, _vp, _vp,
-                                    C.c_int, _i32p, _vp, C.c_int, _f32p, C.c_float, C.c_uint64,
-                                    C.c_uint64, C.c_int, _i32p, _dp, _dp, _dp, _dp]
+                                    C.c_int, _i32p, _vp, C.c_int, _f32p, C.c_float, _f32p,
+                                    C.c_uint64, C.c_uint64, C.c_int, _i32p, _dp, _dp, _dp, _dp]
     L.orc_overlap.argtypes = [C.c_int, C.c_int, C.c_double, _vp, _vp, _dp]
     L.orc_overlap.restype = C.c_double
     L.orc_select_n.argtypes = [_dp, C.c_int, C.c_int]
-    L.orc_schedule.argtypes = [C.c_int, C.c_int, C.c_int, _f32p, _f32p, _dp, C.c_int, _i32p, _i32p,
-                               _f32p, _i32p, _dp, _i32p, _dp]
+    L.orc_schedule.argtypes = [C.c_int, C.c_int, C.c_int, C.c_double, _f32p, _f32p, _dp, C.c_int,
+                               _i32p, _i32p, _f32p, _i32p, _dp, _i32p, _dp]
     L.orc_schedule_bruteforce.argtypes = [C.c_int, C.c_int, _f32p, _dp, C.c_int, _i32p]
     L.orc_schedule_bruteforce.restype = C.c_double
     L.orc_verify_request.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_double, C.c_int, _vp,
@@ -146,16 +147,17 @@ def draft_position(U_row, W1, W2, prev, u, temp=1.0, want_law=False):
     return out
 
 
-def conf_head(h_row, w_conf, b_conf, W1, prev):
+def conf_head(h_row, w_conf, b_conf, W1, prev, T=1.0):
+    """c = sigmoid(z / T) for the head's logit z; T is the position's temperature."""
     V, r = W1.shape
     h_row = np.ascontiguousarray(h_row)
     w = np.ascontiguousarray(w_conf, dtype=np.float32)
     return lib().orc_conf_head(h_row.size, r, dtype_code(h_row), _ptr(h_row), _ptr(w, C.c_float),
-                               float(b_conf), _ptr(W1), int(prev))
+                               float(b_conf), float(T), _ptr(W1), int(prev))
 
 
 def draft_request(U_req, W1, W2, x0, seed, rnd, rho, temp=1.0, x_cond=None, h_req=None,
-                  w_conf=None, b_conf=0.0):
+                  w_conf=None, b_conf=0.0, conf_temp=None):
     """Whole block of one request; U_req is [gamma][V]."""
     gamma, V = U_req.shape
     r = W1.shape[1]
@@ -167,9 +169,11 @@ def draft_request(U_req, W1, W2, x0, seed, rnd, rho, temp=1.0, x_cond=None, h_re
     d = 0 if h_req is None else h_req.shape[1]
     h = None if h_req is None else np.ascontiguousarray(h_req)
     w = None if w_conf is None else np.ascontiguousarray(w_conf, dtype=np.float32)
+    ct = None if conf_temp is None else np.ascontiguousarray(conf_temp, dtype=np.float32)
     rc = lib().orc_draft_request(gamma, V, r, dtype_code(U_req), temp, _ptr(U_req), _ptr(W1),
                                  _ptr(W2), int(x0), _ptr(xc, C.c_int32), _ptr(h), d,
-                                 _ptr(w, C.c_float), float(b_conf), seed, rnd, rho,
+                                 _ptr(w, C.c_float), float(b_conf), _ptr(ct, C.c_float), seed, rnd,
+                                 rho,
                                  _ptr(x, C.c_int32), _ptr(qx, C.c_double), _ptr(m, C.c_double),
                                  _ptr(S, C.c_double), _ptr(c, C.c_double))
     assert rc == 0, "oracle draft rejected its arguments"
@@ -182,8 +186,9 @@ def select_n(theta, mode):
     return lib().orc_select_n(_ptr(theta, C.c_double), theta.size - 1, mode)
 
 
-def schedule(c, SPS, mode, c_prev2=None, R=None, gamma=None):
-    """c is [R][gamma] float32 (or None for OFF); SPS is the float64 table indexed by B."""
+def schedule(c, SPS, mode, c_prev2=None, R=None, gamma=None, threshold=0.0):
+    """c is [R][gamma] float32 (or None for OFF); SPS is the float64 table indexed by B
+    (optional in OFF and THRESHOLD modes); threshold is the THRESHOLD mode's cutoff."""
     if c is not None:
         c = np.ascontiguousarray(c, dtype=np.float32)
         R, gamma = c.shape
@@ -194,7 +199,7 @@ def schedule(c, SPS, mode, c_prev2=None, R=None, gamma=None):
     a = np.zeros((R, gamma), dtype=np.float32)
     n_adm, n_plain = C.c_int32(), C.c_int32()
     theta, theta_plain = C.c_double(), C.c_double()
-    rc = lib().orc_schedule(R, gamma, mode, _ptr(c, C.c_float), _ptr(cp, C.c_float),
+    rc = lib().orc_schedule(R, gamma, mode, float(threshold), _ptr(c, C.c_float), _ptr(cp, C.c_float),
                             _ptr(sps, C.c_double), 0 if sps is None else sps.size - 1,
                             _ptr(ell, C.c_int32), _ptr(row_offset, C.c_int32), _ptr(a, C.c_float),
                             C.byref(n_adm), C.byref(theta), C.byref(n_plain), C.byref(theta_plain))

@@ -40,7 +40,7 @@ extern "C" {
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_STREAM_DRAFT = 0, ORC_STREAM_ACCEPT = 1, ORC_STREAM_FINAL = 2 };
 enum { ORC_SCHED_OFF = 0, ORC_SCHED_EARLY_STOP = 1, ORC_SCHED_FULL_SEARCH = 2,
-       ORC_SCHED_ASYNC_TOPK = 3 };
+       ORC_SCHED_ASYNC_TOPK = 3, ORC_SCHED_THRESHOLD = 4 };
 
 /* Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
  * easy as 1, 2, 3", SC'11): 10 rounds of the 4x64 Philox S-box with the
@@ -75,10 +75,13 @@ int orc_draft_position(int V, int r, int dt, double temp,
                        int prev, double u,
                        double *q, double *cdf, double *m, double *S, double *qx);
 
-/* Confidence head (Bangkok 4.2.1; KB section 4): c = sigmoid(sum_j w[j] h[j] +
- * sum_i w[d + i] W1[prev, i] + b), linear over the concatenation [h_k ; W1[x_{k-1}]]. */
+/* Confidence head (Bangkok 4.2.1; KB section 4): z = sum_j w[j] h[j] +
+ * sum_i w[d + i] W1[prev, i] + b, linear over the concatenation
+ * [h_k ; W1[x_{k-1}]], then c = sigmoid(z / T) with the position's
+ * temperature T > 0 (sequential temperature scaling, Blog "Sequential
+ * temperature scaling"; Bangkok 4.2.1; T = 1 is the uncalibrated head). */
 double orc_conf_head(int d, int r, int dt, const void *h_row, const float *w,
-                     float b, const void *W1, int prev);
+                     float b, double T, const void *W1, int prev);
 
 /* Whole draft of one request with the oracle's own samples.  x0 is the anchor.
  * Outputs x[gamma], qx[gamma], m[gamma], S[gamma] and, if h != NULL,
@@ -89,7 +92,8 @@ int orc_draft_request(int gamma, int V, int r, int dt, double temp,
                       const void *U_req /*[gamma][V]*/, const void *W1, const void *W2,
                       int x0, const int32_t *x_cond,
                       const void *h_req /*[gamma][d] or NULL*/, int d, const float *w_conf,
-                      float b_conf, uint64_t seed, uint64_t round, int rho,
+                      float b_conf, const float *conf_temp /*[gamma] or NULL = 1*/,
+                      uint64_t seed, uint64_t round, int rho,
                       int32_t *x, double *qx, double *m, double *S, double *c);
 
 /* TV overlap label (Blog "Total variation label"): sum_v min(p(v), q(v)) for
@@ -114,8 +118,13 @@ int orc_select_n(const double *theta, int N, int mode);
  * n_admitted, theta (theta_{n*}; NaN in OFF mode without c).
  * theta_plain (optional) receives theta_{n*'} of the same rule computed with a
  * plain fp64 running sum of a instead of the fixed-point sum, and n_plain its n*'.
+ * THRESHOLD (the static confidence cutoff the pages test before the scheduler,
+ * Bangkok 5.3; KB section 7): request rho keeps its leading positions whose
+ * confidence c[rho][j] >= threshold, up to the first one below it (the kept
+ * tokens stay a prefix); n* = sum ell; theta = tau * SPS[R + n*] with tau over
+ * the kept positions, or NaN without SPS (SPS is optional in this mode).
  * Returns 0, or -1 on bad arguments (c outside [0, 1], SPS too short). */
-int orc_schedule(int R, int gamma, int mode, const float *c, const float *c_prev2,
+int orc_schedule(int R, int gamma, int mode, double threshold, const float *c, const float *c_prev2,
                  const double *SPS, int B_max, int32_t *ell, int32_t *row_offset,
                  float *a, int32_t *n_admitted, double *theta,
                  int32_t *n_plain, double *theta_plain);

@@ -48,19 +48,21 @@ extern "C" int orc_draft_position(int V, int r, int dt, double temp, const void 
 }
 
 extern "C" double orc_conf_head(int d, int r, int dt, const void *h_row, const float *w, float b,
-                                const void *W1, int prev) {
-  // linear layer on the concatenation [h_k ; W1[x_{k-1}]], then a sigmoid
+                                double T, const void *W1, int prev) {
+  // linear layer on the concatenation [h_k ; W1[x_{k-1}]], then the
+  // position's temperature, then a sigmoid
   double s = (double)b;
   for (int j = 0; j < d; ++j) s += (double)w[j] * orc_internal_widen(dt, h_row, j);
   for (int i = 0; i < r; ++i)
     s += (double)w[d + i] * orc_internal_widen(dt, W1, (int64_t)prev * r + i);
-  return 1.0 / (1.0 + std::exp(-s));
+  return 1.0 / (1.0 + std::exp(-s / T));
 }
 
 extern "C" int orc_draft_request(int gamma, int V, int r, int dt, double temp, const void *U_req,
                                  const void *W1, const void *W2, int x0, const int32_t *x_cond,
                                  const void *h_req, int d, const float *w_conf, float b_conf,
-                                 uint64_t seed, uint64_t round, int rho, int32_t *x, double *qx,
+                                 const float *conf_temp, uint64_t seed, uint64_t round, int rho,
+                                 int32_t *x, double *qx,
                                  double *m, double *S, double *c) {
   if (gamma < 1 || x0 < 0 || x0 >= V) return -1;
   int prev = x0;
@@ -76,7 +78,9 @@ extern "C" int orc_draft_request(int gamma, int V, int r, int dt, double temp, c
     x[k - 1] = xk;
     if (h_req && c) {
       const void *h_row = orc_internal_row(dt, h_req, k - 1, d);
-      c[k - 1] = orc_conf_head(d, r, dt, h_row, w_conf, b_conf, W1, prev);
+      const double T = conf_temp ? (double)conf_temp[k - 1] : 1.0;
+      if (!(T > 0.0) || !std::isfinite(T)) return -1;
+      c[k - 1] = orc_conf_head(d, r, dt, h_row, w_conf, b_conf, T, W1, prev);
     }
   }
   return 0;

@@ -102,12 +102,40 @@ extern "C" int orc_select_n(const double *theta, int N, int mode) {
   return -1;
 }
 
-extern "C" int orc_schedule(int R, int gamma, int mode, const float *c, const float *c_prev2,
+extern "C" int orc_schedule(int R, int gamma, int mode, double threshold, const float *c,
+                            const float *c_prev2,
                             const double *SPS, int B_max, int32_t *ell, int32_t *row_offset,
                             float *a_out, int32_t *n_admitted, double *theta, int32_t *n_plain,
                             double *theta_plain) {
   if (R < 1 || gamma < 1) return -1;
   const int N = R * gamma;
+  if (mode == ORC_SCHED_THRESHOLD) {
+    if (!c || !std::isfinite(threshold)) return -1;
+    if (SPS && B_max < R + N) return -1;
+    std::vector<float> a;
+    if (!survival(R, gamma, c, a)) return -1;
+    if (a_out) std::memcpy(a_out, a.data(), sizeof(float) * (size_t)N);
+    int n = 0;
+    int64_t A = 0;
+    double A_plain = 0.0;
+    row_offset[0] = 0;
+    for (int rho = 0; rho < R; ++rho) {
+      int l = 0;
+      while (l < gamma && (double)c[(size_t)rho * gamma + l] >= threshold) {
+        A += fixed_weight(a[(size_t)rho * gamma + l]);
+        A_plain += (double)a[(size_t)rho * gamma + l];
+        ++l;
+      }
+      ell[rho] = l;
+      n += l;
+      row_offset[rho + 1] = row_offset[rho] + 1 + l;
+    }
+    *n_admitted = n;
+    *theta = SPS ? ((double)R + (double)A * 0x1p-32) * SPS[R + n] : NAN;
+    if (n_plain) *n_plain = n;
+    if (theta_plain) *theta_plain = SPS ? ((double)R + A_plain) * SPS[R + n] : NAN;
+    return 0;
+  }
   if (mode < ORC_SCHED_OFF || mode > ORC_SCHED_ASYNC_TOPK) return -1;
   if (mode != ORC_SCHED_OFF && (!c || !SPS || B_max < R + N)) return -1;
   if (mode == ORC_SCHED_ASYNC_TOPK && !c_prev2) return -1;

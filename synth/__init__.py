@@ -22,7 +22,7 @@ from typing import Optional
 import numpy as np
 
 F32, BF16 = 0, 1
-SCHED_OFF, SCHED_EARLY_STOP, SCHED_FULL_SEARCH, SCHED_ASYNC_TOPK = 0, 1, 2, 3
+SCHED_OFF, SCHED_EARLY_STOP, SCHED_FULL_SEARCH, SCHED_ASYNC_TOPK, SCHED_THRESHOLD = 0, 1, 2, 3, 4
 
 # tensor ids of the seed sequences
 _T_TARGET, _T_UNOISE, _T_W1, _T_W2, _T_X0, _T_C, _T_CPREV, _T_SIGMA, _T_H, _T_WCONF = range(10)

@@ -51,7 +51,8 @@ def test_workspace_sizes_grow_with_shape():
 
 def draft_args(**over):
     a = dict(R=4, gamma=4, V=1024, r=16, dt=A.DSPARK_F32, temp=1.0, U=P, W1=P, W2=P, x0=P, h=None,
-             d=0, w_conf=None, b_conf=0.0, seed=0, round_=0, x=P, q_stats=P, q_x=P, c=None, ws=P,
+             d=0, w_conf=None, b_conf=0.0, conf_temp=None, seed=0, round_=0, x=P, q_stats=P, q_x=P,
+             c=None, ws=P,
              ws_bytes=1 << 30, stream=None)
     a.update(over)
     return a
@@ -77,7 +78,8 @@ def test_draft_bf16_allows_rank_256_but_not_272():
 
 
 def sched_args(**over):
-    a = dict(R=4, gamma=4, mode=A.DSPARK_SCHED_EARLY_STOP, c=P, c_prev2=None, SPS=P, B_max=20,
+    a = dict(R=4, gamma=4, mode=A.DSPARK_SCHED_EARLY_STOP, threshold=0.5, c=P, c_prev2=None, SPS=P,
+             B_max=20,
              ell=P, row_offset=P, a=None, n_admitted=P, theta=P, ws=P, ws_bytes=256, stream=None)
     a.update(over)
     return a
@@ -85,7 +87,11 @@ def sched_args(**over):
 
 @pytest.mark.parametrize("over,expect", [
     (dict(R=0), SHAPE), (dict(gamma=65), SHAPE), (dict(R=1024, gamma=9), SHAPE),
-    (dict(mode=4), MODE), (dict(mode=-1), MODE), (dict(c=None), MODE),
+    (dict(mode=5), MODE), (dict(mode=-1), MODE), (dict(c=None), MODE),
+    (dict(mode=A.DSPARK_SCHED_THRESHOLD, c=None), MODE),
+    (dict(mode=A.DSPARK_SCHED_THRESHOLD, threshold=float("nan")), VALUE),
+    (dict(mode=A.DSPARK_SCHED_THRESHOLD, threshold=float("inf")), VALUE),
+    (dict(mode=A.DSPARK_SCHED_THRESHOLD, B_max=19), SPS),
     (dict(mode=A.DSPARK_SCHED_ASYNC_TOPK), MODE), (dict(SPS=None), SPS), (dict(B_max=19), SPS),
     (dict(ell=None), NULL), (dict(theta=None), NULL), (dict(ws=None), NULL),
     (dict(ws_bytes=8), WS), (dict(ws=P + 4), ALIGN),

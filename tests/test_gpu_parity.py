@@ -210,3 +210,63 @@ def test_verify_output_law_chi2_on_gpu():
     c1 = float(v["c_star"].cpu().numpy()[0, 0])
     acc = float(np.mean(n >= 1))
     assert abs(acc - c1) < 3.29 * np.sqrt(c1 * (1 - c1) / R)
+
+
+# ----------------------------------------------- next rows: STS and thresholds
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", [np.float32, "bf16"])
+def test_confidence_head_position_temperatures(dtype):
+    """c_k = sigmoid(z_k / T_k) against the oracle's head at the GPU's tokens;
+    a temperature that is not a finite positive number is flagged and taken as 1."""
+    rng = np.random.default_rng(21)
+    R, gamma, V, r, d = 16, 5, 512, 16, 64
+    store = (lambda a: synth.to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    U = store(rng.standard_normal((R, gamma, V)).astype(np.float32))
+    W1 = store((0.3 * rng.standard_normal((V, r))).astype(np.float32))
+    W2 = store((0.3 * rng.standard_normal((V, r))).astype(np.float32))
+    h = store(rng.standard_normal((R, gamma, d)).astype(np.float32))
+    w = (0.2 * rng.standard_normal(d + r)).astype(np.float32)
+    x0 = rng.integers(0, V, R).astype(np.int32)
+    T = np.array([0.6, 1.0, 1.7, 3.0, 0.9], dtype=np.float32)
+    ws = ds.Workspace()
+    g = ds.draft(dev(U), dev(W1), dev(W2), dev(x0), h=dev(h), w_conf=dev(w), b_conf=0.25,
+                 conf_temp=dev(T), seed=3, round=1, ws=ws)
+    x, c = g["x"].cpu().numpy(), g["c"].cpu().numpy()
+    assert ws.error_code() == 0
+    tol = 1e-5 if dtype == np.float32 else 2e-3
+    for rho in range(R):
+        for k in range(gamma):
+            prev = int(x0[rho]) if k == 0 else int(x[rho, k - 1])
+            o = oracle.conf_head(h[rho, k], w, np.float32(0.25), W1, prev, T=float(T[k]))
+            assert abs(c[rho, k] - o) <= tol
+    bad = T.copy()
+    bad[2] = 0.0
+    ws2 = ds.Workspace()
+    g2 = ds.draft(dev(U), dev(W1), dev(W2), dev(x0), h=dev(h), w_conf=dev(w), b_conf=0.25,
+                  conf_temp=dev(bad), seed=3, round=1, ws=ws2)
+    assert ws2.error_code() & 2
+    c2 = g2["c"].cpu().numpy()
+    for rho in range(R):
+        o = oracle.conf_head(h[rho, 2], w, np.float32(0.25), W1, int(x[rho, 1]), T=1.0)
+        assert abs(c2[rho, 2] - o) <= tol
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("R,gamma", [(4, 4), (128, 16), (512, 15), (1024, 8)])
+def test_threshold_schedule_matches_oracle(R, gamma):
+    rng = np.random.default_rng(R + gamma)
+    c = (1.0 / (1.0 + np.exp(-(2.0 + 1.5 * rng.standard_normal((R, gamma)))))).astype(np.float32)
+    sps = 60.0 * 1024.0 / (1024.0 + np.arange(R * (gamma + 1) + 1, dtype=np.float64))
+    for thr in np.float32([0.0, 0.6, 0.85, 0.97, 1.5]):
+        for table in (sps, None):
+            o = oracle.schedule(c, table, oracle.SCHED_THRESHOLD, threshold=thr)
+            ws = ds.Workspace()
+            g = ds.schedule(dev(c), dev(table) if table is not None else None,
+                            ds.DSPARK_SCHED_THRESHOLD, threshold=float(thr), ws=ws)
+            assert ws.error_code() == 0
+            assert np.array_equal(g["ell"].cpu().numpy(), o["ell"])
+            assert np.array_equal(g["row_offset"].cpu().numpy(), o["row_offset"])
+            assert int(g["n_admitted"].cpu().numpy()[0]) == o["n_admitted"]
+            assert np.array_equal(g["a"].cpu().numpy(), o["a"])
+            th = float(g["theta"].cpu().numpy()[0])
+            assert (np.isnan(th) and np.isnan(o["theta"])) or th == o["theta"]

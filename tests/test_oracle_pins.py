@@ -424,3 +424,99 @@ def test_schedule_rejects_bad_confidence():
     c = np.array([[0.5, np.nan]], dtype=np.float32)
     with pytest.raises(ValueError):
         oracle.schedule(c, np.ones(8), oracle.SCHED_EARLY_STOP)
+
+
+# ---------------------------------------- sequential temperature scaling (STS)
+def test_sts_head_divides_the_logit():
+    """c = sigmoid(z / T): against the T = 1 head of the same inputs."""
+    rng = np.random.default_rng(6)
+    V, r, d = 16, 8, 24
+    W1 = rng.standard_normal((V, r)).astype(np.float32)
+    h = rng.standard_normal(d).astype(np.float32)
+    w = (0.3 * rng.standard_normal(d + r)).astype(np.float32)
+    c1 = oracle.conf_head(h, w, np.float32(0.4), W1, 5)
+    z = special.logit(c1)
+    for T in (0.5, 2.0, 7.0):
+        assert oracle.conf_head(h, w, np.float32(0.4), W1, 5, T=T) == \
+            pytest.approx(special.expit(z / T), rel=1e-12)
+    # a very hot position says nothing: 1/2
+    assert abs(oracle.conf_head(h, w, np.float32(0.4), W1, 5, T=1e6) - 0.5) < 1e-5
+
+
+def test_sts_printed_example():
+    """Blog, "Sequential temperature scaling": raw confidences 0.98, 0.92, 0.80
+    against empirical survival 0.94, 0.82, 0.65.  Fitting left to right (each
+    position's temperature makes the survival through it match, the earlier
+    ones frozen) and applying the temperatures to the raw logits reproduces the
+    printed survival, and leaves the ranking of the raw scores unchanged."""
+    raw = np.array([0.98, 0.92, 0.80])
+    surv = np.array([0.94, 0.82, 0.65])
+    d, r, V = 8, 8, 4
+    h = np.zeros(d, dtype=np.float32)
+    w = np.zeros(d + r, dtype=np.float32)
+    W1 = np.zeros((V, r), dtype=np.float32)
+    T = []
+    a = 1.0
+    for k in range(3):
+        target = surv[k] / a                        # conditional c that matches survival k
+        T.append(special.logit(raw[k]) / special.logit(target))
+        c = oracle.conf_head(h, w, np.float32(special.logit(raw[k])), W1, 0, T=T[-1])
+        a *= c
+        assert a == pytest.approx(surv[k], abs=1e-6)
+    # the calibration makes the head less confident at every position
+    assert all(t > 1.0 for t in T)
+
+
+def test_draft_request_applies_position_temperatures():
+    rng = np.random.default_rng(7)
+    gamma, V, r, d = 3, 32, 8, 16
+    U = rng.standard_normal((gamma, V)).astype(np.float32)
+    W1 = (0.5 * rng.standard_normal((V, r))).astype(np.float32)
+    W2 = (0.5 * rng.standard_normal((V, r))).astype(np.float32)
+    h = rng.standard_normal((gamma, d)).astype(np.float32)
+    w = (0.2 * rng.standard_normal(d + r)).astype(np.float32)
+    T = np.array([0.7, 1.0, 3.0], dtype=np.float32)
+    out = oracle.draft_request(U, W1, W2, 2, 1, 0, 0, h_req=h, w_conf=w, b_conf=0.3, conf_temp=T)
+    prev = [2, out["x"][0], out["x"][1]]
+    for k in range(gamma):
+        assert out["c"][k] == oracle.conf_head(h[k], w, np.float32(0.3), W1, prev[k], T=float(T[k]))
+    with pytest.raises(AssertionError):
+        oracle.draft_request(U, W1, W2, 2, 1, 0, 0, h_req=h, w_conf=w, b_conf=0.3,
+                             conf_temp=np.array([1.0, 0.0, 1.0], dtype=np.float32))
+
+
+# ------------------------------------------ static confidence-threshold admission
+def test_threshold_schedule_prefixes_and_limits():
+    rng = np.random.default_rng(8)
+    R, gamma = 12, 6
+    c = rng.uniform(0.05, 1.0, (R, gamma)).astype(np.float32)
+    sps = 100.0 / (1.0 + np.arange(R * (gamma + 1) + 1) / 8.0)
+    prev_ell = np.full(R, gamma + 1)
+    for thr in np.float32([0.0, 0.2, 0.5, 0.7, 0.9, 1.01]):
+        s = oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=thr)
+        ell = s["ell"]
+        for rho in range(R):
+            kept = c[rho, : ell[rho]]
+            assert np.all(kept >= thr)                              # kept tokens pass
+            assert ell[rho] == gamma or c[rho, ell[rho]] < thr      # stopped at the first miss
+        assert np.all(ell <= prev_ell)                              # monotone in the cutoff
+        prev_ell = ell
+        assert s["n_admitted"] == ell.sum()
+        assert np.array_equal(s["row_offset"], np.concatenate(([0], np.cumsum(1 + ell))))
+    assert np.all(oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=0.0)["ell"] == gamma)
+    assert np.all(oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=1.01)["ell"] == 0)
+
+
+def test_threshold_theta_agrees_with_other_modes():
+    """Every token kept: theta is the scheduler-off theta of the same c; none
+    kept: R * SPS[R], the full path's theta_0; no SPS table: NaN."""
+    rng = np.random.default_rng(9)
+    R, gamma = 10, 5
+    c = rng.uniform(0.3, 1.0, (R, gamma)).astype(np.float32)
+    sps = 60.0 * 1024.0 / (1024.0 + np.arange(R * (gamma + 1) + 1))
+    all_kept = oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=0.0)
+    off = oracle.schedule(c, sps, oracle.SCHED_OFF)
+    assert all_kept["theta"] == off["theta"] and np.array_equal(all_kept["a"], off["a"])
+    none_kept = oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=1.5)
+    assert none_kept["theta"] == R * sps[R]
+    assert np.isnan(oracle.schedule(c, None, oracle.SCHED_THRESHOLD, threshold=0.5)["theta"])
