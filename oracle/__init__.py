@@ -60,6 +60,8 @@ def _declare(L):
     L.orc_select_n.argtypes = [_dp, C.c_int, C.c_int]
     L.orc_schedule.argtypes = [C.c_int, C.c_int, C.c_int, C.c_double, _f32p, _f32p, _dp, C.c_int,
                                _i32p, _i32p, _f32p, _i32p, _dp, _i32p, _dp]
+    L.orc_train_losses.argtypes = [C.c_int] * 5 + [C.c_double, _vp, _vp, _vp, _i32p, _i32p, _vp,
+                                                   _f32p, C.c_double, C.c_double, C.c_double, _dp, _dp]
     L.orc_schedule_bruteforce.argtypes = [C.c_int, C.c_int, _f32p, _dp, C.c_int, _i32p]
     L.orc_schedule_bruteforce.restype = C.c_double
     L.orc_verify_request.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_double, C.c_int, _vp,
@@ -244,3 +246,26 @@ def verify_request(P_req, U_req, W1, W2, x0, x, ell, seed, rnd, rho, temp=1.0, f
     assert rc == 0, "oracle verify rejected its arguments"
     return dict(n_acc=n_acc.value, y=y, c_star=c_star, ratio=ratio, u_acc=u_acc,
                 final_cdf=fcdf, final_u=fu.value, residual_fallback=fb.value)
+
+
+# ------------------------------------------------------------ training losses
+def train_losses(U, W1, W2, x0, y, P, c, temp=1.0, alpha=(0.1, 0.9, 1.0)):
+    """Forward-only training reductions, teacher-forced.  U [R][gamma][V], y
+    [R][gamma] ground-truth tokens, P [R][gamma + 1][V] (verify layout), c
+    [R][gamma].  Returns per-position (CE, L1, BCE) [3][R][gamma] and the totals
+    (L_ce, L_tv, L_conf, L)."""
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    U, P = np.ascontiguousarray(U), np.ascontiguousarray(P)
+    x0 = np.ascontiguousarray(x0, dtype=np.int32)
+    y = np.ascontiguousarray(y, dtype=np.int32)
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    per = np.zeros((3, R, gamma))
+    tot = np.zeros(4)
+    rc = lib().orc_train_losses(R, gamma, V, r, dtype_code(U), float(temp), _ptr(U), _ptr(W1),
+                                _ptr(W2), _ptr(x0, C.c_int32), _ptr(y, C.c_int32), _ptr(P),
+                                _ptr(c, C.c_float), float(alpha[0]), float(alpha[1]),
+                                float(alpha[2]), _ptr(per, C.c_double), _ptr(tot, C.c_double))
+    assert rc == 0, "oracle train_losses rejected its arguments"
+    return per, tot
+

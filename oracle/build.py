@@ -8,7 +8,8 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["oracle_core.cpp", "oracle_draft.cpp", "oracle_verify.cpp", "oracle_schedule.cpp"]
+SOURCES = ["oracle_core.cpp", "oracle_draft.cpp", "oracle_verify.cpp", "oracle_schedule.cpp",
+           "oracle_train.cpp"]
 LIB = os.path.join(HERE, "liboracle.so")
 
 

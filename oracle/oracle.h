@@ -96,6 +96,21 @@ int orc_draft_request(int gamma, int V, int r, int dt, double temp,
                       uint64_t seed, uint64_t round, int rho,
                       int32_t *x, double *qx, double *m, double *S, double *c);
 
+/* Forward-only training reductions (Blog "Training objective"; KB section 5),
+ * teacher-forced: position k of request rho conditions on x_{k-1} with x_0 =
+ * x0[rho] and x_{k-1} = y[rho][k-2] (y [R][gamma] are the ground-truth tokens).
+ * q_k = the draft law of orc_draft_position, p_k = softmax(P_row / T) with P in
+ * the verify layout (row rho (gamma + 1) + k - 1; the last row of a request is
+ * not read); CE_k = -log q_k(y_k); L1_k = sum_v |p_k(v) - q_k(v)|;
+ * BCE_k = -(c*_k log c_k + (1 - c*_k) log(1 - c_k)) with c*_k = sum_v min(p, q);
+ * w_k = exp(-(k - 1) / gamma); L_x = (1/R) sum_rho sum_k w_k L_x,k / sum_k w_k;
+ * totals = (L_ce, L_tv, L_conf, a_ce L_ce + a_tv L_tv + a_conf L_conf).
+ * per_pos (optional) receives [3][R][gamma] (CE, L1, BCE). */
+int orc_train_losses(int R, int gamma, int V, int r, int dt, double temp, const void *U,
+                     const void *W1, const void *W2, const int32_t *x0, const int32_t *y,
+                     const void *P, const float *c, double a_ce, double a_tv, double a_conf,
+                     double *per_pos, double *totals);
+
 /* TV overlap label (Blog "Total variation label"): sum_v min(p(v), q(v)) for
  * p = softmax(P_row / T), q = softmax(Q_row / T).  Also returns, through tv
  * (optional), 1/2 ||p - q||_1 computed separately. */

@@ -520,3 +520,109 @@ def test_threshold_theta_agrees_with_other_modes():
     none_kept = oracle.schedule(c, sps, oracle.SCHED_THRESHOLD, threshold=1.5)
     assert none_kept["theta"] == R * sps[R]
     assert np.isnan(oracle.schedule(c, None, oracle.SCHED_THRESHOLD, threshold=0.5)["theta"])
+
+
+# ------------------------------------------------------------ training losses
+# Blog, "Training objective", and the knowledge-base summary of the paper's
+# training recipe: L = a_ce L_ce + a_tv L_tv + a_conf L_conf with defaults
+# (0.1, 0.9, 1.0), position weights w_k = exp(-(k - 1) / gamma), hard CE, an
+# L1 target/draft distance, BCE of the confidence against c*, all on the
+# ground-truth prefix.
+def _train_inputs(R, gamma, V, r, seed=0):
+    g = np.random.default_rng(seed)
+    U = g.normal(0, 1.0, (R, gamma, V)).astype(np.float32)
+    W1 = g.normal(0, 0.5, (V, r)).astype(np.float32)
+    W2 = g.normal(0, 0.5, (r, V)).astype(np.float32)
+    P = g.normal(0, 1.5, (R, gamma + 1, V)).astype(np.float32)
+    x0 = g.integers(0, V, R).astype(np.int32)
+    y = g.integers(0, V, (R, gamma)).astype(np.int32)
+    c = g.uniform(0.05, 0.95, (R, gamma)).astype(np.float32)
+    return U, W1, W2, x0, y, P, c
+
+
+def test_train_losses_uniform_case():
+    """All-zero logits on both sides: q = p = uniform, so CE = log V, the L1
+    distance is 0, c* = 1 and the BCE reduces to -log c.  Equal per-position
+    values make every weighted mean equal to that value."""
+    R, gamma, V, r = 2, 5, 8, 3
+    U = np.zeros((R, gamma, V), np.float32)
+    W1 = np.zeros((V, r), np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    P = np.zeros((R, gamma + 1, V), np.float32)
+    x0 = np.array([1, 6], np.int32)
+    y = np.arange(R * gamma, dtype=np.int32).reshape(R, gamma) % V
+    c = np.full((R, gamma), 0.8, np.float32)
+    per, tot = oracle.train_losses(U, W1, W2, x0, y, P, c)
+    np.testing.assert_allclose(per[0], math.log(V), rtol=1e-14)
+    np.testing.assert_allclose(per[1], 0.0, atol=1e-15)
+    np.testing.assert_allclose(per[2], -math.log(np.float32(0.8)), rtol=1e-12)
+    lce, lconf = math.log(V), -math.log(np.float32(0.8))
+    np.testing.assert_allclose(tot, [lce, 0.0, lconf, 0.1 * lce + lconf], rtol=1e-12, atol=1e-15)
+
+
+def test_train_losses_teacher_forced_prefix_and_weights():
+    """A head whose bias only lifts token 2 after token 1: with W2 row (0, 0,
+    40, 0) and W1[1] = 1 (other rows 0) the draft is uniform unless the
+    previous token is 1.  The prefix must come from the labels (x0, then
+    y_{k-1}), and the label scored at position k is y_k.  Request 0 sees
+    CE = (log 4, ~0, log 4); request 1 scores token 3 after token 1, CE ~ 40.
+    The totals are position-weighted means with w_k = exp(-(k - 1) / gamma),
+    averaged over requests."""
+    R, gamma, V, r = 2, 3, 4, 1
+    U = np.zeros((R, gamma, V), np.float32)
+    W1 = np.array([[0.0], [1.0], [0.0], [0.0]], np.float32)
+    W2 = np.array([[0.0, 0.0, 40.0, 0.0]], np.float32)
+    P = np.zeros((R, gamma + 1, V), np.float32)
+    x0 = np.array([0, 1], np.int32)
+    y = np.array([[1, 2, 3], [3, 0, 0]], np.int32)
+    c = np.full((R, gamma), 0.5, np.float32)
+    per, tot = oracle.train_losses(U, W1, W2, x0, y, P, c)
+    peak = 40.0 - math.log(math.exp(40.0) + 3.0)  # log q(2) after token 1
+    low = -math.log(math.exp(40.0) + 3.0)         # log q(v != 2) after token 1
+    np.testing.assert_allclose(per[0][0], [math.log(4), -peak, math.log(4)], rtol=1e-12)
+    np.testing.assert_allclose(per[0][1], [-low, math.log(4), math.log(4)], rtol=1e-12)
+    w = np.exp(-np.arange(gamma) / gamma)
+    req = (per[0] * w).sum(1) / w.sum()
+    np.testing.assert_allclose(tot[0], req.mean(), rtol=1e-14)
+    # weights favour early positions: the first request's loss sits at k = 1, 3
+    np.testing.assert_allclose(req[0], math.log(4) * (w[0] + w[2]) / w.sum(), rtol=1e-12)
+
+
+def test_train_losses_l1_is_twice_one_minus_cstar():
+    """The L1 distance of two distributions equals 2 (1 - sum min(p, q)) (twice
+    the total variation); the BCE is linear in its soft label, so c* can be
+    read back from it and the two losses checked against each other."""
+    U, W1, W2, x0, y, P, c = _train_inputs(3, 6, 50, 4, seed=11)
+    per, _ = oracle.train_losses(U, W1, W2, x0, y, P, c, temp=0.8)
+    cd = c.astype(np.float64)
+    cs = (per[2] + np.log1p(-cd)) / (np.log1p(-cd) - np.log(cd))
+    assert np.all((cs > 0) & (cs < 1))
+    np.testing.assert_allclose(per[1], 2.0 * (1.0 - cs), rtol=1e-9, atol=1e-12)
+
+
+def test_train_losses_temperature_and_library_softmax():
+    """With W1 = W2 = 0 the draft logits are U, so CE is scipy's log-softmax of
+    U / T at the label; a target row equal to U gives p = q at any T (L1 = 0,
+    c* = 1)."""
+    R, gamma, V, r = 2, 4, 33, 2
+    U, _, _, x0, y, _, c = _train_inputs(R, gamma, V, r, seed=5)
+    W1 = np.zeros((V, r), np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    P = np.zeros((R, gamma + 1, V), np.float32)
+    P[:, :gamma] = U
+    T = 0.6
+    per, tot = oracle.train_losses(U, W1, W2, x0, y, P, c, temp=T)
+    ls = special.log_softmax(U.astype(np.float64) / T, axis=-1)
+    ce = -np.take_along_axis(ls, y[..., None].astype(np.int64), -1)[..., 0]
+    np.testing.assert_allclose(per[0], ce, rtol=1e-12)
+    np.testing.assert_allclose(per[1], 0.0, atol=1e-12)
+    np.testing.assert_allclose(per[2], -np.log(c.astype(np.float64)), rtol=1e-9)
+
+
+def test_train_losses_alpha_combination_is_linear():
+    args = _train_inputs(2, 4, 40, 3, seed=2)
+    _, tot = oracle.train_losses(*args)
+    for i, a in enumerate([(1, 0, 0), (0, 1, 0), (0, 0, 1)]):
+        _, t = oracle.train_losses(*args, alpha=a)
+        assert t[3] == pytest.approx(tot[i], rel=1e-14)
+    assert tot[3] == pytest.approx(0.1 * tot[0] + 0.9 * tot[1] + tot[2], rel=1e-14)
