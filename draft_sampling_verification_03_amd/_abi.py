@@ -54,6 +54,10 @@ def library():
         L.dspark_tv_overlap_workspace.argtypes = [_i, _i]
         L.dspark_tv_overlap_workspace.restype = _sz
         L.dspark_tv_overlap.argtypes = [_i, _i, _i, _f] + [_vp] * 6 + [_sz, _vp]
+        L.dspark_train_losses_workspace.argtypes = [_i, _i, _i]
+        L.dspark_train_losses_workspace.restype = _sz
+        L.dspark_train_losses.argtypes = ([_i] * 5 + [_f] + [_vp] * 7 + [_f, _f, _f]
+                                          + [_vp] * 3 + [_sz, _vp])
         L.dspark_device_error.argtypes = [_vp, _vp, _vp]
         L.dspark_clear_device_error.argtypes = [_vp, _vp]
         L.dspark_trace_enable.argtypes = [_i]
@@ -61,6 +65,7 @@ def library():
         L.dspark_trace_entry.argtypes = [_i, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                          C.POINTER(C.c_int)]
         for name in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_tv_overlap",
+                     "dspark_train_losses",
                      "dspark_device_error", "dspark_clear_device_error", "dspark_trace_enable",
                      "dspark_trace_collect", "dspark_trace_entry"):
             getattr(L, name).restype = _i
@@ -130,6 +135,17 @@ def dspark_tv_overlap_workspace(n_rows, V):
 def dspark_tv_overlap(n_rows, V, dt, temp, P, Q, p_stats, q_stats, c_star, ws, ws_bytes, stream):
     return library().dspark_tv_overlap(n_rows, V, dt, temp, _p(P), _p(Q), _p(p_stats),
                                        _p(q_stats), _p(c_star), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_train_losses_workspace(R, gamma, V):
+    return library().dspark_train_losses_workspace(R, gamma, V)
+
+
+def dspark_train_losses(R, gamma, V, r, dt, temp, U, W1, W2, P, x0, y, c, a_ce, a_tv, a_conf,
+                        per_pos, totals, ws, ws_bytes, stream):
+    return library().dspark_train_losses(R, gamma, V, r, dt, temp, _p(U), _p(W1), _p(W2), _p(P),
+                                         _p(x0), _p(y), _p(c), a_ce, a_tv, a_conf, _p(per_pos),
+                                         _p(totals), _p(ws), ws_bytes, _s(stream))
 
 
 def dspark_device_error(ws, stream):

@@ -128,3 +128,27 @@ def tv_overlap(P, Q, *, p_stats=None, q_stats=None, temp=1.0, ws=None, stream=No
                              buf.numel(), _stream(stream))
     _check(st, "dspark_tv_overlap")
     return out
+
+
+def train_losses(U, W1, W2, P, x0, y, c, *, temp=1.0, alpha=(0.1, 0.9, 1.0), per_pos=True,
+                 ws=None, stream=None, out=None):
+    """Forward-only training losses on the label prefix.  U [R][gamma][V], P
+    [R][gamma + 1][V] (position k of request rho at row rho (gamma + 1) + k - 1),
+    y [R][gamma] int32 labels, c [R][gamma] fp32 confidences.  Returns
+    {"per_pos": [3][R][gamma] (CE, L1, BCE) or None, "totals": [4] fp64
+    (L_ce, L_tv, L_conf, L)}."""
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dt = _dt(U)
+    dev = U.device
+    if out is None:
+        out = dict(per_pos=torch.empty((3, R, gamma), dtype=torch.float32, device=dev)
+                   if per_pos else None,
+                   totals=torch.empty(4, dtype=torch.float64, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(A.dspark_train_losses_workspace(R, gamma, V))
+    st = A.dspark_train_losses(R, gamma, V, r, dt, float(temp), U, W1, W2, P, x0, y, c,
+                               float(alpha[0]), float(alpha[1]), float(alpha[2]), out["per_pos"],
+                               out["totals"], buf, buf.numel(), _stream(stream))
+    _check(st, "dspark_train_losses")
+    return out

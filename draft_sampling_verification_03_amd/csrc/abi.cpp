@@ -157,6 +157,61 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
   return from_hip(launch_verify(L, stream));
 }
 
+size_t dspark_train_losses_workspace(int R, int gamma, int V) {
+  if (R < 1 || gamma < 1 || V < 1) return 0;
+  return train_ws_bytes(R, gamma, V);
+}
+
+dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                  const void *U, const void *W1, const void *W2, const void *P,
+                                  const int32_t *x0, const int32_t *y, const float *c, float a_ce,
+                                  float a_tv, float a_conf, float *per_pos, double *totals,
+                                  void *ws, size_t ws_bytes, hipStream_t stream) {
+  dspark_status s = check_common(R, gamma, V, r, dt, temp);
+  if (s != DSPARK_OK) return s;
+  if (!U || !W1 || !W2 || !P || !x0 || !y || !c || !totals || !ws) return DSPARK_ERR_NULL;
+  if (!isfinite(a_ce) || !isfinite(a_tv) || !isfinite(a_conf)) return DSPARK_ERR_VALUE;
+  if (!aligned16(P) || !aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(ws))
+    return DSPARK_ERR_ALIGN;
+  if ((int64_t)R * (gamma + 1) > (1 << 24)) return DSPARK_ERR_SHAPE;
+  if (ws_bytes < train_ws_bytes(R, gamma, V)) return DSPARK_ERR_WORKSPACE;
+  const size_t n = (size_t)R * gamma;
+  const int rows = R * (gamma + 1);
+  size_t off = 0;
+  int32_t *err = (int32_t *)carve(ws, &off, kWsHeader);
+  TrainLaunch T{};
+  DraftLaunch &D = T.draft;
+  D.err = err;
+  D.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
+  D.sh = (float *)carve(ws, &off, n * 4);
+  D.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  D.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  D.x = (int32_t *)carve(ws, &off, n * 4);
+  D.q_stats = (float *)carve(ws, &off, n * 8);
+  D.q_x = (float *)carve(ws, &off, n * 4);
+  D.logq_x = (float *)carve(ws, &off, n * 4);
+  D.R = R; D.gamma = gamma; D.V = V; D.r = r; D.bf16 = dt == DSPARK_BF16; D.invT = 1.0f / temp;
+  D.U = U; D.W1 = W1; D.W2 = W2; D.x0 = x0; D.x_force = y;
+  VerifyLaunch &L = T.verify;
+  L.err = err;
+  L.p_chunks = (float2 *)carve(ws, &off, (size_t)rows * 4 * 8);
+  L.bonus_tiles = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
+  L.pair_partials = (float2 *)carve(ws, &off, n * n_tiles_of(V) * 8);
+  L.row_map = (int4 *)carve(ws, &off, n * 16);
+  L.A_rows = carve(ws, &off, n * kMaxRowBytes);
+  T.ell = (int32_t *)carve(ws, &off, ((size_t)R + 1) * 4);
+  T.row_offset = (int32_t *)carve(ws, &off, ((size_t)R + 1) * 4);
+  L.n_acc = (int32_t *)carve(ws, &off, ((size_t)R + 1) * 4);
+  L.y = (int32_t *)carve(ws, &off, (size_t)rows * 4);
+  L.c_star = (float *)carve(ws, &off, n * 4);
+  L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.rows_capacity = rows; L.bf16 = D.bf16;
+  L.invT = D.invT; L.ell = T.ell; L.row_offset = T.row_offset; L.P = P; L.U = U; L.W1 = W1;
+  L.W2 = W2; L.x0 = x0; L.x = y; L.q_stats = D.q_stats; L.q_x = D.q_x;
+  T.R = R; T.gamma = gamma; T.c = c; T.a_ce = a_ce; T.a_tv = a_tv; T.a_conf = a_conf;
+  T.per_pos = per_pos; T.totals = totals;
+  return from_hip(launch_train(T, stream));
+}
+
 size_t dspark_tv_overlap_workspace(int n_rows, int V) {
   if (n_rows < 1 || V < 1) return 0;
   return overlap_ws_bytes(n_rows, V);

@@ -37,6 +37,10 @@ struct SampleParams {
   float b_conf;
   const float *conf_temp;    // [gamma] T_k, or NULL (1)
   float *c;
+  // teacher forcing: if set, x_k is the label x_force[rho][k-1] instead of a
+  // draw, and logq_x (if set) receives log q_k(x_k)
+  const int32_t *x_force;
+  float *logq_x;
   int32_t *err;
 };
 
@@ -60,6 +64,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   const int cpt = (nT + kBlock - 1) / kBlock;
   const int t0 = min(tid * cpt, nT), t1 = min(t0 + cpt, nT);
   float2 pt[kCpt];
+  const int forced_raw = p.x_force != nullptr ? p.x_force[slot] : 0;
   {
     const T *Acur = reinterpret_cast<const T *>(p.A_cur) + (int64_t)rho * r;
     if (p.a_tokens != nullptr)  // validated (and flagged) by the product kernel
@@ -125,6 +130,15 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     if (tid == 0) flag_error(p.err, kErrNonFinite);
     tstar = 0;
   }
+  int forced = -1;  // the label's column, under teacher forcing
+  if (p.x_force != nullptr) {
+    forced = forced_raw;
+    if (forced < 0 || forced >= V) {
+      if (tid == 0) flag_error(p.err, kErrToken);
+      forced = 0;
+    }
+    tstar = forced / kTileN;
+  }
   if (t0 <= tstar && tstar < t1) {  // the owner of the tile: mass before it, its max
     float run = base;
     float mt = 0.0f;
@@ -158,7 +172,9 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
     if (target < cdf0 && e0 > 0.0f) pick = 2 * lane;
     else if (target < cdf1 && e1 > 0.0f) pick = 2 * lane + 1;
     pick = wave_min_int(pick);
-    if (pick == 0x7fffffff) {
+    if (forced >= 0) {
+      pick = forced - tstar * kTileN;
+    } else if (pick == 0x7fffffff) {
       int lp = -1;
       if (e0 > 0.0f) lp = 2 * lane;
       if (e1 > 0.0f) lp = 2 * lane + 1;
@@ -172,6 +188,7 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
       p.q_stats[2 * slot] = m;
       p.q_stats[2 * slot + 1] = S;
       p.q_x[slot] = fexp(zp - m) / S;
+      if (p.logq_x != nullptr) p.logq_x[slot] = (zp - m) - logf(S);
     }
     // 7. the next step's transition row A_{k+1}[rho] = W1[x_k], by this wave
     //    (no barrier: the token is in its registers)
@@ -233,6 +250,7 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   sp.invT = L.invT; sp.U = L.U; sp.W1 = L.W1; sp.W2 = L.W2; sp.x = L.x;
   sp.q_stats = L.q_stats; sp.q_x = L.q_x; sp.tile_stats = L.tile_stats;
   sp.seed = L.seed; sp.round = L.round; sp.err = L.err;
+  sp.x_force = L.x_force; sp.logq_x = L.logq_x;
   if (L.h != nullptr) {
     const int n_slots = L.R * L.gamma;
     DSPARK_LAUNCH("head_hidden_dot", stream,

@@ -26,6 +26,8 @@ struct DraftLaunch {
   uint64_t seed, round;
   int32_t *x;
   float *q_stats, *q_x, *c;
+  const int32_t *x_force;  // [R][gamma] labels (teacher forcing) or NULL
+  float *logq_x;           // [R][gamma] or NULL
   // workspace pieces
   int32_t *err;
   float2 *tile_stats;  // [R][n_tiles]
@@ -77,10 +79,22 @@ struct OverlapLaunch {
   float *partial;               // [n_rows][4]
 };
 
+struct TrainLaunch {
+  int R, gamma;
+  DraftLaunch draft;    // teacher-forced: x_force = labels, logq_x set
+  VerifyLaunch verify;  // every position admitted; its c_star feeds the losses
+  int32_t *ell, *row_offset;  // [R], [R + 1]: filled on the device
+  const float *c;
+  double a_ce, a_tv, a_conf;
+  float *per_pos;  // [3][R][gamma] or NULL
+  double *totals;  // [4]
+};
+
 hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream);
 hipError_t launch_schedule(const ScheduleLaunch &L, hipStream_t stream);
 hipError_t launch_verify(const VerifyLaunch &L, hipStream_t stream);
 hipError_t launch_overlap(const OverlapLaunch &L, hipStream_t stream);
+hipError_t launch_train(const TrainLaunch &L, hipStream_t stream);
 hipError_t launch_clear_error(int32_t *err, hipStream_t stream);
 
 // workspace layouts (bytes), each piece 256-byte aligned
@@ -102,6 +116,12 @@ inline size_t verify_ws_bytes(int R, int gamma, int V, int rows_capacity) {
   return kWsHeader + ws_align((size_t)rows_capacity * 4 * 8) +
          ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * n_tiles_of(V) * 8) +
          ws_align((size_t)R * gamma * 16) + ws_align((size_t)R * gamma * kMaxRowBytes);
+}
+inline size_t train_ws_bytes(int R, int gamma, int V) {
+  const size_t n = (size_t)R * gamma;
+  return draft_ws_bytes(R, gamma, V) + verify_ws_bytes(R, gamma, V, R * (gamma + 1)) +
+         4 * ws_align(n * 4) + ws_align(n * 8) + 3 * ws_align(((size_t)R + 1) * 4) +
+         ws_align((size_t)R * (gamma + 1) * 4);
 }
 inline size_t overlap_ws_bytes(int n_rows, int V) {
   (void)V;

@@ -209,6 +209,42 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
                             int32_t *n_acc, int32_t *y, float *c_star,
                             void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------------- train_losses --
+ * Forward-only training reductions of the drafter on the ground-truth prefix
+ * (Blog "Training objective"; KB section 5).  With the label prefix
+ * x_0 = x0[rho], x_k = y[rho][k-1] (teacher forcing):
+ *   q_k    = the draft law of dspark_draft at position k, conditioned on x_{k-1}
+ *   p_k    = softmax(P[rho (gamma+1) + k - 1] * (1/temp))
+ *   CE_k   = -log q_k(y_k)
+ *   L1_k   = sum_v |p_k(v) - q_k(v)| = 2 (1 - c*_k), twice the total variation
+ *   BCE_k  = -(c*_k log c_k + (1 - c*_k) log(1 - c_k)), c*_k = sum_v min(p_k, q_k)
+ *   w_k    = exp(-(k - 1) / gamma)
+ *   L_x    = (1/R) sum_rho (sum_k w_k x_k) / (sum_k w_k) for x = CE, L1, BCE
+ *   L      = a_ce L_ce + a_tv L_tv + a_conf L_conf (the page's defaults 0.1, 0.9, 1.0)
+ * q and c* come from the draft and verification kernels themselves (a
+ * teacher-forced draft pass, then a verification pass with every position
+ * admitted), so the losses see exactly the distributions the hot path draws from.
+ * Inputs
+ *   U [R][gamma][V], W1, W2, x0: as for dspark_draft (device, dt)
+ *   P [R][gamma+1][V] target logits, position k of request rho at row
+ *     rho (gamma+1) + k - 1 (the last row of each request is not read) (dt)
+ *   y [R][gamma] labels in [0, V), int32; an out-of-range label sets the
+ *     DSPARK_DEVERR_TOKEN bit of the device error word and is read as 0
+ *   c [R][gamma] confidences, fp32 (log of 0 or 1 gives an infinite BCE)
+ *   a_ce, a_tv, a_conf: finite loss weights
+ * Outputs (device)
+ *   per_pos [3][R][gamma] (CE, L1, BCE) per position, fp32, or NULL
+ *   totals  [4] (L_ce, L_tv, L_conf, L), fp64, summed in a fixed order
+ * Workspace: dspark_train_losses_workspace(R, gamma, V) bytes; the device
+ * error word is its first word (dspark_device_error). */
+size_t dspark_train_losses_workspace(int R, int gamma, int V);
+dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                  const void *U, const void *W1, const void *W2, const void *P,
+                                  const int32_t *x0, const int32_t *y, const float *c,
+                                  float a_ce, float a_tv, float a_conf,
+                                  float *per_pos, double *totals,
+                                  void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------- tv_overlap --
  * Soft confidence label on explicit logit pairs (Blog "Total variation label";
  * KB section 4): c*[i] = sum_v min(p_i(v), q_i(v)) with p_i = softmax(P[i]/temp)

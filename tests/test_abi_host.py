@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ds.library()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in dspark.h but not exported"
 
@@ -133,6 +133,33 @@ def overlap_args(**over):
 ])
 def test_overlap_validation(over, expect):
     assert A.dspark_tv_overlap(**overlap_args(**over)) == expect
+
+
+def train_args(**over):
+    a = dict(R=4, gamma=4, V=1024, r=16, dt=A.DSPARK_BF16, temp=1.0, U=P, W1=P, W2=P, P=P, x0=P,
+             y=P, c=P, a_ce=0.1, a_tv=0.9, a_conf=1.0, per_pos=None, totals=P, ws=P,
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(U=None), NULL), (dict(P=None), NULL), (dict(y=None), NULL), (dict(c=None), NULL),
+    (dict(totals=None), NULL), (dict(ws=None), NULL), (dict(R=0), SHAPE), (dict(gamma=65), SHAPE),
+    (dict(V=1001), SHAPE), (dict(r=8), SHAPE), (dict(dt=3), DTYPE), (dict(temp=0.0), VALUE),
+    (dict(a_tv=float("nan")), VALUE), (dict(a_ce=float("inf")), VALUE), (dict(ws_bytes=100), WS),
+    (dict(P=P + 4), ALIGN), (dict(R=1 << 20, gamma=32), SHAPE),
+])
+def test_train_losses_validation(over, expect):
+    assert A.dspark_train_losses(**train_args(**over)) == expect
+
+
+def test_train_losses_workspace_covers_its_parts():
+    R, gamma, V = 128, 16, 151936
+    ws = A.dspark_train_losses_workspace(R, gamma, V)
+    assert ws >= A.dspark_draft_workspace(R, gamma, V, 256, A.DSPARK_BF16) + \
+        A.dspark_verify_workspace(R, gamma, V, R * (gamma + 1))
+    assert A.dspark_train_losses_workspace(0, 4, 1024) == 0
 
 
 def test_device_error_argument_checks():

@@ -532,7 +532,7 @@ def _train_inputs(R, gamma, V, r, seed=0):
     g = np.random.default_rng(seed)
     U = g.normal(0, 1.0, (R, gamma, V)).astype(np.float32)
     W1 = g.normal(0, 0.5, (V, r)).astype(np.float32)
-    W2 = g.normal(0, 0.5, (r, V)).astype(np.float32)
+    W2 = g.normal(0, 0.5, (V, r)).astype(np.float32)  # column-major r x V factor
     P = g.normal(0, 1.5, (R, gamma + 1, V)).astype(np.float32)
     x0 = g.integers(0, V, R).astype(np.int32)
     y = g.integers(0, V, (R, gamma)).astype(np.int32)
@@ -547,7 +547,7 @@ def test_train_losses_uniform_case():
     R, gamma, V, r = 2, 5, 8, 3
     U = np.zeros((R, gamma, V), np.float32)
     W1 = np.zeros((V, r), np.float32)
-    W2 = np.zeros((r, V), np.float32)
+    W2 = np.zeros((V, r), np.float32)
     P = np.zeros((R, gamma + 1, V), np.float32)
     x0 = np.array([1, 6], np.int32)
     y = np.arange(R * gamma, dtype=np.int32).reshape(R, gamma) % V
@@ -607,7 +607,7 @@ def test_train_losses_temperature_and_library_softmax():
     R, gamma, V, r = 2, 4, 33, 2
     U, _, _, x0, y, _, c = _train_inputs(R, gamma, V, r, seed=5)
     W1 = np.zeros((V, r), np.float32)
-    W2 = np.zeros((r, V), np.float32)
+    W2 = np.zeros((V, r), np.float32)
     P = np.zeros((R, gamma + 1, V), np.float32)
     P[:, :gamma] = U
     T = 0.6
