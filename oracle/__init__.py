@@ -67,6 +67,9 @@ def _declare(L):
     L.orc_verify_request.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_double, C.c_int, _vp,
                                      _vp, _vp, _vp, C.c_int, _i32p, C.c_uint64, C.c_uint64, C.c_int,
                                      C.c_int, _i32p, _i32p, _dp, _dp, _dp, _dp, _dp, _i32p]
+    L.orc_verify_request_rows.argtypes = L.orc_verify_request.argtypes
+    L.orc_rnn_states.argtypes = [C.c_int] * 4 + [_vp, _f32p, _vp, _f32p, C.c_int, _i32p, _f32p,
+                                                 _dp]
 
 
 def _ptr(a, ctype=None):
@@ -224,10 +227,17 @@ def schedule_bruteforce(c, SPS):
 
 # --------------------------------------------------------------------- verify
 def verify_request(P_req, U_req, W1, W2, x0, x, ell, seed, rnd, rho, temp=1.0, force_n=-1,
-                   want_cdf=False):
-    """P_req is [ell+1][V] (the request's flattened target rows), U_req [gamma][V]."""
+                   want_cdf=False, A_rows=None):
+    """P_req is [ell+1][V] (the request's flattened target rows), U_req [gamma][V].
+    With A_rows [gamma][r] the draft's transition row of position k is
+    A_rows[k-1] (W1 is then ignored)."""
     gamma, V = U_req.shape
-    r = W1.shape[1]
+    r = (W1 if A_rows is None else A_rows).shape[1]
+    fn = lib().orc_verify_request
+    if A_rows is not None:
+        A_rows = np.ascontiguousarray(A_rows)
+        assert A_rows.shape == (gamma, r) and A_rows.dtype == U_req.dtype
+        W1, fn = A_rows, lib().orc_verify_request_rows
     P_req, U_req = np.ascontiguousarray(P_req), np.ascontiguousarray(U_req)
     assert P_req.shape[0] >= ell + 1
     x = np.ascontiguousarray(x, dtype=np.int32)
@@ -237,7 +247,7 @@ def verify_request(P_req, U_req, W1, W2, x0, x, ell, seed, rnd, rho, temp=1.0, f
     fcdf = np.zeros(V) if want_cdf else None
     fu = C.c_double()
     fb = C.c_int32()
-    rc = lib().orc_verify_request(gamma, V, r, dtype_code(U_req), temp, int(ell), _ptr(P_req),
+    rc = fn(gamma, V, r, dtype_code(U_req), temp, int(ell), _ptr(P_req),
                                   _ptr(U_req), _ptr(W1), _ptr(W2), int(x0), _ptr(x, C.c_int32),
                                   seed, rnd, rho, int(force_n), C.byref(n_acc), _ptr(y, C.c_int32),
                                   _ptr(c_star, C.c_double), _ptr(ratio, C.c_double),
@@ -269,3 +279,26 @@ def train_losses(U, W1, W2, x0, y, P, c, temp=1.0, alpha=(0.1, 0.9, 1.0)):
     assert rc == 0, "oracle train_losses rejected its arguments"
     return per, tot
 
+
+
+# ---------------------------------------------------------- recurrent head
+def rnn_states(G_E, G_h_req, W_hh, b_hh, x0, x, s0=None):
+    """GRU states s_1..s_gamma of one request (fp64 [gamma][r]).  G_E [V][3r]
+    (float32 or bf16 bits), G_h_req [gamma][3r] fp32, W_hh [r][3r] column-major
+    (same dtype as G_E), b_hh [3r] fp32, s0 [r] fp32 or None; tokens x0, then
+    x[0..gamma-2]."""
+    gamma, g3 = G_h_req.shape
+    r = g3 // 3
+    V = G_E.shape[0]
+    G_E, W_hh = np.ascontiguousarray(G_E), np.ascontiguousarray(W_hh)
+    assert G_E.shape == (V, g3) and W_hh.shape == (r, g3) and W_hh.dtype == G_E.dtype
+    G_h_req = np.ascontiguousarray(G_h_req, dtype=np.float32)
+    b_hh = np.ascontiguousarray(b_hh, dtype=np.float32)
+    x = np.ascontiguousarray(np.resize(np.asarray(x, dtype=np.int32), max(gamma - 1, 1)))
+    s0 = None if s0 is None else np.ascontiguousarray(s0, dtype=np.float32)
+    out = np.zeros((gamma, r))
+    rc = lib().orc_rnn_states(gamma, V, r, dtype_code(G_E), _ptr(G_E), _ptr(G_h_req, C.c_float),
+                              _ptr(W_hh), _ptr(b_hh, C.c_float), int(x0), _ptr(x, C.c_int32),
+                              _ptr(s0, C.c_float), _ptr(out, C.c_double))
+    assert rc == 0, "oracle rnn_states rejected its arguments"
+    return out

@@ -9,7 +9,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = ["oracle_core.cpp", "oracle_draft.cpp", "oracle_verify.cpp", "oracle_schedule.cpp",
-           "oracle_train.cpp"]
+           "oracle_train.cpp", "oracle_rnn.cpp"]
 LIB = os.path.join(HERE, "liboracle.so")
 
 

@@ -175,6 +175,32 @@ int orc_verify_request(int gamma, int V, int r, int dt, double temp, int ell,
                        double *ratio, double *u_acc, double *final_cdf, double *final_u,
                        int32_t *residual_fallback);
 
+/* As orc_verify_request, with the draft's transition row of position k taken
+ * from row k - 1 of A_rows [gamma][r] (dt) instead of W1[x_{k-1}]. */
+int orc_verify_request_rows(int gamma, int V, int r, int dt, double temp, int ell,
+                            const void *P_req, const void *U_req, const void *A_rows,
+                            const void *W2, int x0, const int32_t *x, uint64_t seed,
+                            uint64_t round, int rho, int force_n, int32_t *n_acc, int32_t *y,
+                            double *c_star, double *ratio, double *u_acc, double *final_cdf,
+                            double *final_u, int32_t *residual_fallback);
+
+/* Recurrent sequential head (Blog "RNN sequential head"; KB section 3): the
+ * state s_k = f(s_{k-1}, E(x_{k-1}), h_k) with f a gated recurrent unit, read
+ * as the standard GRU (reset gate, update gate, candidate):
+ *   g = G_E[x_{k-1}] + G_h[k-1]            input pre-activations [3r]
+ *   a = W_hh s_{k-1} + b_hh                 recurrent pre-activations [3r]
+ *   rg = sigmoid(g_r + a_r), zg = sigmoid(g_z + a_z)
+ *   n  = tanh(g_n + rg * a_n)
+ *   s_k = (1 - zg) * n + zg * s_{k-1}
+ * G_E [V][3r] (dt) is the input projection of the token embedding table, G_h
+ * [gamma][3r] fp32 that of the backbone hidden states (input biases folded
+ * in), W_hh column-major [r][3r] (dt, element (g, i) at W_hh[i * 3r + g]),
+ * b_hh [3r] fp32, s0 [r] fp32 or NULL (zeros).  Tokens: x_0 = x0, x_k = x[k-1].
+ * Output s_out [gamma][r] in fp64.  Returns 0, or -1 on bad arguments. */
+int orc_rnn_states(int gamma, int V, int r, int dt, const void *G_E, const float *G_h,
+                   const void *W_hh, const float *b_hh, int x0, const int32_t *x,
+                   const float *s0, double *s_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,13 +14,15 @@
 #include "oracle.h"
 #include "oracle_internal.h"
 
-extern "C" int orc_verify_request(int gamma, int V, int r, int dt, double temp, int ell,
-                                  const void *P_req, const void *U_req, const void *W1,
-                                  const void *W2, int x0, const int32_t *x, uint64_t seed,
-                                  uint64_t round, int rho, int force_n, int32_t *n_acc,
-                                  int32_t *y, double *c_star, double *ratio, double *u_acc,
-                                  double *final_cdf, double *final_u,
-                                  int32_t *residual_fallback) {
+// A_rows (or NULL): the draft's transition row of position k is row k - 1 of
+// A_rows [gamma][r] instead of W1[x_{k-1}] (a head whose bias row is not a
+// table lookup, e.g. the recurrent head's state).
+static int verify_impl(int gamma, int V, int r, int dt, double temp, int ell,
+                       const void *P_req, const void *U_req, const void *W1, const void *A_rows,
+                       const void *W2, int x0, const int32_t *x, uint64_t seed, uint64_t round,
+                       int rho, int force_n, int32_t *n_acc, int32_t *y, double *c_star,
+                       double *ratio, double *u_acc, double *final_cdf, double *final_u,
+                       int32_t *residual_fallback) {
   if (gamma < 1 || V < 1 || ell < 0 || ell > gamma || !(temp > 0.0)) return -1;
   if (x0 < 0 || x0 >= V) return -1;
   for (int k = 0; k < ell; ++k)
@@ -32,9 +34,10 @@ extern "C" int orc_verify_request(int gamma, int V, int r, int dt, double temp, 
     p[k - 1] = orc_internal_softmax(
         orc_internal_scaled_row(V, dt, temp, orc_internal_row(dt, P_req, k - 1, V)));
   for (int k = 1; k <= ell; ++k) {
-    int prev = k == 1 ? x0 : x[k - 2];
+    const int prev = k == 1 ? x0 : x[k - 2];
     q[k - 1] = orc_internal_softmax(orc_internal_draft_logits(
-        V, r, dt, temp, orc_internal_row(dt, U_req, k - 1, V), W1, W2, prev));
+        V, r, dt, temp, orc_internal_row(dt, U_req, k - 1, V), A_rows ? A_rows : W1, W2,
+        A_rows ? k - 1 : prev));
   }
 
   // Soft confidence target and the accept/reject decisions.
@@ -86,4 +89,29 @@ extern "C" int orc_verify_request(int gamma, int V, int r, int dt, double temp, 
   for (int i = 0; i < n; ++i) y[i] = x[i];
   y[n] = final_token;
   return final_token >= 0 ? 0 : -1;
+}
+
+extern "C" int orc_verify_request(int gamma, int V, int r, int dt, double temp, int ell,
+                                  const void *P_req, const void *U_req, const void *W1,
+                                  const void *W2, int x0, const int32_t *x, uint64_t seed,
+                                  uint64_t round, int rho, int force_n, int32_t *n_acc,
+                                  int32_t *y, double *c_star, double *ratio, double *u_acc,
+                                  double *final_cdf, double *final_u,
+                                  int32_t *residual_fallback) {
+  return verify_impl(gamma, V, r, dt, temp, ell, P_req, U_req, W1, nullptr, W2, x0, x, seed,
+                     round, rho, force_n, n_acc, y, c_star, ratio, u_acc, final_cdf, final_u,
+                     residual_fallback);
+}
+
+extern "C" int orc_verify_request_rows(int gamma, int V, int r, int dt, double temp, int ell,
+                                       const void *P_req, const void *U_req, const void *A_rows,
+                                       const void *W2, int x0, const int32_t *x, uint64_t seed,
+                                       uint64_t round, int rho, int force_n, int32_t *n_acc,
+                                       int32_t *y, double *c_star, double *ratio, double *u_acc,
+                                       double *final_cdf, double *final_u,
+                                       int32_t *residual_fallback) {
+  if (!A_rows) return -1;
+  return verify_impl(gamma, V, r, dt, temp, ell, P_req, U_req, nullptr, A_rows, W2, x0, x, seed,
+                     round, rho, force_n, n_acc, y, c_star, ratio, u_acc, final_cdf, final_u,
+                     residual_fallback);
 }

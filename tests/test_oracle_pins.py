@@ -626,3 +626,94 @@ def test_train_losses_alpha_combination_is_linear():
         _, t = oracle.train_losses(*args, alpha=a)
         assert t[3] == pytest.approx(tot[i], rel=1e-14)
     assert tot[3] == pytest.approx(0.1 * tot[0] + 0.9 * tot[1] + tot[2], rel=1e-14)
+
+
+# ------------------------------------------------------------ recurrent head
+# Blog, "RNN sequential head"; KB section 3: s_k = f(s_{k-1}, E(x_{k-1}), h_k)
+# with a gated update, read as the standard GRU.
+def _gru_case(V, r, gamma, bf16, seed):
+    g = np.random.default_rng(seed)
+    GE = g.normal(0, 1.0, (V, 3 * r)).astype(np.float32)
+    Gh = g.normal(0, 1.0, (gamma, 3 * r)).astype(np.float32)
+    Whh = g.normal(0, 0.4, (r, 3 * r)).astype(np.float32)
+    bhh = g.normal(0, 0.5, 3 * r).astype(np.float32)
+    s0 = g.normal(0, 0.5, r).astype(np.float32)
+    x0 = int(g.integers(0, V))
+    x = g.integers(0, V, gamma - 1).astype(np.int32)
+    if bf16:
+        import synth
+        GE, Whh = synth.to_bf16_bits(GE), synth.to_bf16_bits(Whh)
+    return GE, Gh, Whh, bhh, s0, x0, x
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_rnn_states_match_library_gru_cell(bf16):
+    """torch.nn.GRUCell (float64) with input u = [one-hot(x_{k-1}); G_h[k]],
+    input weights [G_E^T | I] and no input bias has input pre-activations
+    exactly G_E[x_{k-1}] + G_h[k]; its recurrent weights are W_hh (stored
+    column-major here) and b_hh."""
+    import torch
+    import synth
+    V, r, gamma = 11, 8, 6
+    GE, Gh, Whh, bhh, s0, x0, x = _gru_case(V, r, gamma, bf16, seed=3)
+    wid = (lambda a: synth.bf16_bits_to_f32(a)) if bf16 else (lambda a: a)
+    cell = torch.nn.GRUCell(V + 3 * r, r, dtype=torch.float64)
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(np.concatenate(
+            [wid(GE).astype(np.float64).T, np.eye(3 * r)], axis=1)))
+        cell.bias_ih.zero_()
+        cell.weight_hh.copy_(torch.from_numpy(wid(Whh).astype(np.float64).T))
+        cell.bias_hh.copy_(torch.from_numpy(bhh.astype(np.float64)))
+        s = torch.from_numpy(s0.astype(np.float64))[None]
+        ref = []
+        for k in range(1, gamma + 1):
+            prev = x0 if k == 1 else int(x[k - 2])
+            u = torch.zeros(1, V + 3 * r, dtype=torch.float64)
+            u[0, prev] = 1.0
+            u[0, V:] = torch.from_numpy(Gh[k - 1].astype(np.float64))
+            s = cell(u, s)
+            ref.append(s[0].numpy().copy())
+    got = oracle.rnn_states(GE, Gh, Whh, bhh, x0, x, s0=s0)
+    np.testing.assert_allclose(got, np.array(ref), rtol=1e-12, atol=1e-14)
+
+
+def test_rnn_states_closed_forms():
+    """A saturated update gate keeps the state (s_k = s_0); a closed update
+    gate with zero recurrent weights gives s_k = tanh(g_n) regardless of the
+    past; s0 = None starts from zeros."""
+    V, r, gamma = 7, 4, 3
+    GE, Gh, Whh, bhh, s0, x0, x = _gru_case(V, r, gamma, False, seed=9)
+    GEk = GE.copy()
+    GEk[:, r:2 * r] = 60.0
+    got = oracle.rnn_states(GEk, Gh, Whh, bhh, x0, x, s0=s0)
+    np.testing.assert_allclose(got, np.tile(s0.astype(np.float64), (gamma, 1)), atol=1e-12)
+    GEo = GE.copy()
+    GEo[:, r:2 * r] = -60.0
+    Z = np.zeros_like(Whh)
+    bz = np.zeros_like(bhh)
+    got = oracle.rnn_states(GEo, Gh, Z, bz, x0, x, s0=s0)
+    for k in range(1, gamma + 1):
+        prev = x0 if k == 1 else int(x[k - 2])
+        want = np.tanh(GEo[prev, 2 * r:].astype(np.float64) + Gh[k - 1, 2 * r:])
+        np.testing.assert_allclose(got[k - 1], want, rtol=1e-12, atol=1e-14)
+    a = oracle.rnn_states(GE, Gh, Whh, bhh, x0, x, s0=None)
+    b = oracle.rnn_states(GE, Gh, Whh, bhh, x0, x, s0=np.zeros(r, np.float32))
+    assert np.array_equal(a, b)
+
+
+def test_verify_with_given_rows_equals_table_rows():
+    """Verification with the transition rows given explicitly equals the
+    table form when the given rows are the table's rows W1[x_{k-1}]."""
+    g = np.random.default_rng(4)
+    gamma, V, r = 4, 300, 16
+    U = g.normal(0, 1, (gamma, V)).astype(np.float32)
+    P = g.normal(0, 1, (gamma + 1, V)).astype(np.float32)
+    W1 = g.normal(0, 0.5, (V, r)).astype(np.float32)
+    W2 = g.normal(0, 0.5, (V, r)).astype(np.float32)
+    x0 = 5
+    x = g.integers(0, V, gamma).astype(np.int32)
+    prevs = np.concatenate([[x0], x[:-1]])
+    a = oracle.verify_request(P, U, W1, W2, x0, x, gamma, 1, 2, 0)
+    b = oracle.verify_request(P, U, None, W2, x0, x, gamma, 1, 2, 0, A_rows=W1[prevs])
+    for key in ("n_acc", "y", "c_star", "ratio"):
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key]), equal_nan=True), key
