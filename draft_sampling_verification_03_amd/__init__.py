@@ -12,6 +12,7 @@ from ._abi import (  # noqa: F401
     dspark_clear_device_error, dspark_device_error, dspark_draft, dspark_draft_workspace,
     dspark_schedule, dspark_schedule_workspace, dspark_status_string, dspark_tv_overlap,
     dspark_tv_overlap_workspace, dspark_trace_collect, dspark_trace_enable, dspark_trace_entry,
-    dspark_train_losses, dspark_train_losses_workspace,
+    dspark_train_losses, dspark_train_losses_workspace, dspark_draft_rnn, dspark_verify_rnn,
     dspark_verify, dspark_verify_workspace, library, trace_summary)
-from .api import draft, schedule, train_losses, tv_overlap, verify, Workspace  # noqa: F401
+from .api import (draft, draft_rnn, schedule, train_losses, tv_overlap, verify, verify_rnn,
+                  Workspace)  # noqa: F401

@@ -54,6 +54,9 @@ def library():
         L.dspark_tv_overlap_workspace.argtypes = [_i, _i]
         L.dspark_tv_overlap_workspace.restype = _sz
         L.dspark_tv_overlap.argtypes = [_i, _i, _i, _f] + [_vp] * 6 + [_sz, _vp]
+        L.dspark_draft_rnn.argtypes = ([_i] * 5 + [_f] + [_vp] * 8 + [_u64, _u64] + [_vp] * 6
+                                       + [_sz, _vp])
+        L.dspark_verify_rnn.argtypes = L.dspark_verify.argtypes
         L.dspark_train_losses_workspace.argtypes = [_i, _i, _i]
         L.dspark_train_losses_workspace.restype = _sz
         L.dspark_train_losses.argtypes = ([_i] * 5 + [_f] + [_vp] * 7 + [_f, _f, _f]
@@ -65,7 +68,7 @@ def library():
         L.dspark_trace_entry.argtypes = [_i, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                          C.POINTER(C.c_int)]
         for name in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_tv_overlap",
-                     "dspark_train_losses",
+                     "dspark_train_losses", "dspark_draft_rnn", "dspark_verify_rnn",
                      "dspark_device_error", "dspark_clear_device_error", "dspark_trace_enable",
                      "dspark_trace_collect", "dspark_trace_entry"):
             getattr(L, name).restype = _i
@@ -135,6 +138,22 @@ def dspark_tv_overlap_workspace(n_rows, V):
 def dspark_tv_overlap(n_rows, V, dt, temp, P, Q, p_stats, q_stats, c_star, ws, ws_bytes, stream):
     return library().dspark_tv_overlap(n_rows, V, dt, temp, _p(P), _p(Q), _p(p_stats),
                                        _p(q_stats), _p(c_star), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_draft_rnn(R, gamma, V, r, dt, temp, U, W_o, G_E, G_h, W_hh, b_hh, x0, s0, seed, round_,
+                     x, q_stats, q_x, s, A, ws, ws_bytes, stream):
+    return library().dspark_draft_rnn(R, gamma, V, r, dt, temp, _p(U), _p(W_o), _p(G_E), _p(G_h),
+                                      _p(W_hh), _p(b_hh), _p(x0), _p(s0), seed, round_, _p(x),
+                                      _p(q_stats), _p(q_x), _p(s), _p(A), _p(ws), ws_bytes,
+                                      _s(stream))
+
+
+def dspark_verify_rnn(R, gamma, V, r, dt, temp, ell, row_offset, rows_capacity, P, U, A, W_o, x0,
+                      x, q_stats, q_x, seed, round_, n_acc, y, c_star, ws, ws_bytes, stream):
+    return library().dspark_verify_rnn(R, gamma, V, r, dt, temp, _p(ell), _p(row_offset),
+                                       rows_capacity, _p(P), _p(U), _p(A), _p(W_o), _p(x0),
+                                       _p(x), _p(q_stats), _p(q_x), seed, round_, _p(n_acc),
+                                       _p(y), _p(c_star), _p(ws), ws_bytes, _s(stream))
 
 
 def dspark_train_losses_workspace(R, gamma, V):

@@ -152,3 +152,50 @@ def train_losses(U, W1, W2, P, x0, y, c, *, temp=1.0, alpha=(0.1, 0.9, 1.0), per
                                out["totals"], buf, buf.numel(), _stream(stream))
     _check(st, "dspark_train_losses")
     return out
+
+
+def draft_rnn(U, W_o, G_E, G_h, W_hh, b_hh, x0, *, s0=None, temp=1.0, seed=0, round=0, ws=None,
+              stream=None, out=None):
+    """Draft with the recurrent head.  U [R][gamma][V], W_o [V][r] storage
+    (column-major r x V), G_E [V][3r], G_h [R][gamma][3r] fp32, W_hh [r][3r]
+    storage, b_hh [3r] fp32, x0 [R] int32, s0 [R][r] fp32 or None.  Returns x,
+    q_stats, q_x, s [R][gamma][r] fp32 and A [gamma][R][r] (U's dtype)."""
+    R, gamma, V = U.shape
+    r = W_o.shape[1]
+    dt = _dt(U)
+    dev = U.device
+    if out is None:
+        out = dict(x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+                   q_stats=torch.empty((R, gamma, 2), dtype=torch.float32, device=dev),
+                   q_x=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   s=torch.empty((R, gamma, r), dtype=torch.float32, device=dev),
+                   A=torch.empty((gamma, R, r), dtype=U.dtype, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(A.dspark_draft_workspace(R, gamma, V, r, dt))
+    st = A.dspark_draft_rnn(R, gamma, V, r, dt, float(temp), U, W_o, G_E, G_h, W_hh, b_hh, x0, s0,
+                            int(seed), int(round), out["x"], out["q_stats"], out["q_x"], out["s"],
+                            out["A"], buf, buf.numel(), _stream(stream))
+    _check(st, "dspark_draft_rnn")
+    return out
+
+
+def verify_rnn(ell, row_offset, P, U, A_rows, W_o, x0, x, q_stats, q_x, *, rows_capacity=None,
+               temp=1.0, seed=0, round=0, ws=None, stream=None, out=None):
+    """verify() for recurrent-head drafts: A_rows [gamma][R][r] from draft_rnn."""
+    R, gamma, V = U.shape
+    r = W_o.shape[1]
+    dt = _dt(U)
+    dev = U.device
+    rows_capacity = P.shape[0] if rows_capacity is None else rows_capacity
+    if out is None:
+        out = dict(n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+                   y=torch.empty((R, gamma + 1), dtype=torch.int32, device=dev),
+                   c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(A.dspark_verify_workspace(R, gamma, V, rows_capacity))
+    st = A.dspark_verify_rnn(R, gamma, V, r, dt, float(temp), ell, row_offset, rows_capacity, P, U,
+                             A_rows, W_o, x0, x, q_stats, q_x, int(seed), int(round),
+                             out["n_acc"], out["y"], out["c_star"], buf, buf.numel(),
+                             _stream(stream))
+    _check(st, "dspark_verify_rnn")
+    return out

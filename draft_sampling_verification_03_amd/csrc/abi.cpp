@@ -90,6 +90,34 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   return from_hip(launch_draft(L, stream));
 }
 
+dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                               const void *U, const void *W_o, const void *G_E, const float *G_h,
+                               const void *W_hh, const float *b_hh, const int32_t *x0,
+                               const float *s0, uint64_t seed, uint64_t round, int32_t *x,
+                               float *q_stats, float *q_x, float *s, void *A, void *ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  dspark_status st = check_common(R, gamma, V, r, dt, temp);
+  if (st != DSPARK_OK) return st;
+  if (!U || !W_o || !G_E || !G_h || !W_hh || !b_hh || !x0 || !x || !q_stats || !q_x || !s || !A ||
+      !ws)
+    return DSPARK_ERR_NULL;
+  if (!aligned16(U) || !aligned16(W_o) || !aligned16(A) || !aligned16(ws)) return DSPARK_ERR_ALIGN;
+  if (ws_bytes < draft_ws_bytes(R, gamma, V)) return DSPARK_ERR_WORKSPACE;
+  size_t off = 0;
+  DraftLaunch L{};
+  L.err = (int32_t *)carve(ws, &off, kWsHeader);
+  L.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
+  L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
+  L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp;
+  L.U = U; L.W1 = nullptr; L.W2 = W_o; L.x0 = x0; L.seed = seed; L.round = round; L.x = x;
+  L.q_stats = q_stats; L.q_x = q_x;
+  RnnHead H{G_E, G_h, W_hh, b_hh, s0, s, A};
+  L.rnn = &H;
+  return from_hip(launch_draft(L, stream));
+}
+
 size_t dspark_schedule_workspace(int R, int gamma) {
   if (R < 1 || gamma < 1) return 0;
   return schedule_ws_bytes(R, gamma);
@@ -125,13 +153,13 @@ size_t dspark_verify_workspace(int R, int gamma, int V, int rows_capacity) {
   return verify_ws_bytes(R, gamma, V, rows_capacity);
 }
 
-dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
-                            const int32_t *ell, const int32_t *row_offset, int rows_capacity,
-                            const void *P, const void *U, const void *W1, const void *W2,
-                            const int32_t *x0, const int32_t *x, const float *q_stats,
-                            const float *q_x, uint64_t seed, uint64_t round, int32_t *n_acc,
-                            int32_t *y, float *c_star, void *ws, size_t ws_bytes,
-                            hipStream_t stream) {
+static dspark_status verify_impl(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                 const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                                 const void *P, const void *U, const void *W1, const void *W2,
+                                 const int32_t *x0, const int32_t *x, const float *q_stats,
+                                 const float *q_x, uint64_t seed, uint64_t round, int32_t *n_acc,
+                                 int32_t *y, float *c_star, void *ws, size_t ws_bytes,
+                                 hipStream_t stream, const void *A_given) {
   dspark_status s = check_common(R, gamma, V, r, dt, temp);
   if (s != DSPARK_OK) return s;
   if ((int64_t)rows_capacity < R || (int64_t)rows_capacity > (int64_t)R * (1 + gamma))
@@ -154,7 +182,35 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
   L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp; L.ell = ell; L.row_offset = row_offset;
   L.P = P; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
   L.seed = seed; L.round = round; L.n_acc = n_acc; L.y = y; L.c_star = c_star;
+  L.A_given = A_given;
   return from_hip(launch_verify(L, stream));
+}
+
+dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                            const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                            const void *P, const void *U, const void *W1, const void *W2,
+                            const int32_t *x0, const int32_t *x, const float *q_stats,
+                            const float *q_x, uint64_t seed, uint64_t round, int32_t *n_acc,
+                            int32_t *y, float *c_star, void *ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return verify_impl(R, gamma, V, r, dt, temp, ell, row_offset, rows_capacity, P, U, W1, W2, x0,
+                     x, q_stats, q_x, seed, round, n_acc, y, c_star, ws, ws_bytes, stream,
+                     nullptr);
+}
+
+dspark_status dspark_verify_rnn(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                                const void *P, const void *U, const void *A, const void *W_o,
+                                const int32_t *x0, const int32_t *x, const float *q_stats,
+                                const float *q_x, uint64_t seed, uint64_t round, int32_t *n_acc,
+                                int32_t *y, float *c_star, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!A) return DSPARK_ERR_NULL;
+  if (!aligned16(A)) return DSPARK_ERR_ALIGN;
+  // the table argument only has to pass the pointer checks: with given rows
+  // no kernel reads it
+  return verify_impl(R, gamma, V, r, dt, temp, ell, row_offset, rows_capacity, P, U, A, W_o, x0,
+                     x, q_stats, q_x, seed, round, n_acc, y, c_star, ws, ws_bytes, stream, A);
 }
 
 size_t dspark_train_losses_workspace(int R, int gamma, int V) {

@@ -39,6 +39,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
+// binary32 -> bfloat16, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ void store_elem(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(bf16_t *p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+
 // element type traits: T = float (DSPARK_F32) or bf16_t (DSPARK_BF16)
 template <typename T> struct Elem;
 template <> struct Elem<float> {

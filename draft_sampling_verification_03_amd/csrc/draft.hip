@@ -238,6 +238,68 @@ __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, in
   if (lane == 0) sh[slot] = acc;
 }
 
+// Recurrent head (Blog "RNN sequential head"; KB section 3), the gated update
+// read as a GRU: one workgroup per request, thread j < r owns state unit j and
+// its three gate rows.  W_hh is column-major ([r][3r]), so for each input i
+// the threads read one contiguous row segment; s_{k-1} sits in LDS.
+//   g = G_E[x_{k-1}] + G_h[rho][k-1];  a = W_hh s_{k-1} + b_hh
+//   s_k = (1 - sigmoid(g_z + a_z)) tanh(g_n + sigmoid(g_r + a_r) a_n)
+//         + sigmoid(g_z + a_z) s_{k-1}
+// s_k is kept in fp32; the product's transition row A_k = s_k in the
+// weights' element type.
+struct GruParams {
+  int R, gamma, V, r, k;
+  const void *G_E;     // [V][3r]
+  const float *G_h;    // [R][gamma][3r]
+  const void *W_hh;    // [r][3r]
+  const float *b_hh;   // [3r]
+  const int32_t *x0, *x;
+  const float *s0;     // [R][r] or NULL (zeros)
+  float *s;            // [R][gamma][r]
+  void *A;             // [gamma][R][r]
+  int32_t *err;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gru_step_kernel(GruParams p) {
+  __shared__ float sprev[kMaxRank];
+  const int rho = blockIdx.x, j = threadIdx.x, r = p.r, g3 = 3 * r, k = p.k;
+  int prev = k == 1 ? p.x0[rho] : p.x[(int64_t)rho * p.gamma + k - 2];
+  if (prev < 0 || prev >= p.V) {
+    if (j == 0) flag_error(p.err, kErrToken);
+    prev = min(max(prev, 0), p.V - 1);
+  }
+  if (j < r) {
+    float v = 0.0f;
+    if (k > 1) v = p.s[((int64_t)rho * p.gamma + k - 2) * r + j];
+    else if (p.s0 != nullptr) v = p.s0[(int64_t)rho * r + j];
+    sprev[j] = v;
+  }
+  __syncthreads();
+  if (j >= r) return;
+  const T *W = reinterpret_cast<const T *>(p.W_hh);
+  float ar = p.b_hh[j], az = p.b_hh[r + j], an = p.b_hh[2 * r + j];
+#pragma unroll 8
+  for (int i = 0; i < r; ++i) {
+    const float si = sprev[i];
+    const T *wi = W + (int64_t)i * g3;
+    ar = fmaf(Elem<T>::at(wi, j), si, ar);
+    az = fmaf(Elem<T>::at(wi, r + j), si, az);
+    an = fmaf(Elem<T>::at(wi, 2 * r + j), si, an);
+  }
+  const T *ge = reinterpret_cast<const T *>(p.G_E) + (int64_t)prev * g3;
+  const float *gh = p.G_h + ((int64_t)rho * p.gamma + k - 1) * g3;
+  const float gr = Elem<T>::at(ge, j) + gh[j];
+  const float gz = Elem<T>::at(ge, r + j) + gh[r + j];
+  const float gn = Elem<T>::at(ge, 2 * r + j) + gh[2 * r + j];
+  const float rg = 1.0f / (1.0f + expf(-(gr + ar)));
+  const float zg = 1.0f / (1.0f + expf(-(gz + az)));
+  const float n = tanhf(gn + rg * an);
+  const float sk = (1.0f - zg) * n + zg * sprev[j];
+  p.s[((int64_t)rho * p.gamma + k - 1) * r + j] = sk;
+  store_elem(reinterpret_cast<T *>(p.A), ((int64_t)(k - 1) * p.R + rho) * r + j, sk);
+}
+
 template <typename T, int KS>
 static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   const int n_tiles = (L.V + kTileN - 1) / kTileN;
@@ -267,6 +329,13 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   const bool wide = L.R > 4 * kRowsPerWave;
   const int n_items = (L.R + (wide ? 8 : 4) * kRowsPerWave - 1) / ((wide ? 8 : 4) * kRowsPerWave) * n_tiles;
   const int grid = stream_tile_grid(n_items, kComputeUnits);
+  GruParams gp{};
+  if (L.rnn != nullptr) {
+    const RnnHead &h = *L.rnn;
+    gp.R = L.R; gp.gamma = L.gamma; gp.V = L.V; gp.r = L.r; gp.G_E = h.G_E; gp.G_h = h.G_h;
+    gp.W_hh = h.W_hh; gp.b_hh = h.b_hh; gp.x0 = L.x0; gp.x = L.x; gp.s0 = h.s0; gp.s = h.s;
+    gp.A = h.A; gp.err = L.err;
+  }
   for (int k = 1; k <= L.gamma; ++k) {
     bp.k = k;
     bp.A = A[(k - 1) & 1];
@@ -275,6 +344,14 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     sp.A_cur = A[(k - 1) & 1];
     sp.a_tokens = k == 1 ? L.x0 : nullptr;
     sp.A_next = k < L.gamma ? A[k & 1] : nullptr;
+    if (L.rnn != nullptr) {
+      // the state update of step k gives the transition rows of step k
+      gp.k = k;
+      DSPARK_LAUNCH("gru_step", stream, gru_step_kernel<T><<<L.R, kBlock, 0, stream>>>(gp));
+      void *Ak = reinterpret_cast<T *>(L.rnn->A) + (int64_t)(k - 1) * L.R * L.r;
+      bp.A = Ak; bp.a_tokens = nullptr;
+      sp.A_cur = Ak; sp.a_tokens = nullptr; sp.A_next = nullptr;
+    }
     if (wide) {
       DSPARK_LAUNCH("bias_tile_draft", stream,
                     (stream_tile_kernel<T, Epi::kDraft, KS, 8, 1><<<grid, 8 * kWave, 0, stream>>>(bp)));

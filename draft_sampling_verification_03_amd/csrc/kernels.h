@@ -13,6 +13,17 @@ constexpr int kComputeUnits = 256;  // MI355X
 // bytes 0..3 of every workspace hold the sticky error word
 constexpr size_t kWsHeader = 256;
 
+// recurrent head: the transition row of step k is the GRU state s_k
+struct RnnHead {
+  const void *G_E;    // [V][3r] token input projection
+  const float *G_h;   // [R][gamma][3r] hidden-state input projection (input biases folded in)
+  const void *W_hh;   // [r][3r] column-major recurrent weights
+  const float *b_hh;  // [3r]
+  const float *s0;    // [R][r] or NULL
+  float *s;           // [R][gamma][r] states (fp32)
+  void *A;            // [gamma][R][r] states in the weights' element type
+};
+
 struct DraftLaunch {
   int R, gamma, V, r, d;
   bool bf16;
@@ -28,6 +39,7 @@ struct DraftLaunch {
   float *q_stats, *q_x, *c;
   const int32_t *x_force;  // [R][gamma] labels (teacher forcing) or NULL
   float *logq_x;           // [R][gamma] or NULL
+  const RnnHead *rnn;      // recurrent head instead of the W1 table, or NULL
   // workspace pieces
   int32_t *err;
   float2 *tile_stats;  // [R][n_tiles]
@@ -65,6 +77,7 @@ struct VerifyLaunch {
   float2 *pair_partials; // [R * gamma][n_tiles]
   int4 *row_map;         // [R * gamma]
   void *A_rows;          // [R * gamma][r] transition rows of the compact rows
+  const void *A_given;   // [gamma][R][r] given transition rows (recurrent head), or NULL
 };
 
 struct OverlapLaunch {

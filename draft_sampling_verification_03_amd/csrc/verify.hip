@@ -34,6 +34,7 @@ struct RowStatsParams {
   int r;
   const void *W1;
   void *A_rows;               // [R*gamma][r]: W1[x_{k-1}] of compact row i
+  const void *A_given;        // or, if set, row ((k-1) R + rho) of [gamma][R][r]
 };
 
 // One quarter of one row per workgroup, in rounds of kBatch 16-byte pieces per
@@ -120,8 +121,11 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
         if (tid < p.r * (int)sizeof(T) / 16)
           *reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.A_rows) + (int64_t)i * p.r +
                                      tid * kPerA) =
-              *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
-                                               (int64_t)prev * p.r + tid * kPerA);
+              *reinterpret_cast<const uint4 *>(
+                  (p.A_given != nullptr
+                       ? reinterpret_cast<const T *>(p.A_given) + ((int64_t)(k - 1) * p.R + lo) * p.r
+                       : reinterpret_cast<const T *>(p.W1) + (int64_t)prev * p.r) +
+                  tid * kPerA);
       } else if (tid == 0) {
         flag_error(p.err, kErrLength);
       }
@@ -208,6 +212,7 @@ struct FinalizeParams {
   float invT;
   const int32_t *ell, *row_offset;
   const void *P, *U, *W1, *W2;
+  const void *A_given;  // [gamma][R][r] transition rows, or NULL (W1[x_{k-1}])
   const int32_t *x0, *x;
   const float *q_stats, *q_x;
   uint64_t seed, round;
@@ -406,11 +411,13 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
 #pragma unroll
     for (int i = 0; i < kTpt; ++i) w[i] = pp[min(tid + i * kBlock, nT - 1)].y;
     const int prev = j == 1 ? min(max(x0, 0), V - 1) : s_x[j - 2];
-    const T *W1 = reinterpret_cast<const T *>(p.W1);
+    const T *arow_src = p.A_given != nullptr
+                            ? reinterpret_cast<const T *>(p.A_given) + ((int64_t)(j - 1) * p.R + rho) * p.r
+                            : reinterpret_cast<const T *>(p.W1) + (int64_t)prev * p.r;
     const int pieces = p.r * (int)sizeof(T) / 16;
     uint4 arow_piece = make_uint4(0, 0, 0, 0);
     if (tid < pieces)
-      arow_piece = *reinterpret_cast<const uint4 *>(W1 + (int64_t)prev * p.r + tid * (16 / sizeof(T)));
+      arow_piece = *reinterpret_cast<const uint4 *>(arow_src + tid * (16 / sizeof(T)));
     const int64_t qi = (int64_t)rho * gamma + j - 1;
     const float mq = p.q_stats[2 * qi], sq = p.q_stats[2 * qi + 1];
 #pragma unroll
@@ -510,7 +517,7 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   rs.row_offset = L.row_offset; rs.R = L.R; rs.chunks = L.p_chunks;
   rs.bonus_tiles = L.bonus_tiles; rs.err = L.err;
   rs.gamma = L.gamma; rs.x0 = L.x0; rs.x = L.x; rs.row_map = L.row_map;
-  rs.r = L.r; rs.W1 = L.W1; rs.A_rows = L.A_rows;
+  rs.r = L.r; rs.W1 = L.W1; rs.A_rows = L.A_rows; rs.A_given = L.A_given;
   DSPARK_LAUNCH("row_chunk_stats", stream,
                 row_chunk_stats_kernel<T><<<dim3(kChunks, L.rows_capacity), kBlock, 0, stream>>>(rs));
 
@@ -538,7 +545,7 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   }
 
   FinalizeParams fp{};
-  fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT;
+  fp.R = L.R; fp.gamma = L.gamma; fp.V = L.V; fp.r = L.r; fp.n_tiles = nT; fp.A_given = L.A_given;
   fp.rows_capacity = L.rows_capacity; fp.invT = L.invT; fp.ell = L.ell; fp.row_offset = L.row_offset;
   fp.P = L.P; fp.U = L.U; fp.W1 = L.W1; fp.W2 = L.W2; fp.x0 = L.x0; fp.x = L.x;
   fp.q_stats = L.q_stats; fp.q_x = L.q_x; fp.seed = L.seed; fp.round = L.round;

@@ -209,6 +209,54 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
                             int32_t *n_acc, int32_t *y, float *c_star,
                             void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* -------------------------------------------------------- recurrent head --
+ * The draft with the recurrent sequential head instead of the Markov table
+ * (Blog "RNN sequential head"; KB section 3): a running state replaces the
+ * previous-token lookup, z_k = (U_k + s_k W_o) / temp, with the gated update
+ * read as a GRU over the previous token's embedding and the position's
+ * backbone hidden state:
+ *   g   = G_E[x_{k-1}] + G_h[rho][k-1]          input pre-activations [3r]
+ *   a   = W_hh s_{k-1} + b_hh                    recurrent pre-activations [3r]
+ *   s_k = (1 - zg) tanh(g_n + rg a_n) + zg s_{k-1},
+ *         rg = sigmoid(g_r + a_r), zg = sigmoid(g_z + a_z)   (gate blocks r, z, n)
+ * with s_0 = s0[rho] (zeros if s0 is NULL) and x_0 = x0[rho].  s_k is kept in
+ * fp32; the product uses A_k = s_k rounded to dt (round to nearest even).
+ * Sampling, q_stats and q_x are those of dspark_draft (same streams and
+ * uniforms).  No confidence head here.
+ * Inputs
+ *   U [R][gamma][V] (dt); W_o column-major like W2 of dspark_draft (dt)
+ *   G_E [V][3r] (dt): the token embedding table times the input weights of the
+ *       update, computed once from the static weights
+ *   G_h [R][gamma][3r] fp32: the backbone hidden states times the hidden-state
+ *       input weights, plus the input biases (a product of the backbone's
+ *       outputs, made with the backbone)
+ *   W_hh [r][3r] column-major (dt): element (g, i) at W_hh[i * 3r + g]
+ *   b_hh [3r] fp32; x0 [R] int32; s0 [R][r] fp32 or NULL
+ * Outputs
+ *   x, q_stats, q_x as dspark_draft
+ *   s [R][gamma][r] fp32 states; A [gamma][R][r] (dt) the transition rows the
+ *   product used (row ((k-1) R + rho)): dspark_verify_rnn takes them
+ * Workspace: dspark_draft_workspace(R, gamma, V, r, dt) bytes. */
+dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                               const void *U, const void *W_o, const void *G_E, const float *G_h,
+                               const void *W_hh, const float *b_hh, const int32_t *x0,
+                               const float *s0, uint64_t seed, uint64_t round, int32_t *x,
+                               float *q_stats, float *q_x, float *s, void *A,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* dspark_verify for drafts of the recurrent head: the draft law of position k
+ * is recomputed from the given transition row A[(k-1) R + rho] (as written by
+ * dspark_draft_rnn) instead of W1[x_{k-1}]; W_o takes the place of W2.  All
+ * other arguments, outputs and the workspace are those of dspark_verify. */
+dspark_status dspark_verify_rnn(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                const int32_t *ell, const int32_t *row_offset, int rows_capacity,
+                                const void *P, const void *U, const void *A, const void *W_o,
+                                const int32_t *x0, const int32_t *x,
+                                const float *q_stats, const float *q_x,
+                                uint64_t seed, uint64_t round,
+                                int32_t *n_acc, int32_t *y, float *c_star,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ----------------------------------------------------------- train_losses --
  * Forward-only training reductions of the drafter on the ground-truth prefix
  * (Blog "Training objective"; KB section 5).  With the label prefix

@@ -135,10 +135,12 @@ def overlap(P_row, Q_row, temp=1.0, with_tv=False):
 
 # ----------------------------------------------------------------------- draft
 def draft_position(U_row, W1, W2, prev, u, temp=1.0, want_law=False):
-    """One Markov-head position.  W1 is [V][r]; W2 is column-major, i.e. the
-    array W2[v, i] holds element (i, v) of the r x V factor."""
-    V, r = W1.shape
+    """One Markov-head position.  W1 is [V][r] (any table of transition rows,
+    indexed by prev); W2 is column-major, i.e. the array W2[v, i] holds element
+    (i, v) of the r x V factor."""
     U_row = np.ascontiguousarray(U_row)
+    V, r = U_row.shape[-1], W1.shape[1]
+    assert W2.shape == (V, r) and 0 <= prev < W1.shape[0]
     dt = dtype_code(U_row)
     q = np.empty(V) if want_law else None
     cdf = np.empty(V) if want_law else None

@@ -347,3 +347,26 @@ def markov_sps(m: MarkovLoop) -> np.ndarray:
     if m.sps == "tiny":
         return 100.0 / (1.0 + B / 8.0)
     return 60.0 * 1024.0 / (1024.0 + B)
+
+
+# ------------------------------------------------------------ recurrent head
+_T_RGE, _T_RGH, _T_RWHH, _T_RBHH, _T_RS0, _T_RWO = range(200, 206)
+
+
+def rnn_head(cfg: Config):
+    """Random weights of a recurrent head of state size r (no trained weights
+    exist): the token input projection G_E [V][3r] ~ N(0, 0.5^2) (stored like
+    the weights), the hidden-state input projection G_h [R][gamma][3r] fp32
+    ~ N(0, 0.5^2), W_hh [r][3r] (column-major storage) ~ N(0, 1/r), b_hh [3r]
+    fp32 ~ N(0, 0.1^2), s0 [R][r] fp32 ~ N(0, 0.3^2), and the output factor
+    W_o (stored like W2) ~ N(0, 0.15^2)."""
+    r3 = 3 * cfg.r
+    GE = 0.5 * _rng(cfg, _T_RGE).standard_normal((cfg.V, r3), dtype=np.float32)
+    Gh = 0.5 * _rng(cfg, _T_RGH).standard_normal((cfg.R, cfg.gamma, r3), dtype=np.float32)
+    Whh = _rng(cfg, _T_RWHH).standard_normal((cfg.r, r3), dtype=np.float32) / np.float32(
+        np.sqrt(cfg.r))
+    bhh = 0.1 * _rng(cfg, _T_RBHH).standard_normal(r3, dtype=np.float32)
+    s0 = 0.3 * _rng(cfg, _T_RS0).standard_normal((cfg.R, cfg.r), dtype=np.float32)
+    Wo = 0.15 * _rng(cfg, _T_RWO).standard_normal((cfg.V, cfg.r), dtype=np.float32)
+    return (_store(cfg, GE), Gh.astype(np.float32), _store(cfg, Whh.astype(np.float32)),
+            bhh.astype(np.float32), s0.astype(np.float32), _store(cfg, Wo))

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ds.library()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in dspark.h but not exported"
 
@@ -133,6 +133,32 @@ def overlap_args(**over):
 ])
 def test_overlap_validation(over, expect):
     assert A.dspark_tv_overlap(**overlap_args(**over)) == expect
+
+
+def rnn_args(**over):
+    a = dict(R=4, gamma=4, V=1024, r=16, dt=A.DSPARK_F32, temp=1.0, U=P, W_o=P, G_E=P, G_h=P,
+             W_hh=P, b_hh=P, x0=P, s0=None, seed=0, round_=0, x=P, q_stats=P, q_x=P, s=P, A=P,
+             ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(G_E=None), NULL), (dict(G_h=None), NULL), (dict(W_hh=None), NULL), (dict(b_hh=None), NULL),
+    (dict(s=None), NULL), (dict(A=None), NULL), (dict(W_o=None), NULL), (dict(r=8), SHAPE),
+    (dict(gamma=65), SHAPE), (dict(temp=0.0), VALUE), (dict(dt=7), DTYPE), (dict(A=P + 4), ALIGN),
+    (dict(ws_bytes=64), WS),
+])
+def test_draft_rnn_validation(over, expect):
+    assert A.dspark_draft_rnn(**rnn_args(**over)) == expect
+
+
+def test_verify_rnn_validation():
+    base = dict(verify_args())
+    base.pop("W1"); base.pop("W2")
+    assert A.dspark_verify_rnn(**base, A=None, W_o=P) == NULL
+    assert A.dspark_verify_rnn(**base, A=P + 4, W_o=P) == ALIGN
+    assert A.dspark_verify_rnn(**dict(base, R=0), A=P, W_o=P) == SHAPE
 
 
 def train_args(**over):
