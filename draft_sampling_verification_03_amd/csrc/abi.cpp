@@ -101,7 +101,8 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, dspark_dtype dt, 
   if (!U || !W_o || !G_E || !G_h || !W_hh || !b_hh || !x0 || !x || !q_stats || !q_x || !s || !A ||
       !ws)
     return DSPARK_ERR_NULL;
-  if (!aligned16(U) || !aligned16(W_o) || !aligned16(A) || !aligned16(ws)) return DSPARK_ERR_ALIGN;
+  if (!aligned16(U) || !aligned16(W_o) || !aligned16(W_hh) || !aligned16(A) || !aligned16(ws))
+    return DSPARK_ERR_ALIGN;
   if (ws_bytes < draft_ws_bytes(R, gamma, V)) return DSPARK_ERR_WORKSPACE;
   size_t off = 0;
   DraftLaunch L{};

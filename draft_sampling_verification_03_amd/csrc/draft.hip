@@ -239,14 +239,19 @@ __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, in
 }
 
 // Recurrent head (Blog "RNN sequential head"; KB section 3), the gated update
-// read as a GRU: one workgroup per request, thread j < r owns state unit j and
-// its three gate rows.  W_hh is column-major ([r][3r]), so for each input i
-// the threads read one contiguous row segment; s_{k-1} sits in LDS.
+// read as a GRU:
 //   g = G_E[x_{k-1}] + G_h[rho][k-1];  a = W_hh s_{k-1} + b_hh
 //   s_k = (1 - sigmoid(g_z + a_z)) tanh(g_n + sigmoid(g_r + a_r) a_n)
 //         + sigmoid(g_z + a_z) s_{k-1}
-// s_k is kept in fp32; the product's transition row A_k = s_k in the
-// weights' element type.
+// a = W_hh s is a small product [R x r] x [r x 3r] over the column-major
+// weights (393 KB at r = 256 bf16, L2-resident).  A workgroup takes 4
+// requests x 64 state units (the three gate columns of each unit), so every
+// weight it loads serves 4 requests and the grid has R/4 x r/64 workgroups.
+// Thread (og, sp) owns 16 bytes of output columns og and a contiguous range
+// sp of the inputs: one coalesced 16-byte load per input row, up to 16 input
+// ranges so the dependent load chain stays short (the kernel is bound by load
+// latency); the ranges' partial sums meet in LDS in a fixed order.  s_k is
+// kept in fp32; the product's transition row A_k = s_k in the weights' type.
 struct GruParams {
   int R, gamma, V, r, k;
   const void *G_E;     // [V][3r]
@@ -260,42 +265,89 @@ struct GruParams {
   int32_t *err;
 };
 
+constexpr int kGruReq = 4, kGruUnits = 64, kGruSplits = 16, kGruBlock = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(kBlock) void gru_step_kernel(GruParams p) {
-  __shared__ float sprev[kMaxRank];
-  const int rho = blockIdx.x, j = threadIdx.x, r = p.r, g3 = 3 * r, k = p.k;
-  int prev = k == 1 ? p.x0[rho] : p.x[(int64_t)rho * p.gamma + k - 2];
-  if (prev < 0 || prev >= p.V) {
-    if (j == 0) flag_error(p.err, kErrToken);
-    prev = min(max(prev, 0), p.V - 1);
+__global__ __launch_bounds__(kGruBlock) void gru_step_kernel(GruParams p) {
+  constexpr int kPer = 16 / (int)sizeof(T);
+  __shared__ float sprev[kGruReq][kMaxRank];
+  __shared__ float apart[kGruSplits][kGruReq][3 * kGruUnits];
+  const int tid = threadIdx.x, r = p.r, g3 = 3 * r, k = p.k;
+  const int rho0 = blockIdx.x * kGruReq;
+  const int nu = min(r, kGruUnits), u0 = blockIdx.y * nu;
+  // the combining thread's input pre-activations g load first, so their
+  // latency (token, then embedding row) overlaps the product below
+  const int cq = tid / nu, cj = u0 + tid % nu, crho = rho0 + cq;
+  const bool combiner = tid < kGruReq * nu && crho < p.R && cj < r;
+  float gr = 0.0f, gz = 0.0f, gn = 0.0f;
+  if (combiner) {
+    int prev = k == 1 ? p.x0[crho] : p.x[(int64_t)crho * p.gamma + k - 2];
+    if (prev < 0 || prev >= p.V) {
+      if (cj == u0) flag_error(p.err, kErrToken);
+      prev = min(max(prev, 0), p.V - 1);
+    }
+    const T *ge = reinterpret_cast<const T *>(p.G_E) + (int64_t)prev * g3;
+    const float *gh = p.G_h + ((int64_t)crho * p.gamma + k - 1) * g3;
+    gr = Elem<T>::at(ge, cj) + gh[cj];
+    gz = Elem<T>::at(ge, r + cj) + gh[r + cj];
+    gn = Elem<T>::at(ge, 2 * r + cj) + gh[2 * r + cj];
   }
-  if (j < r) {
+  for (int idx = tid; idx < kGruReq * r; idx += kGruBlock) {
+    const int q = idx / r, i = idx % r, rho = rho0 + q;
     float v = 0.0f;
-    if (k > 1) v = p.s[((int64_t)rho * p.gamma + k - 2) * r + j];
-    else if (p.s0 != nullptr) v = p.s0[(int64_t)rho * r + j];
-    sprev[j] = v;
+    if (rho < p.R) {
+      if (k > 1) v = p.s[((int64_t)rho * p.gamma + k - 2) * r + i];
+      else if (p.s0 != nullptr) v = p.s0[(int64_t)rho * r + i];
+    }
+    sprev[q][i] = v;
   }
   __syncthreads();
-  if (j >= r) return;
-  const T *W = reinterpret_cast<const T *>(p.W_hh);
-  float ar = p.b_hh[j], az = p.b_hh[r + j], an = p.b_hh[2 * r + j];
-#pragma unroll 8
-  for (int i = 0; i < r; ++i) {
-    const float si = sprev[i];
-    const T *wi = W + (int64_t)i * g3;
-    ar = fmaf(Elem<T>::at(wi, j), si, ar);
-    az = fmaf(Elem<T>::at(wi, r + j), si, az);
-    an = fmaf(Elem<T>::at(wi, 2 * r + j), si, an);
+  const int ppg = nu / kPer;        // 16-byte pieces per gate
+  const int groups = 3 * ppg;
+  const int nsplit = min(kGruSplits, kGruBlock / groups);
+  const int per = (r + nsplit - 1) / nsplit;
+  if (tid < groups * nsplit) {
+    const int og = tid % groups, sp = tid / groups;
+    const int gate = og / ppg, pc = og % ppg;
+    const int unit = u0 + pc * kPer;  // a piece is wholly inside [0, r) or wholly outside
+    float acc[kGruReq][kPer];
+#pragma unroll
+    for (int q = 0; q < kGruReq; ++q)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[q][e] = 0.0f;
+    if (unit < r) {
+      const T *W = reinterpret_cast<const T *>(p.W_hh) + gate * r + unit;
+      const int i0 = sp * per, i1 = min(r, i0 + per);
+#pragma unroll 16
+      for (int i = i0; i < i1; ++i) {
+        float w[kPer];
+        Elem<T>::vec(W, (int64_t)i * g3, w);
+#pragma unroll
+        for (int q = 0; q < kGruReq; ++q) {
+          const float si = sprev[q][i];
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[q][e] = fmaf(w[e], si, acc[q][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGruReq; ++q)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) apart[sp][q][gate * nu + pc * kPer + e] = acc[q][e];
   }
-  const T *ge = reinterpret_cast<const T *>(p.G_E) + (int64_t)prev * g3;
-  const float *gh = p.G_h + ((int64_t)rho * p.gamma + k - 1) * g3;
-  const float gr = Elem<T>::at(ge, j) + gh[j];
-  const float gz = Elem<T>::at(ge, r + j) + gh[r + j];
-  const float gn = Elem<T>::at(ge, 2 * r + j) + gh[2 * r + j];
+  __syncthreads();
+  if (!combiner) return;
+  const int q = cq, jj = tid % nu, j = cj, rho = crho;
+  float ar = p.b_hh[j], az = p.b_hh[r + j], an = p.b_hh[2 * r + j];
+  for (int sp = 0; sp < nsplit; ++sp) {
+    ar += apart[sp][q][jj];
+    az += apart[sp][q][nu + jj];
+    an += apart[sp][q][2 * nu + jj];
+  }
   const float rg = 1.0f / (1.0f + expf(-(gr + ar)));
   const float zg = 1.0f / (1.0f + expf(-(gz + az)));
   const float n = tanhf(gn + rg * an);
-  const float sk = (1.0f - zg) * n + zg * sprev[j];
+  const float sk = (1.0f - zg) * n + zg * sprev[q][j];
   p.s[((int64_t)rho * p.gamma + k - 1) * r + j] = sk;
   store_elem(reinterpret_cast<T *>(p.A), ((int64_t)(k - 1) * p.R + rho) * r + j, sk);
 }
@@ -330,6 +382,8 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   const int n_items = (L.R + (wide ? 8 : 4) * kRowsPerWave - 1) / ((wide ? 8 : 4) * kRowsPerWave) * n_tiles;
   const int grid = stream_tile_grid(n_items, kComputeUnits);
   GruParams gp{};
+  const int gru_units = L.r < kGruUnits ? L.r : kGruUnits;
+  const dim3 gru_grid((L.R + kGruReq - 1) / kGruReq, (L.r + gru_units - 1) / gru_units);
   if (L.rnn != nullptr) {
     const RnnHead &h = *L.rnn;
     gp.R = L.R; gp.gamma = L.gamma; gp.V = L.V; gp.r = L.r; gp.G_E = h.G_E; gp.G_h = h.G_h;
@@ -347,7 +401,7 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     if (L.rnn != nullptr) {
       // the state update of step k gives the transition rows of step k
       gp.k = k;
-      DSPARK_LAUNCH("gru_step", stream, gru_step_kernel<T><<<L.R, kBlock, 0, stream>>>(gp));
+      DSPARK_LAUNCH("gru_step", stream, gru_step_kernel<T><<<gru_grid, kGruBlock, 0, stream>>>(gp));
       void *Ak = reinterpret_cast<T *>(L.rnn->A) + (int64_t)(k - 1) * L.R * L.r;
       bp.A = Ak; bp.a_tokens = nullptr;
       sp.A_cur = Ak; sp.a_tokens = nullptr; sp.A_next = nullptr;

@@ -230,7 +230,7 @@ dspark_status dspark_verify(int R, int gamma, int V, int r, dspark_dtype dt, flo
  *   G_h [R][gamma][3r] fp32: the backbone hidden states times the hidden-state
  *       input weights, plus the input biases (a product of the backbone's
  *       outputs, made with the backbone)
- *   W_hh [r][3r] column-major (dt): element (g, i) at W_hh[i * 3r + g]
+ *   W_hh [r][3r] column-major (dt, 16-byte aligned): element (g, i) at W_hh[i * 3r + g]
  *   b_hh [3r] fp32; x0 [R] int32; s0 [R][r] fp32 or NULL
  * Outputs
  *   x, q_stats, q_x as dspark_draft

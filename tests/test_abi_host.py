@@ -147,6 +147,7 @@ def rnn_args(**over):
     (dict(G_E=None), NULL), (dict(G_h=None), NULL), (dict(W_hh=None), NULL), (dict(b_hh=None), NULL),
     (dict(s=None), NULL), (dict(A=None), NULL), (dict(W_o=None), NULL), (dict(r=8), SHAPE),
     (dict(gamma=65), SHAPE), (dict(temp=0.0), VALUE), (dict(dt=7), DTYPE), (dict(A=P + 4), ALIGN),
+    (dict(W_hh=P + 8), ALIGN),
     (dict(ws_bytes=64), WS),
 ])
 def test_draft_rnn_validation(over, expect):
