@@ -249,7 +249,8 @@ __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, in
 // weight it loads serves 4 requests and the grid has R/4 x r/64 workgroups.
 // Thread (og, sp) owns 16 bytes of output columns og and a contiguous range
 // sp of the inputs: one coalesced 16-byte load per input row, up to 16 input
-// ranges so the dependent load chain stays short (the kernel is bound by load
+// ranges so the dependent load chain stays short, and each thread issues its
+// rows' loads 8 at a time before using any (the kernel is bound by load
 // latency); the ranges' partial sums meet in LDS in a fixed order.  s_k is
 // kept in fp32; the product's transition row A_k = s_k in the weights' type.
 struct GruParams {
@@ -265,7 +266,7 @@ struct GruParams {
   int32_t *err;
 };
 
-constexpr int kGruReq = 4, kGruUnits = 64, kGruSplits = 16, kGruBlock = 1024;
+constexpr int kGruReq = 4, kGruUnits = 64, kGruSplits = 16, kGruBlock = 512, kGruBatch = 8;
 
 template <typename T>
 __global__ __launch_bounds__(kGruBlock) void gru_step_kernel(GruParams p) {
@@ -315,18 +316,37 @@ __global__ __launch_bounds__(kGruBlock) void gru_step_kernel(GruParams p) {
     for (int q = 0; q < kGruReq; ++q)
 #pragma unroll
       for (int e = 0; e < kPer; ++e) acc[q][e] = 0.0f;
-    if (unit < r) {
+    const int i0 = sp * per, i1 = min(r, i0 + per);
+    if (unit < r && i0 < i1) {
       const T *W = reinterpret_cast<const T *>(p.W_hh) + gate * r + unit;
-      const int i0 = sp * per, i1 = min(r, i0 + per);
-#pragma unroll 16
-      for (int i = i0; i < i1; ++i) {
-        float w[kPer];
-        Elem<T>::vec(W, (int64_t)i * g3, w);
+      // batches of kGruBatch rows: all their loads issue before the first is
+      // used (rows past the range re-read the last one and count with weight 0)
+      for (int ib = i0; ib < i1; ib += kGruBatch) {
+        uint4 raw[kGruBatch];
 #pragma unroll
-        for (int q = 0; q < kGruReq; ++q) {
-          const float si = sprev[q][i];
+        for (int u = 0; u < kGruBatch; ++u)
+          raw[u] = *reinterpret_cast<const uint4 *>(W + (int64_t)min(ib + u, i1 - 1) * g3);
 #pragma unroll
-          for (int e = 0; e < kPer; ++e) acc[q][e] = fmaf(w[e], si, acc[q][e]);
+        for (int u = 0; u < kGruBatch; ++u) {
+          float w[kPer];
+          const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+          if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __uint_as_float(wd[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[2 * e] = __uint_as_float(wd[e] << 16);
+              w[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+            }
+          }
+          const bool in = ib + u < i1;
+#pragma unroll
+          for (int q = 0; q < kGruReq; ++q) {
+            const float si = in ? sprev[q][min(ib + u, i1 - 1)] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) acc[q][e] = fmaf(w[e], si, acc[q][e]);
+          }
         }
       }
     }
