@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=10,
                     help="requests in the CPU-oracle sample (0 disables)")
     ap.add_argument("--workers", type=int, default=16, help="host threads drawing the inputs")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the recurrent-head and training-reduction passes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters); not part of the timed steps")
@@ -239,6 +241,65 @@ def main():
     ds.dspark_trace_enable(False)
     kern_ov = ds.trace_summary()
 
+    # ---- secondary figures of the next rows on the same workload, separate passes:
+    #      a round with the recurrent head (scheduler off, every position verified:
+    #      compare with the scheduler-off round above) and the forward-only
+    #      training reductions on label prefixes (teacher-forced draft + c*)
+    next_rows = None
+    if not args.no_next_rows:
+        GE, Gh, Whh, bhh, s0, Wo = synth.rnn_head(cfg)
+        dGE, dGh, dWhh, dbhh, ds0, dWo = up(GE), up(Gh), up(Whh), up(bhh), up(s0), up(Wo)
+        wsr, wsrv, wst = ds.Workspace(), ds.Workspace(), ds.Workspace()
+        y_lab = up(np.random.default_rng(11).integers(0, V, (R, gamma)).astype(np.int32))
+        c_lab = up(np.random.default_rng(12).uniform(0.05, 0.95, (R, gamma)).astype(np.float32))
+        keep = {}
+
+        def rnn_round():
+            d = ds.draft_rnn(dU, dWo, dGE, dGh, dWhh, dbhh, dx0, s0=ds0, temp=cfg.temp,
+                             seed=cfg.seed, round=cfg.round, ws=wsr, stream=stream,
+                             out=keep.get("d"))
+            keep["d"] = d
+            keep["v"] = ds.verify_rnn(sout_off["ell"], sout_off["row_offset"], dT, dU, d["A"], dWo,
+                                      dx0, d["x"], d["q_stats"], d["q_x"], temp=cfg.temp,
+                                      seed=cfg.seed, round=cfg.round, ws=wsrv, stream=stream,
+                                      out=keep.get("v"))
+
+        def train():
+            keep["t"] = ds.train_losses(dU, dW1, dW2, dT, dx0, y_lab, c_lab, temp=cfg.temp,
+                                        ws=wst, stream=stream, out=keep.get("t"))
+
+        def timed(fn, n):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        n_next = max(1, args.steps // 2)
+        ms_rnn, ms_train = timed(rnn_round, n_next), timed(train, n_next)
+        assert wsr.error_code() == 0 and wsrv.error_code() == 0 and wst.error_code() == 0, \
+            "device error word set in a next-row pass"
+        ds.dspark_trace_enable(True)
+        rnn_round()
+        torch.cuda.synchronize()
+        ds.dspark_trace_enable(False)
+        kr = ds.trace_summary()
+        gru_ms, gru_n = kr.get("gru_step", (float("nan"), 1))
+        next_rows = {
+            "rnn_head": {"ms_per_round": round(ms_rnn, 4),
+                         "positions_per_s": round(R * gamma / (ms_rnn / 1e3), 1),
+                         "verify_rows": rows_off, "gru_step_us": round(gru_ms / gru_n * 1e3, 3),
+                         "markov_same_rows_ms": round(ms_off, 4)},
+            "train_losses": {"ms_per_call": round(ms_train, 4),
+                             "positions_per_s": round(R * gamma / (ms_train / 1e3), 1)},
+        }
+        print(f"[bench] next rows: recurrent-head round {ms_rnn:.3f} ms, "
+              f"training reductions {ms_train:.3f} ms", file=sys.stderr, flush=True)
+
     # ---- algorithmic work per launch of each kernel
     rows_used = R + sum_ell
     n_ov = Pp.shape[0]
@@ -347,6 +408,7 @@ def main():
                          "verify": round(t_ver, 4)},
         "roofline": roof,
         "kernels": kernels,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
