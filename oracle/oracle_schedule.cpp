@@ -28,13 +28,16 @@ struct Candidate {
 };
 
 // Survival products in binary32, left to right: a_j = fl32(a_{j-1} * c_j).
+// A confidence is a probability: -0.0 is the value 0 and is read as +0.0, so
+// every survival product is a non-negative number with a non-negative sign.
 bool survival(int R, int gamma, const float *c, std::vector<float> &a) {
   a.assign((size_t)R * gamma, 0.0f);
   for (int rho = 0; rho < R; ++rho) {
     float run = 1.0f;
     for (int j = 1; j <= gamma; ++j) {
-      const float cj = c[(size_t)rho * gamma + (j - 1)];
+      float cj = c[(size_t)rho * gamma + (j - 1)];
       if (!(cj >= 0.0f && cj <= 1.0f)) return false;  // also rejects NaN
+      if (cj == 0.0f) cj = 0.0f;                        // -0.0 -> +0.0
       run = run * cj;
       a[(size_t)rho * gamma + (j - 1)] = run;
     }

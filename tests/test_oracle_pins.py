@@ -426,6 +426,90 @@ def test_schedule_rejects_bad_confidence():
         oracle.schedule(c, np.ones(8), oracle.SCHED_EARLY_STOP)
 
 
+# ------------------------------------------- scheduler tie rules (readings)
+# KB section 4 stops the non-anticipating scheduler the first time theta does
+# not increase, so a plateau ends admission; Bangkok 4.2.2's "stops once it
+# drops" would admit through it.  The pins below take the first reading, and
+# the full search returns the smallest maximiser (no extra verify slot for the
+# same expected throughput).  Each case has an exact fp64 tie.
+def test_select_n_tie_rules_on_theta_paths():
+    # a plateau, then a rise: early stop halts at the plateau, full search
+    # finds the later maximum
+    assert oracle.select_n([4.0, 6.0, 6.0, 8.0], oracle.SCHED_EARLY_STOP) == 1
+    assert oracle.select_n([4.0, 6.0, 6.0, 8.0], oracle.SCHED_FULL_SEARCH) == 3
+    # equal maxima apart: the smaller admission count wins
+    assert oracle.select_n([1.0, 2.0, 1.5, 2.0], oracle.SCHED_FULL_SEARCH) == 1
+    assert oracle.select_n([1.0, 2.0, 1.5, 2.0], oracle.SCHED_EARLY_STOP) == 1
+    # a flat start admits nothing under either rule
+    assert oracle.select_n([3.0, 3.0, 5.0], oracle.SCHED_EARLY_STOP) == 0
+    assert oracle.select_n([3.0, 3.0, 2.0], oracle.SCHED_FULL_SEARCH) == 0
+
+
+def test_schedule_zero_confidence_plateau():
+    """Zero-confidence candidates add nothing to tau; under a flat SPS they
+    leave theta unchanged, so neither rule admits them."""
+    c = np.array([[1.0, 1.0], [0.0, 0.0]], dtype=np.float32)
+    sps = np.ones(2 * 3 + 1)
+    for mode in (oracle.SCHED_EARLY_STOP, oracle.SCHED_FULL_SEARCH):
+        out = oracle.schedule(c, sps, mode)
+        assert out["n_admitted"] == 2 and list(out["ell"]) == [2, 0]
+        assert out["theta"] == 4.0
+    best, ell_b = oracle.schedule_bruteforce(c, sps)
+    assert best == 4.0 and list(ell_b) == [2, 0]
+
+
+def test_schedule_plateau_before_a_rise():
+    """One request, c = 1 everywhere (tau_n = 1 + n), SPS chosen so that
+    theta = 4, 6, 6, 8: early stop admits 1, full search 3."""
+    c = np.ones((1, 3), dtype=np.float32)
+    sps = np.array([0.0, 4.0, 3.0, 2.0, 2.0])
+    assert oracle.schedule(c, sps, oracle.SCHED_EARLY_STOP)["n_admitted"] == 1
+    full = oracle.schedule(c, sps, oracle.SCHED_FULL_SEARCH)
+    assert full["n_admitted"] == 3 and full["theta"] == 8.0
+
+
+def test_schedule_full_search_two_equal_maxima():
+    """theta = 1, 2, 1.5, 2: the smallest maximiser (1) and the brute force
+    over allocations, whose own tie rule prefers fewer admitted drafts, agree."""
+    c = np.ones((1, 3), dtype=np.float32)
+    sps = np.array([0.0, 1.0, 1.0, 0.5, 0.5])
+    full = oracle.schedule(c, sps, oracle.SCHED_FULL_SEARCH)
+    assert full["n_admitted"] == 1 and full["theta"] == 2.0
+    best, ell_b = oracle.schedule_bruteforce(c, sps)
+    assert best == 2.0 and list(ell_b) == [1]
+    asy = oracle.schedule(c, sps, oracle.SCHED_ASYNC_TOPK, c_prev2=c)
+    assert asy["n_admitted"] == 1
+
+
+def test_threshold_keeps_a_confidence_equal_to_the_cutoff():
+    """Only drafts below the cutoff are dropped (Bangkok 5.3): c equal to it is kept."""
+    c = np.array([[0.5, 0.5, 0.25], [0.25, 0.5, 0.5]], dtype=np.float32)
+    out = oracle.schedule(c, None, oracle.SCHED_THRESHOLD, threshold=0.5)
+    assert list(out["ell"]) == [2, 0]
+
+
+def test_negative_zero_confidence_is_zero():
+    """-0.0 is the probability 0: every output equals that of +0.0 bit for bit,
+    and the survival products carry no negative sign."""
+    rng = np.random.default_rng(17)
+    c = rng.uniform(0.2, 1.0, (6, 4)).astype(np.float32)
+    c[1, 0] = c[3, 2] = c[4, 3] = 0.0
+    cn = c.copy()
+    cn[1, 0] = cn[3, 2] = cn[4, 3] = np.float32(-0.0)
+    sps = np.ones(6 * 5 + 1)
+    sps[6 + 20:] = 0.5
+    for mode in (oracle.SCHED_OFF, oracle.SCHED_EARLY_STOP, oracle.SCHED_FULL_SEARCH,
+                 oracle.SCHED_ASYNC_TOPK, oracle.SCHED_THRESHOLD):
+        kw = dict(c_prev2=cn) if mode == oracle.SCHED_ASYNC_TOPK else {}
+        o_pos = oracle.schedule(c, sps, mode, threshold=0.3, **({"c_prev2": c} if kw else {}))
+        o_neg = oracle.schedule(cn, sps, mode, threshold=0.3, **kw)
+        for key in ("ell", "row_offset"):
+            assert np.array_equal(o_pos[key], o_neg[key])
+        assert o_pos["n_admitted"] == o_neg["n_admitted"] and o_pos["theta"] == o_neg["theta"]
+        assert np.array_equal(o_pos["a"].view(np.uint32), o_neg["a"].view(np.uint32))
+        assert not np.signbit(o_neg["a"]).any()
+
+
 # ---------------------------------------- sequential temperature scaling (STS)
 def test_sts_head_divides_the_logit():
     """c = sigmoid(z / T): against the T = 1 head of the same inputs."""
