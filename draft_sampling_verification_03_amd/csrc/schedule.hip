@@ -6,7 +6,8 @@
 //     left to right (binary32, as the products that rank the candidates)
 //  2. candidate keys ((0xFFFFFFFF - bits(a)) << 32) | (j << 20) | rho: ascending
 //     key order is a descending, then depth ascending, then request ascending;
-//     a >= 0 so its bit pattern orders like its value.  Bitonic sort with the
+//     a >= +0 (a -0.0 confidence is read as +0.0) so its bit pattern orders
+//     like its value.  Bitonic sort with the
 //     keys in registers (E per thread, blocked): strides inside a thread swap
 //     registers, strides inside a wave use lane shuffles, and only strides
 //     across waves exchange through LDS (two barriers each).
@@ -158,6 +159,7 @@ __device__ __forceinline__ int64_t survival(int R, int gamma, int gs, bool keys,
         bad = true;
         c = 0.0f;
       }
+      c = c == 0.0f ? 0.0f : c;  // -0.0 is the probability 0: no sign in any product
       run = run * c;
       row[j - 1] = run;
       wsum += fixed_weight(run);
@@ -413,6 +415,7 @@ __device__ __forceinline__ int64_t threshold_survival(int R, int gamma, int gs, 
         bad = true;
         c = 0.0f;
       }
+      c = c == 0.0f ? 0.0f : c;  // -0.0 -> +0.0, as in the ranked modes
       run = run * c;
       row[j - 1] = run;
       kept = kept && c >= thr;

@@ -202,3 +202,102 @@ def test_product_package_does_not_reference_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liboracle" not in text, f
+
+
+# ------------------------------------------------ torch wrappers: argument checks
+# The wrappers check element type, shape, contiguity and device before any
+# library call; every case below fails those checks, so nothing is launched
+# (these run on a host without a GPU, with CPU tensors).
+import torch  # noqa: E402
+
+
+def _draft_tensors(R=4, gamma=3, V=64, r=16, dtype=torch.float32):
+    return dict(U=torch.zeros(R, gamma, V, dtype=dtype), W1=torch.zeros(V, r, dtype=dtype),
+                W2=torch.zeros(V, r, dtype=dtype), x0=torch.zeros(R, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("change,exc", [
+    (dict(x0=torch.zeros(4, dtype=torch.int64)), TypeError),        # int64 tokens
+    (dict(W1=torch.zeros(64, 16, dtype=torch.bfloat16)), TypeError),  # weight dtype != U's
+    (dict(W2=torch.zeros(64, 8)), ValueError),                      # rank mismatch
+    (dict(x0=torch.zeros(5, dtype=torch.int32)), ValueError),       # R mismatch
+    (dict(U=torch.zeros(4, 64, 3).transpose(1, 2)), ValueError),    # strided view
+    (dict(U=torch.zeros(4, 3, 64, dtype=torch.float16)), TypeError),
+    ({}, ValueError),                                               # host tensors
+])
+def test_draft_wrapper_rejects_bad_tensors(change, exc):
+    t = _draft_tensors()
+    t.update(change)
+    with pytest.raises(exc):
+        ds.draft(t["U"], t["W1"], t["W2"], t["x0"])
+
+
+def test_draft_wrapper_checks_head_inputs():
+    t = _draft_tensors()
+    h = torch.zeros(4, 3, 32)
+    with pytest.raises(ValueError):   # w_conf missing
+        ds.draft(t["U"], t["W1"], t["W2"], t["x0"], h=h)
+    with pytest.raises(ValueError):   # w_conf of the wrong length (d + r = 48)
+        ds.draft(t["U"], t["W1"], t["W2"], t["x0"], h=h, w_conf=torch.zeros(40))
+    with pytest.raises(TypeError):    # h in another dtype than U
+        ds.draft(t["U"], t["W1"], t["W2"], t["x0"], h=h.bfloat16(), w_conf=torch.zeros(48))
+
+
+def test_schedule_wrapper_rejects_bad_tensors():
+    c = torch.full((4, 3), 0.5)
+    sps = torch.ones(4 * 4 + 1, dtype=torch.float64)
+    with pytest.raises(TypeError):
+        ds.schedule(c.double(), sps, 1)
+    with pytest.raises(TypeError):
+        ds.schedule(c, sps.float(), 1)
+    with pytest.raises(ValueError):
+        ds.schedule(c.t(), sps, 1)                    # [3][4] view, not contiguous
+    with pytest.raises(ValueError):
+        ds.schedule(c, sps, 3)                        # ASYNC_TOPK without c_prev2
+    with pytest.raises(ValueError):
+        ds.schedule(c, sps, 1)                        # host tensors
+
+
+def test_verify_wrapper_rejects_bad_tensors():
+    R, gamma, V, r = 4, 3, 64, 16
+    t = _draft_tensors(R, gamma, V, r)
+    ell = torch.zeros(R, dtype=torch.int32)
+    ro = torch.arange(R + 1, dtype=torch.int32)
+    P = torch.zeros(R, V)
+    x = torch.zeros(R, gamma, dtype=torch.int32)
+    qs, qx = torch.ones(R, gamma, 2), torch.ones(R, gamma)
+    args = [ell, ro, P, t["U"], t["W1"], t["W2"], t["x0"], x, qs, qx]
+    for i, bad, exc in [(0, ell.long(), TypeError), (1, ro[:R], ValueError),
+                        (2, torch.zeros(R, V + 8), ValueError), (7, x[:, :2], ValueError),
+                        (8, qs.double(), TypeError), (2, P.bfloat16(), TypeError)]:
+        a = list(args)
+        a[i] = bad
+        with pytest.raises(exc):
+            ds.verify(*a)
+    with pytest.raises(ValueError):
+        ds.verify(*args, rows_capacity=R + 1)         # more rows than P holds
+    with pytest.raises(ValueError):
+        ds.verify(*args)                              # host tensors
+
+
+def test_other_wrappers_reject_bad_tensors():
+    P, Q = torch.zeros(5, 64), torch.zeros(5, 64)
+    with pytest.raises(ValueError):
+        ds.tv_overlap(P, Q, p_stats=torch.ones(5, 2))  # one statistic without the other
+    with pytest.raises(TypeError):
+        ds.tv_overlap(P, Q.bfloat16())
+    R, gamma, V, r = 2, 3, 64, 16
+    t = _draft_tensors(R, gamma, V, r)
+    y = torch.zeros(R, gamma, dtype=torch.int32)
+    with pytest.raises(ValueError):                    # P with gamma rows per request, not gamma + 1
+        ds.train_losses(t["U"], t["W1"], t["W2"], torch.zeros(R * gamma, V), t["x0"], y,
+                        torch.ones(R, gamma))
+    with pytest.raises(TypeError):
+        ds.train_losses(t["U"], t["W1"], t["W2"], torch.zeros(R * (gamma + 1), V), t["x0"],
+                        y.long(), torch.ones(R, gamma))
+    with pytest.raises(TypeError):                     # G_h must be fp32
+        ds.draft_rnn(t["U"], t["W1"], torch.zeros(V, 3 * r), torch.zeros(R, gamma, 3 * r,
+                     dtype=torch.float64), torch.zeros(r, 3 * r), torch.zeros(3 * r), t["x0"])
+    with pytest.raises(ValueError):                    # host tensors
+        ds.draft_rnn(t["U"], t["W1"], torch.zeros(V, 3 * r), torch.zeros(R, gamma, 3 * r),
+                     torch.zeros(r, 3 * r), torch.zeros(3 * r), t["x0"])

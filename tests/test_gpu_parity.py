@@ -270,3 +270,52 @@ def test_threshold_schedule_matches_oracle(R, gamma):
             assert np.array_equal(g["a"].cpu().numpy(), o["a"])
             th = float(g["theta"].cpu().numpy()[0])
             assert (np.isnan(th) and np.isnan(o["theta"])) or th == o["theta"]
+
+
+def _schedule_against_oracle(c, sps, mode, c_prev2=None, threshold=0.0):
+    o = oracle.schedule(c, sps, mode, c_prev2=c_prev2, threshold=threshold)
+    ws = ds.Workspace()
+    g = ds.schedule(dev(c), dev(sps), mode, c_prev2=dev(c_prev2) if c_prev2 is not None else None,
+                    threshold=float(threshold), ws=ws)
+    assert ws.error_code() == 0
+    assert np.array_equal(g["ell"].cpu().numpy(), o["ell"])
+    assert np.array_equal(g["row_offset"].cpu().numpy(), o["row_offset"])
+    assert int(g["n_admitted"].cpu().numpy()[0]) == o["n_admitted"]
+    assert np.array_equal(g["a"].cpu().numpy().view(np.uint32), o["a"].view(np.uint32))
+    th = float(g["theta"].cpu().numpy()[0])
+    assert (np.isnan(th) and np.isnan(o["theta"])) or th == o["theta"]
+    return o
+
+
+@pytest.mark.parametrize("case", ["plateau", "rise_after_plateau", "equal_maxima"])
+def test_schedule_tie_rules_match_oracle(case):
+    """Exact theta ties: early stop halts at the first non-increase, the full
+    search takes the smallest maximiser (the oracle's pinned readings)."""
+    if case == "plateau":
+        c = np.array([[1.0, 1.0], [0.0, 0.0]], dtype=np.float32)
+        sps, expect = np.ones(7), {1: 2, 2: 2}
+    elif case == "rise_after_plateau":
+        c = np.ones((1, 3), dtype=np.float32)
+        sps, expect = np.array([0.0, 4.0, 3.0, 2.0, 2.0]), {1: 1, 2: 3}
+    else:
+        c = np.ones((1, 3), dtype=np.float32)
+        sps, expect = np.array([0.0, 1.0, 1.0, 0.5, 0.5]), {1: 1, 2: 1}
+    for mode, n in expect.items():
+        assert _schedule_against_oracle(c, sps, mode)["n_admitted"] == n
+    _schedule_against_oracle(c, sps, 3, c_prev2=c)
+
+
+@pytest.mark.parametrize("R,gamma", [(128, 16), (512, 15)])
+def test_schedule_zero_and_negative_zero_confidences(R, gamma):
+    """Many zero-weight candidates (theta plateaus under a stepped SPS) and
+    -0.0 confidences, which rank exactly like +0.0: bit-exact against the oracle."""
+    rng = np.random.default_rng(R)
+    c = (1.0 / (1.0 + np.exp(-(2.0 + 1.5 * rng.standard_normal((R, gamma)))))).astype(np.float32)
+    zero = rng.random((R, gamma)) < 0.3
+    c[zero] = np.where(rng.random(int(zero.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+    B = np.arange(R * (gamma + 1) + 1, dtype=np.float64)
+    for sps in (60.0 * 1024.0 / (1024.0 + 64.0 * np.ceil(B / 64.0)), np.full(B.size, 3.0)):
+        for mode in (1, 2):
+            _schedule_against_oracle(c, sps, mode)
+        _schedule_against_oracle(c, sps, 3, c_prev2=c[::-1].copy())
+        _schedule_against_oracle(c, sps, ds.DSPARK_SCHED_THRESHOLD, threshold=0.0)
