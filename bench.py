@@ -4,40 +4,56 @@
 One step = one round of the whole path on resident synthetic inputs:
 dspark_draft (gamma Markov-head steps) -> dspark_schedule -> dspark_verify over
 the flattened sum(1 + ell) target rows.  The target forward itself is outside
-the path: its logits for the scheduled rows are laid out once, before timing
-(the schedule is a deterministic function of the inputs, so every step
-admits the same rows; the bench checks that after timing).
+the path: its logits for the scheduled rows are laid out before the round is
+timed (the schedule is a deterministic function of the inputs and the round
+counter; where it depends on the drafted tokens, i.e. with a confidence head,
+each round's layout comes from an untimed run of that round's draft and
+schedule, and the timed round is checked to admit the same rows).
 
-Prints ONE JSON line: draft+verify positions/s (R * gamma per step), the
-per-kernel rooflines (average launch durations measured with HIP events on
-the launch stream), the achieved HBM bandwidth of the round, and the CPU
-oracle's rate on a bounded sample of the same workload.
+Timing protocol: W warm-up rounds, then K timed rounds, each bracketed by its
+own pair of HIP events on the launch stream, with the Philox round counter
+varied from round to round.  Between rounds, outside the events, a scratch
+buffer larger than the 256 MB Infinity Cache is read and written, so every
+round starts with cold caches (the primary figure: median, p10, p90); the
+same rounds back to back without the flush give the warm figure.
+
+Prints ONE JSON line: draft+verify positions/s (R * gamma per round over the
+cold median), per-kernel rooflines from kernel-execution events, the round's
+fraction of its HBM floor, and the CPU oracle's rate on a bounded sample of
+the same workload.
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "draft+verify positions/sec at V=151936,R=128,γ=16; achieved HBM GB/s"
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix cores
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix cores
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50, help="timed rounds (median/p10/p90 over them)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload id (3 = R=128, gamma=16)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload id: 2 = R32 gamma7, 3 = R128 gamma16 (headline), "
+                         "4 = R256 gamma5 ragged, 5 = R512 gamma15 with the confidence head")
     ap.add_argument("--cpu-requests", type=int, default=10,
                     help="requests in the CPU-oracle sample (0 disables)")
     ap.add_argument("--workers", type=int, default=16, help="host threads drawing the inputs")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="scratch read+written between timed rounds (0: no flush)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="only the headline rounds and the per-kernel pass (for profiler runs)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the recurrent-head and training-reduction passes")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -59,6 +75,28 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def host_cpu():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -67,6 +105,8 @@ def main():
               "the hot path has no collective and this build runs on a single MI355X",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
 
     import numpy as np
     import torch
@@ -99,6 +139,8 @@ def main():
     dsps = up(sps) if sps is not None else None
     dh = up(h) if h is not None else None
     dw = up(w_conf) if w_conf is not None else None
+    flush_buf = (torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+                 if args.flush_mib > 0 else None)
     torch.cuda.synchronize()
     print(f"[bench] inputs for {cfg.name} ready in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
@@ -114,177 +156,268 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def draft():
-        return ds.draft(dU, dW1, dW2, dx0, temp=cfg.temp, seed=cfg.seed, round=cfg.round, h=dh,
-                        w_conf=dw, b_conf=0.0 if b_conf is None else float(b_conf), ws=wsd,
-                        stream=stream, out=dout)
+    def flush():
+        if flush_buf is not None:
+            flush_buf.add_(1)  # every byte read and written: evicts L2 and the Infinity Cache
 
-    dout = None
-    dout = draft()
-    c_in = dout["c"] if dh is not None else dc
-    sout = ds.schedule(c_in, dsps, cfg.mode, c_prev2=dcp, R=R, gamma=gamma, ws=wss, stream=stream)
-    torch.cuda.synchronize()
-    ell = sout["ell"].cpu().numpy().copy()
-    sum_ell = int(ell.sum())
-    idx = np.concatenate([rho * (gamma + 1) + np.arange(int(ell[rho]) + 1) for rho in range(R)])
-    P = torch.zeros((cfg.rows_capacity, V), dtype=dT.dtype, device=dev)
-    P[: idx.size] = dT.index_select(0, torch.from_numpy(idx).to(dev))
-    vout = None
+    keep = {}
+
+    def draft(rnd):
+        keep["d"] = ds.draft(dU, dW1, dW2, dx0, temp=cfg.temp, seed=cfg.seed, round=rnd, h=dh,
+                             w_conf=dw, b_conf=0.0 if b_conf is None else float(b_conf), ws=wsd,
+                             stream=stream, out=keep.get("d"))
+        return keep["d"]
+
+    def conf_in():
+        return keep["d"]["c"] if dh is not None else dc
 
     def schedule():
-        return ds.schedule(c_in, dsps, cfg.mode, c_prev2=dcp, R=R, gamma=gamma, ws=wss,
-                           stream=stream, out=sout)
+        keep["s"] = ds.schedule(conf_in(), dsps, cfg.mode, c_prev2=dcp, R=R, gamma=gamma, ws=wss,
+                                stream=stream, out=keep.get("s"))
+        return keep["s"]
 
-    def verify():
-        return ds.verify(sout["ell"], sout["row_offset"], P, dU, dW1, dW2, dx0, dout["x"],
-                         dout["q_stats"], dout["q_x"], temp=cfg.temp, seed=cfg.seed,
-                         round=cfg.round, ws=wsv, stream=stream, out=vout)
+    P = torch.zeros((cfg.rows_capacity, V), dtype=dT.dtype, device=dev)
 
-    vout = verify()
+    def layout(ell):
+        """The target forward's output for the scheduled rows (outside the path):
+        P[row_offset[rho] + k - 1] = target row (rho, k), k = 1..ell + 1."""
+        idx = np.concatenate([rho * (gamma + 1) + np.arange(int(ell[rho]) + 1) for rho in range(R)])
+        P[: idx.size] = dT.index_select(0, torch.from_numpy(idx).to(dev))
+        return int(ell.sum())
 
-    def step():
-        draft()
+    def verify(rnd):
+        s, d = keep["s"], keep["d"]
+        keep["v"] = ds.verify(s["ell"], s["row_offset"], P, dU, dW1, dW2, dx0, d["x"],
+                              d["q_stats"], d["q_x"], temp=cfg.temp, seed=cfg.seed, round=rnd,
+                              ws=wsv, stream=stream, out=keep.get("v"))
+
+    # A confidence head makes the schedule depend on the drafted tokens, hence
+    # on the round counter: such rounds get their target rows laid out from an
+    # untimed run of the same round's draft and schedule.
+    round_dependent = dh is not None
+    laid = {}
+
+    def prepare(rnd):
+        if not round_dependent and laid:
+            return laid["ell"]
+        draft(rnd)
         schedule()
-        verify()
+        torch.cuda.synchronize()
+        ell = keep["s"]["ell"].cpu().numpy().copy()
+        if not (laid and np.array_equal(laid["ell"], ell)):
+            layout(ell)
+        laid["ell"] = ell
+        return ell
 
-    for _ in range(args.warmup):
-        step()
+    def one_round(rnd):
+        draft(rnd)
+        schedule()
+        verify(rnd)
+
+    base = cfg.round
+    for i in range(args.warmup):
+        prepare(base + i)
+        one_round(base + i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps back to back, one event pair around
-    #      them (an event between entry points costs the stream several us)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly K rounds, cold caches, round counter varied
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    ell_seen = torch.empty((K, R), dtype=torch.int32, device=dev)
+    ell_want = []
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    e0.record(stream)
-    for k in range(args.steps):
-        step()
-    e1.record(stream)
+    for i in range(K):
+        rnd = base + args.warmup + i
+        ell_want.append(prepare(rnd))
+        flush()
+        ev[i][0].record(stream)
+        one_round(rnd)
+        ev[i][1].record(stream)
+        ell_seen[i].copy_(keep["s"]["ell"])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    ms_step = max(ms_step, 1e3 * wall / args.steps)
-
-    # ---- per-entry-point breakdown (separate pass, events around each call)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        draft()
-        ev[k][1].record(stream)
-        schedule()
-        ev[k][2].record(stream)
-        verify()
-        ev[k][3].record(stream)
-    torch.cuda.synchronize()
-    t_draft = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_sched = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    t_ver = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    assert np.array_equal(sout["ell"].cpu().numpy(), ell), "schedule changed during timing"
+    cold = [a.elapsed_time(b) for a, b in ev]
+    assert np.array_equal(ell_seen.cpu().numpy(), np.stack(ell_want)), \
+        "a timed round admitted other rows than its layout"
     errs = (wsd.error_code(), wss.error_code(), wsv.error_code())
     assert errs == (0, 0, 0), f"device error words {errs}"
+    ms_step = float(np.median(cold))
+    sum_ell_rounds = [int(e.sum()) for e in ell_want]
+    sum_ell = int(np.median(sum_ell_rounds))
+    rows_used = R + sum_ell
 
-    # ---- the same workload with the scheduler off (ell = gamma for every request:
-    #      R * (1 + gamma) target rows, the flattened layout of all positions),
-    #      a figure that does not depend on the schedule; separate timed pass
-    wss_off, wsv_off = ds.Workspace(), ds.Workspace()
-    sout_off = ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off,
-                           stream=stream)
-    vout_off = None
+    def timed_rounds(n, fn, flush_between):
+        """Per-round event times of n rounds (round counters continue after the
+        timed region)."""
+        out = []
+        for i in range(n):
+            rnd = base + args.warmup + K + i
+            prepare(rnd)
+            if flush_between:
+                flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(rnd)
+            b.record(stream)
+            out.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in out]
 
-    def step_off():
-        nonlocal vout_off
-        draft()
-        ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off, stream=stream,
-                    out=sout_off)
-        vout_off = ds.verify(sout_off["ell"], sout_off["row_offset"], dT, dU, dW1, dW2, dx0,
-                             dout["x"], dout["q_stats"], dout["q_x"], temp=cfg.temp,
-                             seed=cfg.seed, round=cfg.round, ws=wsv_off, stream=stream,
-                             out=vout_off)
+    # the percentiles cover at least 50 cold rounds: the K timed rounds, plus
+    # more of the same protocol after them when K < 50
+    cold_all = list(cold)
+    if K < 50:
+        cold_all += timed_rounds(50 - K, one_round, True)
 
-    step_off()
-    torch.cuda.synchronize()
-    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_off = max(1, args.steps // 2)
-    e2.record(stream)
-    for _ in range(n_off):
-        step_off()
-    e3.record(stream)
-    torch.cuda.synchronize()
-    ms_off = e2.elapsed_time(e3) / n_off
-    rows_off = R * (gamma + 1)
-    assert wsv_off.error_code() == 0, "device error word set in the scheduler-off pass"
+    warm = None
+    breakdown = None
+    sched_off = None
+    if not args.no_secondary:
+        # ---- warm-W2 secondary figure: the same rounds back to back, no flush
+        if round_dependent:
+            warm_ms = timed_rounds(K, one_round, False)
+        else:
+            ws_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(K)]
+            for i in range(K):
+                ws_ev[i][0].record(stream)
+                one_round(base + args.warmup + i)
+                ws_ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            warm_ms = [a.elapsed_time(b) for a, b in ws_ev]
+        warm = {"ms_per_step_median": round(float(np.median(warm_ms)), 4),
+                "ms_p10": round(pct(warm_ms, 10), 4), "ms_p90": round(pct(warm_ms, 90), 4),
+                "positions_per_s": round(R * gamma / (float(np.median(warm_ms)) / 1e3), 1)}
 
-    # ---- per-kernel launch durations (HIP events on the launch stream, separate pass)
+        # ---- per-entry-point breakdown (cold rounds, events around each call)
+        nb = min(K, 20)
+        bev = []
+        for i in range(nb):
+            rnd = base + args.warmup + i
+            prepare(rnd)
+            flush()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            draft(rnd)
+            e[1].record(stream)
+            schedule()
+            e[2].record(stream)
+            verify(rnd)
+            e[3].record(stream)
+            bev.append(e)
+        torch.cuda.synchronize()
+        t_draft = float(np.median([e[0].elapsed_time(e[1]) for e in bev]))
+        t_sched = float(np.median([e[1].elapsed_time(e[2]) for e in bev]))
+        t_ver = float(np.median([e[2].elapsed_time(e[3]) for e in bev]))
+        breakdown = {"draft": round(t_draft, 4), "schedule": round(t_sched, 4),
+                     "verify": round(t_ver, 4)}
+
+        # ---- the same workload with the scheduler off (ell = gamma for every
+        #      request: R (1 + gamma) target rows), a figure that does not depend
+        #      on the schedule; cold rounds
+        wss_off, wsv_off = ds.Workspace(), ds.Workspace()
+        s_off = ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off,
+                            stream=stream)
+        v_off = {}
+
+        def round_off(rnd):
+            draft(rnd)
+            ds.schedule(None, None, synth.SCHED_OFF, R=R, gamma=gamma, ws=wss_off, stream=stream,
+                        out=s_off)
+            d = keep["d"]
+            v_off["v"] = ds.verify(s_off["ell"], s_off["row_offset"], dT, dU, dW1, dW2, dx0,
+                                   d["x"], d["q_stats"], d["q_x"], temp=cfg.temp, seed=cfg.seed,
+                                   round=rnd, ws=wsv_off, stream=stream, out=v_off.get("v"))
+
+        off_ms = timed_rounds(min(K, 20), round_off, True)
+        assert wsv_off.error_code() == 0, "device error word set in the scheduler-off pass"
+        rows_off = R * (gamma + 1)
+        ms_off = float(np.median(off_ms))
+        off_bytes = (s_el * V * (R * gamma + R * gamma + rows_off) + 2 * s_el * r * V
+                     + (R * gamma * cfg.d * s_el if cfg.d else 0))
+        sched_off = {"ms_per_step": round(ms_off, 4),
+                     "positions_per_s": round(R * gamma / (ms_off / 1e3), 1),
+                     "verify_rows": rows_off,
+                     "round_bytes": int(off_bytes),
+                     "floor_frac": round(off_bytes / (PEAK_HBM_GBPS * 1e9) / (ms_off / 1e3), 4)}
+
+    # ---- per-kernel execution times (events stamped by each kernel's own
+    #      dispatch), cold rounds
+    #      (a schedule that depends on the round is laid out once, before the
+    #      pass, and the pass repeats that round)
+    nk = min(K, 20)
+    rnd0 = base + args.warmup
+    prepare(rnd0)
     ds.dspark_trace_enable(True)
-    for _ in range(args.steps):
-        step()
+    for i in range(nk):
+        rnd = rnd0 if round_dependent else rnd0 + i
+        flush()
+        one_round(rnd)
     torch.cuda.synchronize()
     ds.dspark_trace_enable(False)
     kern = ds.trace_summary()
 
-    # ---- standalone TV overlap on R * gamma logit pairs (statistics supplied)
-    n_pairs = R * gamma
-    Pp = P[:n_pairs] if P.shape[0] >= n_pairs else P
-    Qp = dU.reshape(R * gamma, V)[: Pp.shape[0]]
+    kern_ov = {}
+    n_ov = 0
+    if not args.no_secondary:
+        # ---- standalone TV overlap on R * gamma logit pairs (statistics supplied)
+        n_pairs = R * gamma
+        Pp = dT[:n_pairs]
+        Qp = dU.reshape(R * gamma, V)[: Pp.shape[0]]
+        n_ov = Pp.shape[0]
 
-    def stats(t):
-        z = t.float()
-        m = z.max(dim=1).values
-        return torch.stack([m, torch.exp(z - m[:, None]).sum(dim=1)], dim=1).contiguous()
+        def stats(t):
+            z = t.float()
+            m = z.max(dim=1).values
+            return torch.stack([m, torch.exp(z - m[:, None]).sum(dim=1)], dim=1).contiguous()
 
-    ps, qs = stats(Pp), stats(Qp)
-    ov_out = ds.tv_overlap(Pp, Qp, p_stats=ps, q_stats=qs, ws=wso, stream=stream)
-    ds.dspark_trace_enable(True)
-    for _ in range(args.steps):
-        ds.tv_overlap(Pp, Qp, p_stats=ps, q_stats=qs, ws=wso, stream=stream, out=ov_out)
-    torch.cuda.synchronize()
-    ds.dspark_trace_enable(False)
-    kern_ov = ds.trace_summary()
+        ps, qs = stats(Pp), stats(Qp)
+        ov_out = ds.tv_overlap(Pp, Qp, p_stats=ps, q_stats=qs, ws=wso, stream=stream)
+        ds.dspark_trace_enable(True)
+        for _ in range(nk):
+            flush()
+            ds.tv_overlap(Pp, Qp, p_stats=ps, q_stats=qs, ws=wso, stream=stream, out=ov_out)
+        torch.cuda.synchronize()
+        ds.dspark_trace_enable(False)
+        kern_ov = ds.trace_summary()
 
     # ---- secondary figures of the next rows on the same workload, separate passes:
     #      a round with the recurrent head (scheduler off, every position verified:
     #      compare with the scheduler-off round above) and the forward-only
     #      training reductions on label prefixes (teacher-forced draft + c*)
     next_rows = None
-    if not args.no_next_rows:
+    if not args.no_next_rows and not args.no_secondary:
         GE, Gh, Whh, bhh, s0, Wo = synth.rnn_head(cfg)
         dGE, dGh, dWhh, dbhh, ds0, dWo = up(GE), up(Gh), up(Whh), up(bhh), up(s0), up(Wo)
         wsr, wsrv, wst = ds.Workspace(), ds.Workspace(), ds.Workspace()
         y_lab = up(np.random.default_rng(11).integers(0, V, (R, gamma)).astype(np.int32))
         c_lab = up(np.random.default_rng(12).uniform(0.05, 0.95, (R, gamma)).astype(np.float32))
-        keep = {}
+        nk2 = {}
 
-        def rnn_round():
+        def rnn_round(rnd):
             d = ds.draft_rnn(dU, dWo, dGE, dGh, dWhh, dbhh, dx0, s0=ds0, temp=cfg.temp,
-                             seed=cfg.seed, round=cfg.round, ws=wsr, stream=stream,
-                             out=keep.get("d"))
-            keep["d"] = d
-            keep["v"] = ds.verify_rnn(sout_off["ell"], sout_off["row_offset"], dT, dU, d["A"], dWo,
-                                      dx0, d["x"], d["q_stats"], d["q_x"], temp=cfg.temp,
-                                      seed=cfg.seed, round=cfg.round, ws=wsrv, stream=stream,
-                                      out=keep.get("v"))
+                             seed=cfg.seed, round=rnd, ws=wsr, stream=stream, out=nk2.get("d"))
+            nk2["d"] = d
+            nk2["v"] = ds.verify_rnn(s_off["ell"], s_off["row_offset"], dT, dU, d["A"], dWo,
+                                     dx0, d["x"], d["q_stats"], d["q_x"], temp=cfg.temp,
+                                     seed=cfg.seed, round=rnd, ws=wsrv, stream=stream,
+                                     out=nk2.get("v"))
 
-        def train():
-            keep["t"] = ds.train_losses(dU, dW1, dW2, dT, dx0, y_lab, c_lab, temp=cfg.temp,
-                                        ws=wst, stream=stream, out=keep.get("t"))
+        def train(rnd):
+            nk2["t"] = ds.train_losses(dU, dW1, dW2, dT, dx0, y_lab, c_lab, temp=cfg.temp,
+                                       ws=wst, stream=stream, out=nk2.get("t"))
 
-        def timed(fn, n):
-            fn()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(n):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / n
-
-        n_next = max(1, args.steps // 2)
-        ms_rnn, ms_train = timed(rnn_round, n_next), timed(train, n_next)
+        n_next = max(1, min(K, 20) // 2)
+        rnn_round(base)
+        train(base)
+        ms_rnn = float(np.median(timed_rounds(n_next, rnn_round, True)))
+        ms_train = float(np.median(timed_rounds(n_next, train, True)))
         assert wsr.error_code() == 0 and wsrv.error_code() == 0 and wst.error_code() == 0, \
             "device error word set in a next-row pass"
         ds.dspark_trace_enable(True)
-        rnn_round()
+        rnn_round(base)
         torch.cuda.synchronize()
         ds.dspark_trace_enable(False)
         kr = ds.trace_summary()
@@ -292,55 +425,55 @@ def main():
         next_rows = {
             "rnn_head": {"ms_per_round": round(ms_rnn, 4),
                          "positions_per_s": round(R * gamma / (ms_rnn / 1e3), 1),
-                         "verify_rows": rows_off, "gru_step_us": round(gru_ms / gru_n * 1e3, 3),
-                         "markov_same_rows_ms": round(ms_off, 4)},
+                         "verify_rows": R * (gamma + 1), "gru_step_us": round(gru_ms / gru_n * 1e3, 3),
+                         "markov_same_rows_ms": sched_off["ms_per_step"]},
             "train_losses": {"ms_per_call": round(ms_train, 4),
                              "positions_per_s": round(R * gamma / (ms_train / 1e3), 1)},
         }
         print(f"[bench] next rows: recurrent-head round {ms_rnn:.3f} ms, "
               f"training reductions {ms_train:.3f} ms", file=sys.stderr, flush=True)
 
-    # ---- algorithmic work per launch of each kernel
-    rows_used = R + sum_ell
-    n_ov = Pp.shape[0]
-    # The fused tile kernels do 2*M*r*V flops on (M + r)*V*s bytes (M rows of U or
-    # U and P, plus W2): 2*128*256/((128 + 256)*2) = 85 flop/B for the draft step,
-    # below the MI355X ridge (~312 flop/B), so their roofline is HBM bandwidth;
-    # their matrix-core use is reported beside it.
+    # ---- algorithmic work per launch of each kernel (the method's bytes: every
+    #      input read once per call; W2 once per draft call, i.e. 1/gamma of it
+    #      per draft-step launch, and once per verify call)
     work = {
-        "bias_tile_draft": dict(bytes=R * V * s_el + r * V * s_el + R * r * s_el + R * nT * 8,
-                                flops=2.0 * R * r * V, bound="hbm"),
-        "draft_sample": dict(bytes=R * nT * 8 + R * 128 * (r + 1) * s_el, flops=0.0, bound="hbm"),
+        "bias_tile_draft": dict(bytes=R * V * s_el + r * V * s_el / gamma + R * r * s_el,
+                                flops=2.0 * R * r * V, bound="mfma"),
+        "draft_sample": dict(bytes=R * nT * 8, flops=0.0, bound="latency"),
         "head_hidden_dot": dict(bytes=R * gamma * cfg.d * s_el, flops=2.0 * R * gamma * cfg.d,
                                 bound="hbm"),
-        "schedule": dict(bytes=R * gamma * 4 * 2, flops=0.0, bound="hbm"),
-        "row_chunk_stats": dict(bytes=rows_used * V * s_el + rows_used * 32, flops=0.0, bound="hbm"),
-        "bias_tile_verify": dict(bytes=2 * sum_ell * V * s_el + r * V * s_el + sum_ell * nT * 8,
+        "schedule": dict(bytes=R * gamma * 4 * 2, flops=0.0, bound="latency"),
+        "row_chunk_stats": dict(bytes=rows_used * V * s_el, flops=0.0, bound="hbm"),
+        "bias_tile_verify": dict(bytes=2 * sum_ell * V * s_el + r * V * s_el,
                                  flops=2.0 * sum_ell * r * V, bound="hbm"),
-        "verify_finalize": dict(bytes=sum_ell * nT * 8 + R * nT * 8, flops=0.0, bound="hbm"),
+        "verify_finalize": dict(bytes=sum_ell * nT * 8 + R * nT * 8, flops=0.0, bound="latency"),
         "overlap_chunk": dict(bytes=2 * n_ov * V * s_el, flops=0.0, bound="hbm"),
-        "overlap_combine": dict(bytes=n_ov * 20, flops=0.0, bound="hbm"),
+        "overlap_combine": dict(bytes=n_ov * 20, flops=0.0, bound="latency"),
     }
+    peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == synth.BF16 else PEAK_F32_MFMA_TFLOPS
     kernels = {}
     for name, (ms, n) in list(kern.items()) + list(kern_ov.items()):
-        w = work.get(name, dict(bytes=0, flops=0.0, bound="hbm"))
+        w = work.get(name, dict(bytes=0, flops=0.0, bound="latency"))
+        per_round = n / nk
         avg_s = ms / n / 1e3
-        kernels[name] = dict(launches_per_step=n // args.steps, avg_us=round(avg_s * 1e6, 3),
-                             gbps=round(w["bytes"] / avg_s / 1e9, 1),
-                             tflops=round(w["flops"] / avg_s / 1e12, 2),
-                             bytes_per_launch=int(w["bytes"]), flops_per_launch=w["flops"],
-                             bound=w["bound"])
+        k = dict(launches_per_round=round(per_round, 3), avg_us=round(avg_s * 1e6, 3),
+                 bytes_per_launch=int(w["bytes"]), flops_per_launch=w["flops"], bound=w["bound"],
+                 gbps=round(w["bytes"] / avg_s / 1e9, 1),
+                 tflops=round(w["flops"] / avg_s / 1e12, 2))
+        k["hbm_frac"] = round(k["gbps"] / PEAK_HBM_GBPS, 4)
+        if w["flops"]:
+            k["mfma_frac"] = round(k["tflops"] / peak_mfma, 4)
+        kernels[name] = k
     step_kernels = {k: v for k, v in kernels.items() if not k.startswith("overlap")}
-    dom = max(step_kernels, key=lambda k: step_kernels[k]["avg_us"] * step_kernels[k]["launches_per_step"])
+    dom = max(step_kernels,
+              key=lambda k: step_kernels[k]["avg_us"] * step_kernels[k]["launches_per_round"])
     dk = kernels[dom]
     if dk["bound"] == "mfma":
-        roof = dict(bound="mfma", achieved=dk["tflops"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(dk["tflops"] / PEAK_BF16_TFLOPS, 4))
+        roof = dict(bound="mfma", achieved=dk["tflops"], peak=peak_mfma, unit="TFLOP/s",
+                    frac=dk["mfma_frac"])
     else:
         roof = dict(bound="hbm", achieved=dk["gbps"], peak=PEAK_HBM_GBPS, unit="GB/s",
-                    frac=round(dk["gbps"] / PEAK_HBM_GBPS, 4))
-    roof["kernel"] = dom
-    roof["mfma_frac"] = round(dk["tflops"] / PEAK_BF16_TFLOPS, 4)
+                    frac=dk["hbm_frac"])
     roof["traffic"] = None
     traffic_file = os.path.join(PROFILE_DIR, f"traffic_{dom}_{cfg.name.replace('-', '_')}.json")
     if os.path.exists(traffic_file):
@@ -348,6 +481,10 @@ def main():
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():
             roof["traffic"] = tr.get("bytes_per_launch")
+    roof.update(kernel=dom, avg_us=dk["avg_us"], algorithmic_bytes=dk["bytes_per_launch"],
+                flops_per_launch=dk["flops_per_launch"], hbm_frac=dk["hbm_frac"],
+                traffic_over_algorithmic=(round(roof["traffic"] / dk["bytes_per_launch"], 3)
+                                          if roof["traffic"] else None))
 
     # ---- the round's algorithmic HBM bytes (each input read once per call)
     round_bytes = (s_el * V * (R * gamma + sum_ell + rows_used) + 2 * s_el * r * V
@@ -360,7 +497,7 @@ def main():
     if args.cpu_requests > 0:
         import oracle
         nreq = min(args.cpu_requests, R)
-        o_ell = ell  # the verified lengths of this workload (sets the sample's size only)
+        o_ell = laid["ell"]  # the verified lengths of the last laid-out round (sets sizes only)
         t1 = time.perf_counter()
         for rho in range(nreq):
             hq = h[rho] if h is not None else None
@@ -372,17 +509,20 @@ def main():
         if c is not None:
             oracle.schedule(c, sps, cfg.mode, c_prev2=cp)
         cpu_s = time.perf_counter() - t1
+        model, ncpu, usable = host_cpu()
         cpu = dict(value=round(nreq * gamma / cpu_s, 3), unit="positions/s", cores=1,
-                   kind="oracle",
+                   kind="oracle", cpu_model=model, nproc=ncpu, usable_cpus=usable,
                    sample=f"{nreq} of {R} requests (draft of {gamma} positions + verify of the "
-                          f"scheduled rows each) plus the full schedule; {cpu_s:.1f} s on 1 thread")
+                          f"scheduled rows each) plus the full schedule; {cpu_s:.1f} s on 1 "
+                          f"thread of {model} ({ncpu} logical CPUs, {usable} usable)")
 
     out = {
-        "metric": METRIC,
+        "metric": (f"draft+verify positions/sec at V={V},R={R},γ={gamma}; "
+                   "achieved HBM GB/s"),
         "value": round(value, 1),
         "unit": "positions/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -394,18 +534,26 @@ def main():
                                f"scheduler mode {cfg.mode}, seeded synthetic logits",
                    "R": R, "gamma": gamma, "V": V, "r": r, "sum_ell": sum_ell,
                    "verify_rows": rows_used},
+        "timing": {"protocol": "per-round HIP events; caches flushed between rounds "
+                               f"({args.flush_mib} MiB scratch read+written, outside the events); "
+                               "Philox round counter varied; ms_per_step is the median of the "
+                               "K timed rounds, the percentiles cover n_rounds >= 50 such rounds",
+                   "n_rounds": len(cold_all),
+                   "ms_p10": round(pct(cold_all, 10), 4), "ms_p50": round(pct(cold_all, 50), 4),
+                   "ms_p90": round(pct(cold_all, 90), 4),
+                   "ms_mean": round(float(np.mean(cold_all)), 4),
+                   "wall_s_timed_region": round(wall, 4),
+                   "sum_ell_min": min(sum_ell_rounds), "sum_ell_max": max(sum_ell_rounds)},
+        "warm": warm,
         "achieved_hbm_gbps": round(round_bytes / (ms_step / 1e3) / 1e9, 1),
         "round_bytes": int(round_bytes),
-        "draft_positions_per_s": round(positions / (t_draft / 1e3), 1),
-        "verify_rows_per_s": round(rows_used / (t_ver / 1e3), 1),
-        "scheduler_off": {"ms_per_step": round(ms_off, 4),
-                          "positions_per_s": round(positions / (ms_off / 1e3), 1),
-                          "verify_rows": rows_off,
-                          "achieved_hbm_gbps": round(
-                              (s_el * V * (R * gamma + R * gamma + rows_off) + 2 * s_el * r * V
-                               + (R * gamma * cfg.d * s_el if cfg.d else 0)) / (ms_off / 1e3) / 1e9, 1)},
-        "breakdown_ms": {"draft": round(t_draft, 4), "schedule": round(t_sched, 4),
-                         "verify": round(t_ver, 4)},
+        "floor_frac": round(round_bytes / (PEAK_HBM_GBPS * 1e9) / (ms_step / 1e3), 4),
+        "draft_positions_per_s": (round(positions / (breakdown["draft"] / 1e3), 1)
+                                  if breakdown else None),
+        "verify_rows_per_s": (round(rows_used / (breakdown["verify"] / 1e3), 1)
+                              if breakdown else None),
+        "scheduler_off": sched_off,
+        "breakdown_ms": breakdown,
         "roofline": roof,
         "kernels": kernels,
         "next_rows": next_rows,

@@ -387,9 +387,8 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
   sp.x_force = L.x_force; sp.logq_x = L.logq_x;
   if (L.h != nullptr) {
     const int n_slots = L.R * L.gamma;
-    DSPARK_LAUNCH("head_hidden_dot", stream,
-                  head_hidden_dot_kernel<T><<<(n_slots + 3) / 4, kBlock, 0, stream>>>(
-                      n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh));
+    DSPARK_LAUNCH("head_hidden_dot", stream, head_hidden_dot_kernel<T>, (n_slots + 3) / 4, kBlock,
+                  n_slots, L.d, reinterpret_cast<const T *>(L.h), L.w_conf, L.sh);
     sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
     sp.conf_temp = L.conf_temp;
   }
@@ -421,19 +420,19 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     if (L.rnn != nullptr) {
       // the state update of step k gives the transition rows of step k
       gp.k = k;
-      DSPARK_LAUNCH("gru_step", stream, gru_step_kernel<T><<<gru_grid, kGruBlock, 0, stream>>>(gp));
+      DSPARK_LAUNCH("gru_step", stream, gru_step_kernel<T>, gru_grid, kGruBlock, gp);
       void *Ak = reinterpret_cast<T *>(L.rnn->A) + (int64_t)(k - 1) * L.R * L.r;
       bp.A = Ak; bp.a_tokens = nullptr;
       sp.A_cur = Ak; sp.a_tokens = nullptr; sp.A_next = nullptr;
     }
     if (wide) {
-      DSPARK_LAUNCH("bias_tile_draft", stream,
-                    (stream_tile_kernel<T, Epi::kDraft, KS, 8, 1><<<grid, 8 * kWave, 0, stream>>>(bp)));
+      DSPARK_LAUNCH("bias_tile_draft", stream, (stream_tile_kernel<T, Epi::kDraft, KS, 8, 1>), grid,
+                    8 * kWave, bp);
     } else {
-      DSPARK_LAUNCH("bias_tile_draft", stream,
-                    (stream_tile_kernel<T, Epi::kDraft, KS, 4, 1><<<grid, 4 * kWave, 0, stream>>>(bp)));
+      DSPARK_LAUNCH("bias_tile_draft", stream, (stream_tile_kernel<T, Epi::kDraft, KS, 4, 1>), grid,
+                    4 * kWave, bp);
     }
-    DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T><<<L.R, kBlock, 0, stream>>>(sp));
+    DSPARK_LAUNCH("draft_sample", stream, draft_sample_kernel<T>, L.R, kBlock, sp);
   }
   return hipGetLastError();
 }

@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(ScheduleLaunch 
 }
 
 hipError_t launch_schedule(const ScheduleLaunch &L, hipStream_t stream) {
-  DSPARK_LAUNCH("schedule", stream, schedule_kernel<<<1, kSchedThreads, 0, stream>>>(L));
+  DSPARK_LAUNCH("schedule", stream, schedule_kernel, 1, kSchedThreads, L);
   return hipGetLastError();
 }
 

@@ -51,16 +51,12 @@ void recycle_records() {
 
 bool trace_on() { return g_on.load(std::memory_order_relaxed); }
 
-void trace_begin(const char *name, hipStream_t stream) {
+void trace_events(const char *name, hipEvent_t *start, hipEvent_t *stop) {
   std::lock_guard<std::mutex> lock(g_mu);
   Record r{name, take_event(), take_event()};
-  if (r.start) (void)hipEventRecord(r.start, stream);
   g_records.push_back(r);
-}
-
-void trace_end(hipStream_t stream) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_records.empty() && g_records.back().stop) (void)hipEventRecord(g_records.back().stop, stream);
+  *start = r.start;
+  *stop = r.stop;
 }
 
 }  // namespace dspark

@@ -85,9 +85,8 @@ __global__ __launch_bounds__(kLossWaves * kWave) void loss_reduce_kernel(LossPar
 }
 
 hipError_t launch_train(const TrainLaunch &L, hipStream_t stream) {
-  DSPARK_LAUNCH("train_rows", stream,
-                train_rows_kernel<<<(L.R + 256) / 256, 256, 0, stream>>>(
-                    L.R, L.gamma, L.ell, L.row_offset));
+  DSPARK_LAUNCH("train_rows", stream, train_rows_kernel, (L.R + 256) / 256, 256, L.R, L.gamma,
+                L.ell, L.row_offset);
   hipError_t e = launch_draft(L.draft, stream);
   if (e != hipSuccess) return e;
   e = launch_verify(L.verify, stream);
@@ -96,8 +95,7 @@ hipError_t launch_train(const TrainLaunch &L, hipStream_t stream) {
   lp.R = L.R; lp.gamma = L.gamma; lp.logq = L.draft.logq_x; lp.c_star = L.verify.c_star;
   lp.c = L.c; lp.a_ce = L.a_ce; lp.a_tv = L.a_tv; lp.a_conf = L.a_conf;
   lp.per_pos = L.per_pos; lp.totals = L.totals;
-  DSPARK_LAUNCH("loss_reduce", stream,
-                loss_reduce_kernel<<<1, kLossWaves * kWave, 0, stream>>>(lp));
+  DSPARK_LAUNCH("loss_reduce", stream, loss_reduce_kernel, 1, kLossWaves * kWave, lp);
   return hipGetLastError();
 }
 

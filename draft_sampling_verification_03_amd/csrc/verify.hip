@@ -518,8 +518,8 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   rs.bonus_tiles = L.bonus_tiles; rs.err = L.err;
   rs.gamma = L.gamma; rs.x0 = L.x0; rs.x = L.x; rs.row_map = L.row_map;
   rs.r = L.r; rs.W1 = L.W1; rs.A_rows = L.A_rows; rs.A_given = L.A_given;
-  DSPARK_LAUNCH("row_chunk_stats", stream,
-                row_chunk_stats_kernel<T><<<dim3(kChunks, L.rows_capacity), kBlock, 0, stream>>>(rs));
+  DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.rows_capacity),
+                kBlock, rs);
 
   BiasTileParams bp{};
   bp.R = L.R; bp.gamma = L.gamma; bp.V = L.V; bp.r = L.r; bp.n_tiles = nT; bp.invT = L.invT;
@@ -537,11 +537,11 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   // or 3 row blocks per wave)
   if (L.r == (L.bf16 ? kMaxRank : 128)) {
     DSPARK_LAUNCH("bias_tile_verify", stream,
-                  (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64, 8, 1>
-                   <<<grid, 8 * kWave, 0, stream>>>(bp)));
+                  (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64, 8, 1>),
+                  grid, 8 * kWave, bp);
   } else {
-    DSPARK_LAUNCH("bias_tile_verify", stream,
-                  (stream_tile_kernel<T, Epi::kVerify, 0, 8, 1><<<grid, 8 * kWave, 0, stream>>>(bp)));
+    DSPARK_LAUNCH("bias_tile_verify", stream, (stream_tile_kernel<T, Epi::kVerify, 0, 8, 1>), grid,
+                  8 * kWave, bp);
   }
 
   FinalizeParams fp{};
@@ -551,7 +551,7 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   fp.q_stats = L.q_stats; fp.q_x = L.q_x; fp.seed = L.seed; fp.round = L.round;
   fp.p_chunks = L.p_chunks; fp.bonus_tiles = L.bonus_tiles; fp.pair_partials = L.pair_partials;
   fp.n_acc = L.n_acc; fp.y = L.y; fp.c_star = L.c_star; fp.err = L.err;
-  DSPARK_LAUNCH("verify_finalize", stream, verify_finalize_kernel<T><<<L.R, kBlock, 0, stream>>>(fp));
+  DSPARK_LAUNCH("verify_finalize", stream, verify_finalize_kernel<T>, L.R, kBlock, fp);
   return hipGetLastError();
 }
 
@@ -632,21 +632,20 @@ static hipError_t launch_overlap_t(const OverlapLaunch &L, hipStream_t stream) {
     RowStatsParams rs{};
     rs.n_rows = L.n_rows; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.err = L.err;
     rs.X = L.P; rs.chunks = L.p_chunks;
-    DSPARK_LAUNCH("row_chunk_stats", stream,
-                  row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs));
+    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.n_rows),
+                  kBlock, rs);
     rs.X = L.Q; rs.chunks = L.q_chunks;
-    DSPARK_LAUNCH("row_chunk_stats", stream,
-                  row_chunk_stats_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(rs));
+    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.n_rows),
+                  kBlock, rs);
   }
   OverlapParams op{};
   op.n_rows = L.n_rows; op.V = L.V; op.n_tiles = nT; op.invT = L.invT; op.P = L.P; op.Q = L.Q;
   op.p_stats = L.p_stats; op.q_stats = L.q_stats; op.p_chunks = L.p_chunks;
   op.q_chunks = L.q_chunks; op.partial = L.partial;
-  DSPARK_LAUNCH("overlap_chunk", stream,
-                overlap_chunk_kernel<T><<<dim3(kChunks, L.n_rows), kBlock, 0, stream>>>(op));
-  DSPARK_LAUNCH("overlap_combine", stream,
-                overlap_combine_kernel<<<(L.n_rows + 255) / 256, 256, 0, stream>>>(
-                    L.n_rows, L.partial, L.c_star));
+  DSPARK_LAUNCH("overlap_chunk", stream, overlap_chunk_kernel<T>, dim3(kChunks, L.n_rows), kBlock,
+                op);
+  DSPARK_LAUNCH("overlap_combine", stream, overlap_combine_kernel, (L.n_rows + 255) / 256, 256,
+                L.n_rows, L.partial, L.c_star);
   return hipGetLastError();
 }
 
