@@ -15,7 +15,8 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
  DSPARK_SCHED_THRESHOLD) = range(5)
 STATUS_NAMES = ["DSPARK_OK", "DSPARK_ERR_NULL", "DSPARK_ERR_SHAPE", "DSPARK_ERR_DTYPE",
                 "DSPARK_ERR_VALUE", "DSPARK_ERR_WORKSPACE", "DSPARK_ERR_SPS_TABLE",
-                "DSPARK_ERR_MODE", "DSPARK_ERR_ALIGN", "DSPARK_ERR_HIP"]
+                "DSPARK_ERR_MODE", "DSPARK_ERR_ALIGN", "DSPARK_ERR_HIP", "DSPARK_ERR_SCRATCH"]
+NOALLOC_SCRATCH_BYTES = 8 << 20  # DSPARK_NOALLOC_SCRATCH_BYTES
 
 
 class DSparkError(RuntimeError):
@@ -44,6 +45,10 @@ def library():
         L.dspark_draft_workspace.restype = _sz
         L.dspark_draft.argtypes = ([_i] * 5 + [_f] + [_vp] * 5 + [_i, _vp, _f, _vp, _u64, _u64]
                                    + [_vp] * 5 + [_sz, _vp])
+        L.dspark_draft_noalloc_scratch.argtypes = [_i, _i, _i]
+        L.dspark_draft_noalloc_scratch.restype = _sz
+        L.dspark_draft_noalloc.argtypes = ([_i] * 5 + [_f] + [_vp] * 5 + [_i, _vp, _f, _vp, _u64,
+                                           _u64] + [_vp] * 6)
         L.dspark_schedule_workspace.argtypes = [_i, _i]
         L.dspark_schedule_workspace.restype = _sz
         L.dspark_schedule.argtypes = [_i, _i, _i, _f, _vp, _vp, _vp, _i] + [_vp] * 6 + [_sz, _vp]
@@ -67,8 +72,8 @@ def library():
         L.dspark_trace_collect.argtypes = []
         L.dspark_trace_entry.argtypes = [_i, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                          C.POINTER(C.c_int)]
-        for name in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_tv_overlap",
-                     "dspark_train_losses", "dspark_draft_rnn", "dspark_verify_rnn",
+        for name in ("dspark_draft", "dspark_draft_noalloc", "dspark_schedule", "dspark_verify",
+                     "dspark_tv_overlap", "dspark_train_losses", "dspark_draft_rnn", "dspark_verify_rnn",
                      "dspark_device_error", "dspark_clear_device_error", "dspark_trace_enable",
                      "dspark_trace_collect", "dspark_trace_entry"):
             getattr(L, name).restype = _i
@@ -105,6 +110,18 @@ def dspark_draft(R, gamma, V, r, dt, temp, U, W1, W2, x0, h, d, w_conf, b_conf, 
     return library().dspark_draft(R, gamma, V, r, dt, temp, _p(U), _p(W1), _p(W2), _p(x0), _p(h),
                                   d, _p(w_conf), b_conf, _p(conf_temp), seed, round_, _p(x),
                                   _p(q_stats), _p(q_x), _p(c), _p(ws), ws_bytes, _s(stream))
+
+
+def dspark_draft_noalloc_scratch(R, gamma, V):
+    return library().dspark_draft_noalloc_scratch(R, gamma, V)
+
+
+def dspark_draft_noalloc(R, gamma, V, r, dt, temp, U, W1, W2, x0, h, d, w_conf, b_conf, conf_temp,
+                         seed, round_, x, q_stats, q_x, c, dev_error, stream):
+    return library().dspark_draft_noalloc(R, gamma, V, r, dt, temp, _p(U), _p(W1), _p(W2), _p(x0),
+                                          _p(h), d, _p(w_conf), b_conf, _p(conf_temp), seed,
+                                          round_, _p(x), _p(q_stats), _p(q_x), _p(c),
+                                          _p(dev_error), _s(stream))
 
 
 def dspark_schedule_workspace(R, gamma):

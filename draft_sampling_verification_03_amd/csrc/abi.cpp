@@ -5,12 +5,43 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dspark.h"
 #include "kernels.h"
 
 using namespace dspark;
 
+// Scratch of dspark_draft_noalloc: one copy per GPU, held until the process
+// ends.  Host code never passes this name to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the device address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (nullptr: not yet)
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device.
+hipError_t scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool bad_temp(float t) { return !(t > 0.0f) || !isfinite(t); }
@@ -48,6 +79,7 @@ const char *dspark_status_string(dspark_status s) {
     case DSPARK_ERR_MODE: return "unknown scheduler mode or missing confidences";
     case DSPARK_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case DSPARK_ERR_HIP: return "HIP launch or runtime error";
+    case DSPARK_ERR_SCRATCH: return "shape needs more than the library's static scratch";
   }
   return "unknown status";
 }
@@ -87,6 +119,50 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
   L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
   L.c = c;
+  return from_hip(launch_draft(L, stream));
+}
+
+size_t dspark_draft_noalloc_scratch(int R, int gamma, int V) {
+  if (R < 1 || gamma < 1 || V < 1) return 0;
+  return draft_ws_bytes(R, gamma, V) - kWsHeader;
+}
+
+dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                   const void *U, const void *W1, const void *W2,
+                                   const int32_t *x0, const void *h, int d, const float *w_conf,
+                                   float b_conf, const float *conf_temp, uint64_t seed,
+                                   uint64_t round, int32_t *x, float *q_stats, float *q_x,
+                                   float *c, int32_t *dev_error, hipStream_t stream) {
+  dspark_status s = check_common(R, gamma, V, r, dt, temp);
+  if (s != DSPARK_OK) return s;
+  if (!U || !W1 || !W2 || !x0 || !x || !q_stats || !q_x || !dev_error) return DSPARK_ERR_NULL;
+  if (h != nullptr) {
+    if (!w_conf || !c) return DSPARK_ERR_NULL;
+    if (d < 8 || d > 65536 || d % 8 != 0) return DSPARK_ERR_SHAPE;
+    if (!isfinite(b_conf)) return DSPARK_ERR_VALUE;
+    if (!aligned16(h)) return DSPARK_ERR_ALIGN;
+  }
+  if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || ((uintptr_t)dev_error & 3u) != 0)
+    return DSPARK_ERR_ALIGN;
+  const size_t need = draft_ws_bytes(R, gamma, V) - kWsHeader;
+  if (need > (size_t)DSPARK_NOALLOC_SCRATCH_BYTES) return DSPARK_ERR_SCRATCH;
+  void *base = nullptr;
+  if (scratch_of_current_device(&base) != hipSuccess) return DSPARK_ERR_HIP;
+  // the same pieces as dspark_draft's workspace, without its header: the
+  // sticky error word is the caller's dev_error, cleared by a kernel here
+  size_t off = 0;
+  DraftLaunch L{};
+  L.err = dev_error;
+  L.tile_stats = (float2 *)carve(base, &off, (size_t)R * n_tiles_of(V) * 8);
+  L.sh = (float *)carve(base, &off, (size_t)R * gamma * 4);
+  L.A0 = carve(base, &off, (size_t)R * kMaxRowBytes);
+  L.A1 = carve(base, &off, (size_t)R * kMaxRowBytes);
+  L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
+  L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
+  L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
+  L.seed = seed; L.round = round; L.x = x; L.q_stats = q_stats; L.q_x = q_x;
+  L.c = c;
+  if (launch_clear_error(dev_error, stream) != hipSuccess) return DSPARK_ERR_HIP;
   return from_hip(launch_draft(L, stream));
 }
 

@@ -88,7 +88,8 @@ typedef enum {
   DSPARK_ERR_SPS_TABLE = 6, /* SPS table missing or shorter than R(1+gamma)+1 */
   DSPARK_ERR_MODE = 7,      /* unknown scheduler mode or missing c / c_prev2  */
   DSPARK_ERR_ALIGN = 8,     /* a pointer not 16-byte aligned                  */
-  DSPARK_ERR_HIP = 9        /* a HIP launch or runtime call failed            */
+  DSPARK_ERR_HIP = 9,       /* a HIP launch or runtime call failed            */
+  DSPARK_ERR_SCRATCH = 10   /* the shape needs more than the static scratch   */
 } dspark_status;
 
 /* Bits of the sticky device error word. */
@@ -138,6 +139,32 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
                            const float *conf_temp, uint64_t seed, uint64_t round,
                            int32_t *x, float *q_stats, float *q_x, float *c,
                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------- draft without allocation --
+ * dspark_draft for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as dspark_draft; the
+ * draft's scratch (tile partials R * ceil(V/128) * 8 bytes, the head's dot
+ * products, two transition-row buffers) lives in a static device array of
+ * DSPARK_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * workspace); its first call on a GPU looks up that GPU's copy of the array.
+ *   dev_error  [1] int32 device word: cleared by the call, then receives the
+ *              DSPARK_DEVERR_* bits of this call (as the workspace word of
+ *              dspark_draft does).
+ * Limit: dspark_draft_noalloc_scratch(R, gamma, V) <= DSPARK_NOALLOC_SCRATCH_BYTES,
+ * e.g. R <= 512 at V = 151936; larger shapes return DSPARK_ERR_SCRATCH and
+ * enqueue nothing.  All calls on one GPU share the array: calls whose kernels
+ * may overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller. */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (8u << 20)
+size_t dspark_draft_noalloc_scratch(int R, int gamma, int V);
+dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
+                                   const void *U, const void *W1, const void *W2,
+                                   const int32_t *x0, const void *h, int d, const float *w_conf,
+                                   float b_conf, const float *conf_temp, uint64_t seed,
+                                   uint64_t round, int32_t *x, float *q_stats, float *q_x,
+                                   float *c, int32_t *dev_error, hipStream_t stream);
 
 /* --------------------------------------------------------------- schedule --
  * Hardware-aware prefix scheduler (KB section 4; Blog "Scheduler objective",

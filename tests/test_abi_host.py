@@ -29,14 +29,15 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = ds.library()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in dspark.h but not exported"
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert A.dspark_status_string(s)
+    assert "scratch" in A.dspark_status_string(10)
     assert A.dspark_status_string(99) == "unknown status"
 
 
@@ -301,3 +302,22 @@ def test_other_wrappers_reject_bad_tensors():
     with pytest.raises(ValueError):                    # host tensors
         ds.draft_rnn(t["U"], t["W1"], torch.zeros(V, 3 * r), torch.zeros(R, gamma, 3 * r),
                      torch.zeros(r, 3 * r), torch.zeros(3 * r), t["x0"])
+
+
+def test_draft_noalloc_host_checks():
+    """The allocation-free draft validates like dspark_draft and rejects shapes
+    whose scratch exceeds the static array, before any HIP call."""
+    need = A.dspark_draft_noalloc_scratch(128, 16, 151936)
+    assert need == A.dspark_draft_workspace(128, 16, 151936, 256, A.DSPARK_BF16) - 256
+    assert A.dspark_draft_noalloc_scratch(512, 15, 151936) <= A.NOALLOC_SCRATCH_BYTES
+    assert A.dspark_draft_noalloc_scratch(1024, 15, 151936) > A.NOALLOC_SCRATCH_BYTES
+    base = dict(R=4, gamma=4, V=1024, r=16, dt=A.DSPARK_F32, temp=1.0, U=P, W1=P, W2=P, x0=P,
+                h=None, d=0, w_conf=None, b_conf=0.0, conf_temp=None, seed=0, round_=0, x=P,
+                q_stats=P, q_x=P, c=None, dev_error=P, stream=None)
+    for over, expect in [(dict(R=1024, gamma=15, V=151936, r=256, dt=A.DSPARK_BF16), 10),
+                         (dict(dev_error=None), NULL), (dict(dev_error=P + 2), ALIGN),
+                         (dict(U=P + 8), ALIGN), (dict(temp=0.0), VALUE),
+                         (dict(r=8), SHAPE), (dict(h=P, d=16, w_conf=None), NULL)]:
+        a = dict(base)
+        a.update(over)
+        assert A.dspark_draft_noalloc(**a) == expect, over

@@ -1,0 +1,103 @@
+"""dspark_draft_noalloc (the allocation-free draft, scratch in a static device
+array) against dspark_draft (caller's workspace) through the C ABI: the same
+kernels, so every output must be identical bit for bit, on consecutive calls
+of decreasing size (the static array keeps the previous call's contents)."""
+import numpy as np
+import pytest
+import torch
+
+import draft_sampling_verification_03_amd as ds
+import synth
+from draft_sampling_verification_03_amd import _abi as A
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(R, gamma, V, r, bf16, head, seed):
+    rng = np.random.default_rng(seed)
+    store = synth.to_bf16_bits if bf16 else (lambda a: a.astype(np.float32))
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to("cuda")
+
+    c = dict(U=dev(store(3.0 * rng.standard_normal((R, gamma, V)).astype(np.float32))),
+             W1=dev(store((0.05 * rng.standard_normal((V, r))).astype(np.float32))),
+             W2=dev(store((0.05 * rng.standard_normal((V, r))).astype(np.float32))),
+             x0=dev(rng.integers(0, V, R).astype(np.int32)), h=None, w=None, T=None, d=0)
+    if head:
+        d = 64
+        c.update(h=dev(store(rng.standard_normal((R, gamma, d)).astype(np.float32))),
+                 w=dev((0.2 * rng.standard_normal(d + r)).astype(np.float32)),
+                 T=dev(rng.uniform(0.5, 2.0, gamma).astype(np.float32)), d=d)
+    return c
+
+
+def _noalloc(c, seed, rnd, stream):
+    R, gamma, V = c["U"].shape
+    r = c["W1"].shape[1]
+    dt = A.DSPARK_BF16 if c["U"].dtype == torch.bfloat16 else A.DSPARK_F32
+    o = dict(x=torch.full((R, gamma), -7, dtype=torch.int32, device="cuda"),
+             q_stats=torch.full((R, gamma, 2), float("nan"), device="cuda"),
+             q_x=torch.full((R, gamma), float("nan"), device="cuda"),
+             c=torch.full((R, gamma), float("nan"), device="cuda") if c["h"] is not None else None,
+             err=torch.full((1,), 12345, dtype=torch.int32, device="cuda"))
+    st = A.dspark_draft_noalloc(R, gamma, V, r, dt, 1.0, c["U"], c["W1"], c["W2"], c["x0"], c["h"],
+                                c["d"], c["w"], 0.3, c["T"], seed, rnd, o["x"], o["q_stats"],
+                                o["q_x"], o["c"], o["err"], stream)
+    assert st == 0, A.dspark_status_string(st)
+    return o
+
+
+def _reference(c, seed, rnd, stream):
+    ws = ds.Workspace()
+    o = ds.draft(c["U"], c["W1"], c["W2"], c["x0"], seed=seed, round=rnd, h=c["h"], w_conf=c["w"],
+                 b_conf=0.3, conf_temp=c["T"], ws=ws, stream=stream)
+    return o, ws
+
+
+def _same(a, b):
+    return np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_noalloc_draft_matches_workspace_draft_on_consecutive_calls():
+    stream = torch.cuda.current_stream()
+    cases = [(128, 4, 151936, 256, True, True), (7, 3, 2056, 32, True, False),
+             (5, 2, 1000, 16, False, True)]
+    for i, (R, gamma, V, r, bf16, head) in enumerate(cases):
+        print(f"[noalloc] call {i}: R={R} gamma={gamma} V={V} r={r} bf16={bf16} head={head}",
+              flush=True)
+        c = _case(R, gamma, V, r, bf16, head, seed=40 + i)
+        got = _noalloc(c, seed=3, rnd=i, stream=stream)
+        ref, ws = _reference(c, seed=3, rnd=i, stream=stream)
+        torch.cuda.synchronize()
+        assert int(got["err"].cpu()[0]) == 0 and ws.error_code() == 0
+        assert np.array_equal(got["x"].cpu().numpy(), ref["x"].cpu().numpy())
+        assert _same(got["q_stats"], ref["q_stats"]) and _same(got["q_x"], ref["q_x"])
+        if head:
+            assert _same(got["c"], ref["c"])
+
+
+def test_noalloc_draft_error_word_is_per_call():
+    stream = torch.cuda.current_stream()
+    c = _case(6, 2, 1024, 16, False, False, seed=9)
+    bad = c["x0"].clone()
+    bad[2] = 1024 + 3
+    c_bad = dict(c, x0=bad)
+    got = _noalloc(c_bad, seed=1, rnd=0, stream=stream)
+    torch.cuda.synchronize()
+    assert int(got["err"].cpu()[0]) & 1
+    got = _noalloc(c, seed=1, rnd=0, stream=stream)
+    ref, _ = _reference(c, seed=1, rnd=0, stream=stream)
+    torch.cuda.synchronize()
+    assert int(got["err"].cpu()[0]) == 0
+    assert np.array_equal(got["x"].cpu().numpy(), ref["x"].cpu().numpy())
+
+
+def test_noalloc_draft_rejects_shapes_beyond_the_scratch():
+    R, gamma, V, r = 1024, 15, 151936, 256
+    assert A.dspark_draft_noalloc_scratch(R, gamma, V) > A.NOALLOC_SCRATCH_BYTES
+    p = 1 << 16
+    st = A.dspark_draft_noalloc(R, gamma, V, r, A.DSPARK_BF16, 1.0, p, p, p, p, None, 0, None, 0.0,
+                                None, 0, 0, p, p, p, None, p, None)
+    assert A.STATUS_NAMES[st] == "DSPARK_ERR_SCRATCH"
