@@ -439,6 +439,10 @@ def main():
     work = {
         "bias_tile_draft": dict(bytes=R * V * s_el + r * V * s_el / gamma + R * r * s_el,
                                 flops=2.0 * R * r * V, bound="mfma"),
+        # all gamma steps in one launch: U once, W2 once, the transition rows
+        "draft_persistent": dict(bytes=R * gamma * V * s_el + r * V * s_el + R * gamma * r * s_el,
+                                 flops=2.0 * R * r * V * gamma, bound="mfma"),
+        "persist_clear": dict(bytes=0, flops=0.0, bound="latency"),
         "draft_sample": dict(bytes=R * nT * 8, flops=0.0, bound="latency"),
         "head_hidden_dot": dict(bytes=R * gamma * cfg.d * s_el, flops=2.0 * R * gamma * cfg.d,
                                 bound="hbm"),

@@ -114,6 +114,7 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
   L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
   L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  L.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
   L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
@@ -157,6 +158,7 @@ dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype 
   L.sh = (float *)carve(base, &off, (size_t)R * gamma * 4);
   L.A0 = carve(base, &off, (size_t)R * kMaxRowBytes);
   L.A1 = carve(base, &off, (size_t)R * kMaxRowBytes);
+  L.flags = (int *)carve(base, &off, ((size_t)kComputeUnits + R) * 4);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
   L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
@@ -187,6 +189,7 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, dspark_dtype dt, 
   L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
   L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
   L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  L.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp;
   L.U = U; L.W1 = nullptr; L.W2 = W_o; L.x0 = x0; L.seed = seed; L.round = round; L.x = x;
   L.q_stats = q_stats; L.q_x = q_x;
@@ -319,6 +322,7 @@ dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype d
   D.sh = (float *)carve(ws, &off, n * 4);
   D.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
   D.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
+  D.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
   D.x = (int32_t *)carve(ws, &off, n * 4);
   D.q_stats = (float *)carve(ws, &off, n * 8);
   D.q_x = (float *)carve(ws, &off, n * 4);

@@ -24,7 +24,7 @@ constexpr int kMaxRank = 256;
 constexpr int kMaxGamma = 64;       // draft positions per request
 
 // sticky device error bits (mirrors dspark.h)
-constexpr int kErrToken = 1, kErrConfidence = 2, kErrLength = 4, kErrNonFinite = 8;
+constexpr int kErrToken = 1, kErrConfidence = 2, kErrLength = 4, kErrNonFinite = 8, kErrSync = 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -91,6 +91,17 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Device-coherent 8-byte accesses (agent-scope relaxed atomics): data that one
+// workgroup writes and workgroups on other XCDs read within the same kernel
+// travel this way, so no L2 writeback or invalidation is needed around them.
+__device__ __forceinline__ void st_coherent(void *p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const void *p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void flag_error(int32_t *err, int bits) {

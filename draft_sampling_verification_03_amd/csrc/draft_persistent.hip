@@ -1,0 +1,414 @@
+// Persistent Markov-head draft: all gamma steps of one dspark_draft call in a
+// single cooperative launch, with the W2 factor held on chip for the whole call.
+//
+// The Markov head (Blog, "Markov sequential head"; KB section 2) multiplies
+// the same r x V factor W2 at every one of the gamma serial steps; the head is
+// meant to cost a small, sequential amount on top of the parallel block
+// (Bangkok 5.3).  Streaming W2 from memory at every step would triple the
+// bytes of a step at R = 128 (W2 is 77.8 MB, the step's U_k rows 38.9 MB).
+// Here each workgroup (one per compute unit) owns a fixed range of at most NT
+// whole 128-column vocabulary tiles and keeps their W2 columns for the whole
+// call: wave w holds the 32-column block w of every tile, the first NT - 1
+// tiles' operands in its registers (64 per tile), the last one in LDS.  Per
+// step only U_k and the transition rows move.
+//
+// One step k:
+//   1. the transition rows A_k = W1[x_{k-1}] of every request (x_0 = anchor)
+//      go to LDS;
+//   2. for each 32-request row block, each wave multiplies its W2 blocks with
+//      the rows on the matrix cores (bf16 32x32x16, fp32 accumulation from
+//      zero, K ascending, W2 as the first operand: the same instruction
+//      sequence as the per-step product kernel, so every z = acc + U is
+//      bit-identical to what the sampler recomputes), adds U_k and reduces
+//      each row's 32 columns to (max, sum of exp) in the epilogue, which runs
+//      while the next block's products issue;
+//   3. the four waves' block partials of a tile combine in a fixed order into
+//      the tile partial (m_t, s_t), written to global memory; the workgroup
+//      then publishes "tiles of step k written" in its own flag word;
+//   4. the workgroups that own requests (rho = g, g + G, ...) wait for every
+//      tile flag, draw x_k with the two-level inverse CDF of sampler.h, write
+//      W1[x_k] for step k + 1 and publish "request rho drawn" in the
+//      request's flag word;
+//   5. every workgroup waits for all request flags before step k + 1 reads
+//      the rows W1[x_k].
+// Flags are words written once per step by one workgroup (no contended
+// read-modify-write), with device-coherent stores; every wait is bounded, and
+// a wait that runs out sets DSPARK_DEVERR_SYNC and ends the kernel.  The
+// cooperative launch guarantees that all workgroups are resident at once.
+#include "bias_tile.h"
+#include "kernels.h"
+#include "sampler.h"
+#include "trace.h"
+
+namespace dspark {
+
+constexpr int kPRows = 128;                 // requests whose rows fit in LDS
+constexpr int kPKS = kMaxRank / 16;         // K steps (r = 256)
+constexpr int kPPitch = kMaxRank + 8;       // LDS pitch of a transition row (bf16 elements)
+constexpr int kSpinLimit = 1 << 18;         // polls before a wait gives up
+
+struct PersistParams {
+  int R, gamma, V, n_tiles;
+  float invT;
+  const bf16_t *U;      // [R][gamma][V]
+  const bf16_t *W1;     // [V][256]
+  const bf16_t *W2;     // column-major 256 x V
+  const int32_t *x0;    // [R]
+  float2 *tile_stats;   // [R][n_tiles]
+  bf16_t *A_next;       // [R][256]: W1[x_k], written by the samplers of step k
+  int *flag_tiles;      // [gridDim.x]: last step whose tile partials are written
+  int *flag_rows;       // [R]: last step whose draw (and row W1[x_k]) is published
+  SampleParams sp;      // x, q_stats, q_x, head, forcing, err (A_cur, a_tokens unused)
+  int32_t *err;
+};
+
+template <int NT>
+struct PersistLds {
+  bf16_t rows[kPRows * kPPitch];                    // A_k, one row per request
+  int tok[kPRows];                                   // x_{k-1} of every request
+  u32x4 w2l[kPKS * 4 * kWave];                       // W2 of the last tile slot, per lane
+  float2 part[kPRows][NT][4];                        // (max of v, sum) per row, tile, wave
+  SampleLds sl;
+  int abort;
+};
+
+// The data other workgroups read (tile partials, transition rows) is written
+// with device-coherent stores; once every thread's stores have completed
+// (waitcnt), thread 0 stores `value` into the flag word, also coherently.  No
+// L2 writeback is needed: nothing the readers need is held in an L2.
+__device__ __forceinline__ void publish(int *flag, int value) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until flags[0..n) >= target (thread t polls flags t, t + kBlock, ...);
+// afterwards the data published with them can be read with device-coherent
+// loads.  Returns false (and flags the error) if a poll ran out.
+template <int NT>
+__device__ __forceinline__ bool wait_flags(const int *flags, int n, int target, int32_t *err,
+                                           PersistLds<NT> &sh) {
+  bool ok = true;
+  for (int i = threadIdx.x; i < n && ok; i += kBlock) {
+    int spins = 0;
+    while (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kSpinLimit) {
+        ok = false;
+        break;
+      }
+    }
+  }
+  if (!ok) {
+    sh.abort = 1;
+    flag_error(err, kErrSync);
+  }
+  __syncthreads();
+  return sh.abort == 0;
+}
+
+// The anchors x_0 (validated) into sh.tok (step 1's transition rows are
+// W1[x_0]); thread t takes requests t, t + kBlock, ...
+template <int NT>
+__device__ __forceinline__ void anchor_tokens(const PersistParams &p, PersistLds<NT> &sh) {
+  bool bad = false;
+  for (int row = threadIdx.x; row < p.R; row += kBlock) {
+    int tok = p.x0[row];
+    if (tok < 0 || tok >= p.V) {
+      bad = true;
+      tok = tok < 0 ? 0 : p.V - 1;
+    }
+    sh.tok[row] = tok;
+  }
+  if (bad) flag_error(p.err, kErrToken);
+  __syncthreads();
+}
+
+// NT: vocabulary tiles per workgroup (at most); kMask: V is not a multiple of
+// the tile width, so the last tile has columns past V.
+template <int NT, bool kMask>
+__global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistParams p) {
+  __shared__ __align__(16) PersistLds<NT> sh;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int G = gridDim.x, g = blockIdx.x;
+  const int R = p.R, gamma = p.gamma, V = p.V, nT = p.n_tiles;
+  const int t0 = (int)((int64_t)g * nT / G), t1 = (int)((int64_t)(g + 1) * nT / G);
+  const int ntl = t1 - t0;  // <= NT (checked by the host)
+  const int nrb = (R + kRowsPerWave - 1) / kRowsPerWave;
+  const float invT = p.invT, cl = invT * kLog2e;
+  const int m = lane & 31, half = lane >> 5;
+  if (tid == 0) sh.abort = 0;
+
+  // ---- W2 of this wave's blocks: block `wave` of tiles t0 .. t0 + NT - 1
+  //      (a slot past the range, or a column past V, reads a clamped column;
+  //      its results are dropped); slots 0 .. NT - 2 in registers, the last
+  //      slot in LDS, where each lane keeps its own 16-byte pieces
+  constexpr int kPRegTiles = NT - 1;
+  u16x8 w2r[kPRegTiles][kPKS];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int col = min((t0 + i) * kTileN + wave * kBlockCols + block_col_of_m(m), V - 1);
+    const bf16_t *src = p.W2 + (int64_t)col * kMaxRank + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < kPKS; ++ks) {
+      const u16x8 v = *reinterpret_cast<const u16x8 *>(src + ks * 16);
+      if (i < kPRegTiles) {
+        w2r[i < kPRegTiles ? i : 0][ks] = v;
+        // keep the operand in the accumulation registers (the products read
+        // it there directly); left to itself the allocator moved parts of it
+        // to scratch or copied it into vector registers before every product
+        asm volatile("" : "+a"(w2r[i < kPRegTiles ? i : 0][ks]));
+      }
+      else sh.w2l[(ks * 4 + wave) * kWave + lane] = __builtin_bit_cast(u32x4, v);
+    }
+  }
+
+  // ---- U of item (row block rb, tile slot i) at step k: this lane's 16
+  //      columns of its row (two 16-byte pieces; a piece is wholly inside or
+  //      outside [0, V) because V % 8 == 0)
+  struct UPiece { u32x4 a, b; };
+  auto load_u = [&](int k, int rb, int i) __attribute__((always_inline)) {
+    const int rho = min(rb * kRowsPerWave + m, R - 1);
+    const int c0 = min((t0 + i) * kTileN + wave * kBlockCols + half * 16, V - 16);
+    const bf16_t *src = p.U + ((int64_t)rho * gamma + (k - 1)) * V + c0;
+    UPiece u;
+    u.a = *reinterpret_cast<const u32x4 *>(src);
+    u.b = *reinterpret_cast<const u32x4 *>(src + 8);
+    return u;
+  };
+  // the U ring holds one row block of items ahead; item i is tile slot slot_of(i)
+  auto slot_of = [](int i) { return i == 0 ? NT - 1 : i - 1; };
+  UPiece ur[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, slot_of(i));
+
+  for (int k = 1; k <= gamma; ++k) {
+    // ---- 1. transition rows of step k into LDS: W1[x_0] at k = 1, then the
+    //      rows W1[x_{k-1}] the samplers published (rows >= R are zero)
+    if (k == 1) anchor_tokens<NT>(p, sh);
+    {
+      // thread t: 16-byte piece t % 32 of rows t / 32 + 8 j: every load in
+      // flight before the first LDS store, and no branch between them (a row
+      // past R reads row R - 1 and stores zeros)
+      constexpr int kPieces = kMaxRank * 2 / 16;  // 16-byte pieces per row
+      constexpr int kIt = kPRows * kPieces / kBlock;
+      constexpr int kBatch = kIt;
+      // the thread's piece and first row, redefined every step: hoisted out
+      // of the step loop, the row addresses went to scratch, and each reload
+      // waited for every load issued before it
+      int off = (tid % kPieces) * 8, row0 = tid / kPieces;
+      asm volatile("" : "+v"(off), "+v"(row0));
+      auto store_batch = [&](int b, const u32x4 (&v)[kBatch]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int row = row0 + (b + j) * (kBlock / kPieces);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4 *>(sh.rows + row * kPPitch + off) = row < R ? v[j] : z;
+        }
+      };
+      if (k == 1) {
+#pragma unroll
+        for (int b = 0; b < kIt; b += kBatch) {
+          u32x4 v[kBatch];
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) {
+            const int row = min(row0 + (b + j) * (kBlock / kPieces), R - 1);
+            v[j] = *reinterpret_cast<const u32x4 *>(p.W1 + (int64_t)sh.tok[row] * kMaxRank + off);
+          }
+          store_batch(b, v);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < kIt; b += kBatch) {
+          u32x4 v[kBatch];
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) {
+            const int row = min(row0 + (b + j) * (kBlock / kPieces), R - 1);
+            const bf16_t *src = p.A_next + row * kMaxRank + off;
+            const uint64_t lo = ld_coherent(src), hi = ld_coherent(src + 4);
+            v[j] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+          }
+          store_batch(b, v);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 2. products and epilogues, row block by row block.  Item i of a
+    //      row block is tile slot slot_of(i): the LDS-held slot first, so that
+    //      its operand reads are in flight together with the rows'
+    for (int rb = 0; rb < nrb; ++rb) {
+      u16x8 bfr[kPKS];
+      {
+        const bf16_t *rowp = sh.rows + (rb * kRowsPerWave + m) * kPPitch + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < kPKS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8 *>(rowp + ks * 16);
+      }
+      // products of item i >= 1 (W2 from registers)
+      auto mma = [&](int i) __attribute__((always_inline)) {
+        floatx16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kPKS; ++ks) acc = mfma16<true>(w2r[i > 0 ? i - 1 : 0][ks], bfr[ks], acc);
+        return acc;
+      };
+      // the next U of an item: the same tile slot one row block later, or
+      // the first row block of the next step (the last step reloads its own)
+      const bool last_rb = rb + 1 == nrb;
+      const int k_next = last_rb ? min(k + 1, gamma) : k;
+      const int rb_next = last_rb ? 0 : rb + 1;
+      auto epilogue = [&](int i, const floatx16 &acc) __attribute__((always_inline)) {
+        const int sl = slot_of(i);
+        float v[16];
+        unpack16(ur[i].a, (bf16_t *)nullptr, v);
+        unpack16(ur[i].b, (bf16_t *)nullptr, v + 8);
+        const int c0 = (t0 + sl) * kTileN + wave * kBlockCols + half * 16;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          v[c] = acc[c] + v[c];  // z * T: the product kernels' exact expression
+          if (kMask && c0 + c >= V) v[c] = -INFINITY;
+        }
+        ur[i] = load_u(k_next, rb_next, sl);
+        float bm = v[0];
+#pragma unroll
+        for (int c = 1; c < 16; ++c) bm = fmaxf(bm, v[c]);
+        float s = 0.0f;
+        if (!kMask || bm != -INFINITY) {
+          const float nb = -bm * cl;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) s += exp2_fast(fmaf(v[c], cl, nb));
+        }
+        // the other 16 columns of the row are in lane l ^ 32
+        // (both lanes of a row form the same sum: their operands are swapped
+        // and addition is commutative, so both store the same value)
+        const float om = half_swap(bm), os = half_swap(s);
+        const float M = fmaxf(bm, om);
+        const float S2 = s * exp2_fast((bm - M) * cl) + os * exp2_fast((om - M) * cl);
+        sh.part[rb * kRowsPerWave + m][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
+      };
+      // item 0 (the LDS-held slot): every operand read in flight before
+      // its first product
+      u16x8 w2f[kPKS];
+#pragma unroll
+      for (int ks = 0; ks < kPKS; ++ks)
+        w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane]);
+      __builtin_amdgcn_sched_barrier(0);
+      floatx16 acc0, acc1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc0[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kPKS; ++ks) acc0 = mfma16<true>(w2f[ks], bfr[ks], acc0);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (i + 1 < NT) {
+          if (i & 1) acc0 = mma(i + 1);
+          else acc1 = mma(i + 1);
+        }
+        epilogue(i, (i & 1) ? acc1 : acc0);
+        // the epilogue of item i issues while the products of item i + 1 run
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector ALU
+        }
+        // nothing moves across items: hoisting the next items' loads would
+        // run out of registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+
+    // ---- 3. tile partials (fixed wave order), then this workgroup's flag
+    for (int q = tid; q < R * ntl; q += kBlock) {
+      const int row = q / ntl, i = q - row * ntl;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.part[row][i][w].x);
+      float S = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float2 pw = sh.part[row][i][w];
+          if (pw.x != -INFINITY) S += pw.y * exp2_fast((pw.x - M) * cl);
+        }
+      }
+      // max z = (max of acc + u) / T exactly (rounding is monotone)
+      st_coherent(p.tile_stats + (int64_t)row * nT + t0 + i,
+                  __builtin_bit_cast(uint64_t, make_float2(M * invT, S)));
+    }
+    publish(p.flag_tiles + g, k);
+
+    // ---- 4. draws of this workgroup's requests
+    if (g < R) {
+      if (!wait_flags<NT>(p.flag_tiles, G, k, p.err, sh)) return;
+      for (int rho = g; rho < R; rho += G) {
+        sample_row<bf16_t, true>(p.sp, k, k < gamma ? p.A_next : nullptr, rho,
+                                 sh.rows + rho * kPPitch, false, sh.sl);
+        __syncthreads();  // LDS of the draw is reused by the next request
+        publish(p.flag_rows + rho, k);
+      }
+    }
+    if (k == gamma) break;
+
+    // ---- 5. every request drawn before the next step reads its row
+    if (!wait_flags<NT>(p.flag_rows, R, k, p.err, sh)) return;
+  }
+}
+
+__global__ void persist_clear_kernel(int *flags, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0;
+}
+
+// Launch shape of the persistent draft, or false when the shape does not fit
+// it (then the per-step kernels run).  One workgroup per compute unit; each
+// holds at most 5 tiles (640 columns) of W2.
+bool persistent_draft_shape(int R, int V, int r, bool bf16, int *grid, int *nt) {
+  if (!bf16 || r != kMaxRank || R > kPRows || V < kTileN) return false;
+  const int n_tiles = (V + kTileN - 1) / kTileN;
+  const int G = n_tiles < kComputeUnits ? n_tiles : kComputeUnits;
+  const int per = (n_tiles + G - 1) / G;
+  if (per > 5) return false;
+  *grid = G;
+  *nt = per <= 4 ? 4 : 5;
+  return true;
+}
+
+template <int NT, bool kMask>
+static hipError_t launch_persistent_t(PersistParams &pp, int G, hipStream_t stream) {
+  void *args[] = {&pp};
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (trace_on()) trace_events("draft_persistent", &start, &stop);
+  if (start) (void)hipEventRecord(start, stream);
+  hipError_t e = hipLaunchCooperativeKernel(
+      reinterpret_cast<const void *>(&draft_persistent_kernel<NT, kMask>), dim3(G), dim3(kBlock),
+      args, 0, stream);
+  if (stop) (void)hipEventRecord(stop, stream);
+  return e;
+}
+
+hipError_t launch_draft_persistent(const DraftLaunch &L, int G, int nt, const SampleParams &sp,
+                                   hipStream_t stream) {
+  const int n_tiles = (L.V + kTileN - 1) / kTileN;
+  PersistParams pp{};
+  pp.R = L.R; pp.gamma = L.gamma; pp.V = L.V; pp.n_tiles = n_tiles; pp.invT = L.invT;
+  pp.U = reinterpret_cast<const bf16_t *>(L.U);
+  pp.W1 = reinterpret_cast<const bf16_t *>(L.W1);
+  pp.W2 = reinterpret_cast<const bf16_t *>(L.W2);
+  pp.x0 = L.x0; pp.tile_stats = L.tile_stats;
+  pp.A_next = reinterpret_cast<bf16_t *>(L.A0);
+  pp.flag_tiles = L.flags;
+  pp.flag_rows = L.flags + kComputeUnits;
+  pp.sp = sp;
+  pp.err = L.err;
+  const int nflags = kComputeUnits + L.R;  // tile flags, then the request flags
+  DSPARK_LAUNCH("persist_clear", stream, persist_clear_kernel, (nflags + 255) / 256, 256, L.flags,
+                nflags);
+  const bool mask = L.V % kTileN != 0;
+  if (nt == 4) return mask ? launch_persistent_t<4, true>(pp, G, stream)
+                           : launch_persistent_t<4, false>(pp, G, stream);
+  return mask ? launch_persistent_t<5, true>(pp, G, stream)
+              : launch_persistent_t<5, false>(pp, G, stream);
+}
+
+}  // namespace dspark

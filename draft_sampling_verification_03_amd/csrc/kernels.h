@@ -45,6 +45,7 @@ struct DraftLaunch {
   float2 *tile_stats;  // [R][n_tiles]
   float *sh;           // [R][gamma]
   void *A0, *A1;       // [R][r] each: transition rows of the current and next step
+  int *flags;          // [kComputeUnits + R]: tile and request flags of the persistent draft
 };
 
 struct ScheduleLaunch {
@@ -119,7 +120,7 @@ constexpr size_t kMaxRowBytes = 512;
 
 inline size_t draft_ws_bytes(int R, int gamma, int V) {
   return kWsHeader + ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4) +
-         2 * ws_align((size_t)R * kMaxRowBytes);
+         2 * ws_align((size_t)R * kMaxRowBytes) + ws_align(((size_t)kComputeUnits + R) * 4);
 }
 inline size_t schedule_ws_bytes(int R, int gamma) {
   (void)R; (void)gamma;

@@ -97,6 +97,8 @@ typedef enum {
 #define DSPARK_DEVERR_CONFIDENCE 2 /* a confidence outside [0, 1] or NaN           */
 #define DSPARK_DEVERR_LENGTH 4     /* ell outside [0, gamma] or row_offset mismatch */
 #define DSPARK_DEVERR_NONFINITE 8  /* a row max or normalizer not finite           */
+#define DSPARK_DEVERR_SYNC 16      /* a device-wide wait of the persistent draft
+                                      ran out (its outputs are then incomplete)    */
 
 /* ------------------------------------------------------------------ draft --
  * Semi-autoregressive Markov-head drafting (Blog "Markov sequential head";
