@@ -16,7 +16,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 STATUS_NAMES = ["DSPARK_OK", "DSPARK_ERR_NULL", "DSPARK_ERR_SHAPE", "DSPARK_ERR_DTYPE",
                 "DSPARK_ERR_VALUE", "DSPARK_ERR_WORKSPACE", "DSPARK_ERR_SPS_TABLE",
                 "DSPARK_ERR_MODE", "DSPARK_ERR_ALIGN", "DSPARK_ERR_HIP", "DSPARK_ERR_SCRATCH"]
-NOALLOC_SCRATCH_BYTES = 8 << 20  # DSPARK_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20  # DSPARK_NOALLOC_SCRATCH_BYTES
 
 
 class DSparkError(RuntimeError):

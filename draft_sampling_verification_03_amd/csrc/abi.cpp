@@ -63,6 +63,15 @@ char *carve(void *ws, size_t *off, size_t bytes) {
   return p;
 }
 
+// the draft's workspace pieces after the header, in the order draft_ws_bytes sums them
+void carve_draft(void *base, size_t *off, int R, int gamma, int V, DraftLaunch &L) {
+  L.tile_stats = (float2 *)carve(base, off, (size_t)2 * R * n_tiles_of(V) * 8);
+  L.sh = (float *)carve(base, off, (size_t)R * gamma * 4);
+  L.A0 = carve(base, off, (size_t)R * kMaxRowBytes);
+  L.A1 = carve(base, off, (size_t)R * kMaxRowBytes);
+  L.pub = (uint64_t *)carve(base, off, (size_t)R * 8);
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,11 +119,7 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
   size_t off = 0;
   DraftLaunch L{};
   L.err = (int32_t *)carve(ws, &off, kWsHeader);
-  L.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
-  L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
-  L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  L.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
+  carve_draft(ws, &off, R, gamma, V, L);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
   L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
@@ -154,11 +159,7 @@ dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype 
   size_t off = 0;
   DraftLaunch L{};
   L.err = dev_error;
-  L.tile_stats = (float2 *)carve(base, &off, (size_t)R * n_tiles_of(V) * 8);
-  L.sh = (float *)carve(base, &off, (size_t)R * gamma * 4);
-  L.A0 = carve(base, &off, (size_t)R * kMaxRowBytes);
-  L.A1 = carve(base, &off, (size_t)R * kMaxRowBytes);
-  L.flags = (int *)carve(base, &off, ((size_t)kComputeUnits + R) * 4);
+  carve_draft(base, &off, R, gamma, V, L);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.d = d; L.bf16 = dt == DSPARK_BF16;
   L.invT = 1.0f / temp; L.U = U; L.W1 = W1; L.W2 = W2; L.x0 = x0; L.h = h; L.w_conf = w_conf;
   L.b_conf = b_conf; L.conf_temp = h != nullptr ? conf_temp : nullptr;
@@ -185,11 +186,7 @@ dspark_status dspark_draft_rnn(int R, int gamma, int V, int r, dspark_dtype dt, 
   size_t off = 0;
   DraftLaunch L{};
   L.err = (int32_t *)carve(ws, &off, kWsHeader);
-  L.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
-  L.sh = (float *)carve(ws, &off, (size_t)R * gamma * 4);
-  L.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  L.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  L.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
+  carve_draft(ws, &off, R, gamma, V, L);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp;
   L.U = U; L.W1 = nullptr; L.W2 = W_o; L.x0 = x0; L.seed = seed; L.round = round; L.x = x;
   L.q_stats = q_stats; L.q_x = q_x;
@@ -318,11 +315,7 @@ dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype d
   TrainLaunch T{};
   DraftLaunch &D = T.draft;
   D.err = err;
-  D.tile_stats = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
-  D.sh = (float *)carve(ws, &off, n * 4);
-  D.A0 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  D.A1 = carve(ws, &off, (size_t)R * kMaxRowBytes);
-  D.flags = (int *)carve(ws, &off, ((size_t)kComputeUnits + R) * 4);
+  carve_draft(ws, &off, R, gamma, V, D);
   D.x = (int32_t *)carve(ws, &off, n * 4);
   D.q_stats = (float *)carve(ws, &off, n * 8);
   D.q_x = (float *)carve(ws, &off, n * 4);

@@ -640,7 +640,8 @@ inline int stream_tile_grid(int total_items, int max_groups) {
 // increasing order from a zero accumulator.  Called by all 256 threads; wave w
 // produces columns 32w..32w+31 of the tile.  Writes v (or -inf past V) to
 // vout[0..127].
-template <typename T, bool kW2First>
+// KS > 0 fixes the number of K steps at compile time (see mma_rows).
+template <typename T, bool kW2First, int KS = 0>
 __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, const T *Urow,
                                                  int V, int r, int tile, int row_in_block,
                                                  float *vout) {
@@ -659,7 +660,7 @@ __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, 
     BFrag<T> bfr;
     load_bfrag(W2, V, r, b0 + block_col_of_m(lane & 31), bfr);
     floatx16 acc[1];
-    mma_rows<true, 1>(ldsArow, 0, 0, r, bfr, acc);
+    mma_rows<true, 1, KS>(ldsArow, 0, 0, r, bfr, acc);
     if ((lane & 31) == row_in_block) {
 #pragma unroll
       for (int i = 0; i < 16 / kPer; ++i) {
@@ -680,7 +681,7 @@ __device__ __forceinline__ void recompute_tile_v(const T *ldsArow, const T *W2, 
     BFrag<T> bfr;
     load_bfrag(W2, V, r, col, bfr);
     floatx16 acc[1];
-    mma_rows<false, 1>(ldsArow, 0, 0, r, bfr, acc);
+    mma_rows<false, 1, KS>(ldsArow, 0, 0, r, bfr, acc);
     const int reg = acc_reg_of_row(row_in_block);
     if ((lane >> 5) == acc_half_of_row(row_in_block)) {
       float a = 0.0f;

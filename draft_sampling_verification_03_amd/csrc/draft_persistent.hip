@@ -14,7 +14,8 @@
 //
 // One step k:
 //   1. the transition rows A_k = W1[x_{k-1}] of every request (x_0 = anchor)
-//      go to LDS;
+//      go to LDS, gathered straight from W1 once the step's draws are
+//      published;
 //   2. for each 32-request row block, each wave multiplies its W2 blocks with
 //      the rows on the matrix cores (bf16 32x32x16, fp32 accumulation from
 //      zero, K ascending, W2 as the first operand: the same instruction
@@ -23,18 +24,21 @@
 //      each row's 32 columns to (max, sum of exp) in the epilogue, which runs
 //      while the next block's products issue;
 //   3. the four waves' block partials of a tile combine in a fixed order into
-//      the tile partial (m_t, s_t), written to global memory; the workgroup
-//      then publishes "tiles of step k written" in its own flag word;
-//   4. the workgroups that own requests (rho = g, g + G, ...) wait for every
-//      tile flag, draw x_k with the two-level inverse CDF of sampler.h, write
-//      W1[x_k] for step k + 1 and publish "request rho drawn" in the
-//      request's flag word;
-//   5. every workgroup waits for all request flags before step k + 1 reads
-//      the rows W1[x_k].
-// Flags are words written once per step by one workgroup (no contended
-// read-modify-write), with device-coherent stores; every wait is bounded, and
-// a wait that runs out sets DSPARK_DEVERR_SYNC and ends the kernel.  The
-// cooperative launch guarantees that all workgroups are resident at once.
+//      the tile partial (m_t, s_t), stored as one 8-byte word in the half of
+//      the partial buffer that belongs to the step's parity;
+//   4. the workgroups that own requests (rho = g, g + G, ...) poll their row's
+//      partial words until every one is written, reset them, draw x_k with the
+//      two-level inverse CDF of sampler.h and publish (k << 32) | x_k in the
+//      request's word;
+//   5. every workgroup waits for all R words of step k before step k + 1.
+// The data itself is the signal: no flag word stands between a write and its
+// reader, and no store has to be acknowledged before another is issued,
+// except the resets, which complete before the draw that follows them is
+// published (the partial words are written again two steps later, only
+// after that draw).  Every access to shared words is device-coherent, every
+// wait is bounded, and a wait that runs out sets DSPARK_DEVERR_SYNC and ends
+// the kernel.  The cooperative launch guarantees that all workgroups are
+// resident at once.
 #include "bias_tile.h"
 #include "kernels.h"
 #include "sampler.h"
@@ -45,7 +49,6 @@ namespace dspark {
 constexpr int kPRows = 128;                 // requests whose rows fit in LDS
 constexpr int kPKS = kMaxRank / 16;         // K steps (r = 256)
 constexpr int kPPitch = kMaxRank + 8;       // LDS pitch of a transition row (bf16 elements)
-constexpr int kSpinLimit = 1 << 18;         // polls before a wait gives up
 
 struct PersistParams {
   int R, gamma, V, n_tiles;
@@ -54,10 +57,8 @@ struct PersistParams {
   const bf16_t *W1;     // [V][256]
   const bf16_t *W2;     // column-major 256 x V
   const int32_t *x0;    // [R]
-  float2 *tile_stats;   // [R][n_tiles]
-  bf16_t *A_next;       // [R][256]: W1[x_k], written by the samplers of step k
-  int *flag_tiles;      // [gridDim.x]: last step whose tile partials are written
-  int *flag_rows;       // [R]: last step whose draw (and row W1[x_k]) is published
+  uint64_t *tiles;      // [2][R][n_tiles]: partial words of steps of each parity
+  uint64_t *pub;        // [R]: (k << 32) | x_k, the last published draw
   SampleParams sp;      // x, q_stats, q_x, head, forcing, err (A_cur, a_tokens unused)
   int32_t *err;
 };
@@ -72,36 +73,27 @@ struct PersistLds {
   int abort;
 };
 
-// The data other workgroups read (tile partials, transition rows) is written
-// with device-coherent stores; once every thread's stores have completed
-// (waitcnt), thread 0 stores `value` into the flag word, also coherently.  No
-// L2 writeback is needed: nothing the readers need is held in an L2.
-__device__ __forceinline__ void publish(int *flag, int value) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until flags[0..n) >= target (thread t polls flags t, t + kBlock, ...);
-// afterwards the data published with them can be read with device-coherent
-// loads.  Returns false (and flags the error) if a poll ran out.
+// The draws x_step of every request into sh.tok, once published (thread t
+// polls requests t, t + kBlock, ...).  Returns false (and flags the error)
+// if a poll ran out.
 template <int NT>
-__device__ __forceinline__ bool wait_flags(const int *flags, int n, int target, int32_t *err,
-                                           PersistLds<NT> &sh) {
+__device__ __forceinline__ bool wait_tokens(const PersistParams &p, PersistLds<NT> &sh, int step) {
   bool ok = true;
-  for (int i = threadIdx.x; i < n && ok; i += kBlock) {
-    int spins = 0;
-    while (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > kSpinLimit) {
+  for (int row = threadIdx.x; row < p.R; row += kBlock) {
+    uint64_t v = ld_coherent(p.pub + row);
+    for (int spins = 0; (int64_t)(v >> 32) < step; ++spins) {
+      if (spins > kSpinLimit) {
         ok = false;
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
+      v = ld_coherent(p.pub + row);
     }
+    sh.tok[row] = (int)min((uint32_t)v, (uint32_t)(p.V - 1));  // in range when published
   }
   if (!ok) {
     sh.abort = 1;
-    flag_error(err, kErrSync);
+    flag_error(p.err, kErrSync);
   }
   __syncthreads();
   return sh.abort == 0;
@@ -129,7 +121,8 @@ __device__ __forceinline__ void anchor_tokens(const PersistParams &p, PersistLds
 template <int NT, bool kMask>
 __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistParams p) {
   __shared__ __align__(16) PersistLds<NT> sh;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int G = gridDim.x, g = blockIdx.x;
   const int R = p.R, gamma = p.gamma, V = p.V, nT = p.n_tiles;
   const int t0 = (int)((int64_t)g * nT / G), t1 = (int)((int64_t)(g + 1) * nT / G);
@@ -167,7 +160,7 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   //      columns of its row (two 16-byte pieces; a piece is wholly inside or
   //      outside [0, V) because V % 8 == 0)
   struct UPiece { u32x4 a, b; };
-  auto load_u = [&](int k, int rb, int i) __attribute__((always_inline)) {
+  auto load_u = [&](int k, int rb, int i, int m, int half) __attribute__((always_inline)) {
     const int rho = min(rb * kRowsPerWave + m, R - 1);
     const int c0 = min((t0 + i) * kTileN + wave * kBlockCols + half * 16, V - 16);
     const bf16_t *src = p.U + ((int64_t)rho * gamma + (k - 1)) * V + c0;
@@ -180,56 +173,38 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   auto slot_of = [](int i) { return i == 0 ? NT - 1 : i - 1; };
   UPiece ur[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, slot_of(i));
+  for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, slot_of(i), m, half);
 
   for (int k = 1; k <= gamma; ++k) {
-    // ---- 1. transition rows of step k into LDS: W1[x_0] at k = 1, then the
-    //      rows W1[x_{k-1}] the samplers published (rows >= R are zero)
+    // the thread's index, opaque to the compiler once per step: addresses
+    // derived from it are formed again every step instead of being held
+    // across the whole loop (where they went to scratch, and every reload
+    // waited for all loads in flight, the U prefetch included)
+    int tid_k = tid;
+    asm volatile("" : "+v"(tid_k));
+    const int lane_k = tid_k & (kWave - 1), m_k = lane_k & 31, half_k = lane_k >> 5;
+    // ---- 1. transition rows of step k into LDS: W1[x_{k-1}], x_0 the
+    //      anchors, then the draws the samplers published (rows >= R are zero)
     if (k == 1) anchor_tokens<NT>(p, sh);
+    else if (!wait_tokens<NT>(p, sh, k - 1)) return;
     {
       // thread t: 16-byte piece t % 32 of rows t / 32 + 8 j: every load in
       // flight before the first LDS store, and no branch between them (a row
       // past R reads row R - 1 and stores zeros)
       constexpr int kPieces = kMaxRank * 2 / 16;  // 16-byte pieces per row
       constexpr int kIt = kPRows * kPieces / kBlock;
-      constexpr int kBatch = kIt;
-      // the thread's piece and first row, redefined every step: hoisted out
-      // of the step loop, the row addresses went to scratch, and each reload
-      // waited for every load issued before it
-      int off = (tid % kPieces) * 8, row0 = tid / kPieces;
-      asm volatile("" : "+v"(off), "+v"(row0));
-      auto store_batch = [&](int b, const u32x4 (&v)[kBatch]) __attribute__((always_inline)) {
+      const int off = (tid_k % kPieces) * 8, row0 = tid_k / kPieces;
+      u32x4 v[kIt];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int row = row0 + (b + j) * (kBlock / kPieces);
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4 *>(sh.rows + row * kPPitch + off) = row < R ? v[j] : z;
-        }
-      };
-      if (k == 1) {
+      for (int j = 0; j < kIt; ++j) {
+        const int row = min(row0 + j * (kBlock / kPieces), R - 1);
+        v[j] = *reinterpret_cast<const u32x4 *>(p.W1 + (int64_t)sh.tok[row] * kMaxRank + off);
+      }
 #pragma unroll
-        for (int b = 0; b < kIt; b += kBatch) {
-          u32x4 v[kBatch];
-#pragma unroll
-          for (int j = 0; j < kBatch; ++j) {
-            const int row = min(row0 + (b + j) * (kBlock / kPieces), R - 1);
-            v[j] = *reinterpret_cast<const u32x4 *>(p.W1 + (int64_t)sh.tok[row] * kMaxRank + off);
-          }
-          store_batch(b, v);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < kIt; b += kBatch) {
-          u32x4 v[kBatch];
-#pragma unroll
-          for (int j = 0; j < kBatch; ++j) {
-            const int row = min(row0 + (b + j) * (kBlock / kPieces), R - 1);
-            const bf16_t *src = p.A_next + row * kMaxRank + off;
-            const uint64_t lo = ld_coherent(src), hi = ld_coherent(src + 4);
-            v[j] = u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-          }
-          store_batch(b, v);
-        }
+      for (int j = 0; j < kIt; ++j) {
+        const int row = row0 + j * (kBlock / kPieces);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(sh.rows + row * kPPitch + off) = row < R ? v[j] : z;
       }
     }
     __syncthreads();
@@ -240,7 +215,7 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
     for (int rb = 0; rb < nrb; ++rb) {
       u16x8 bfr[kPKS];
       {
-        const bf16_t *rowp = sh.rows + (rb * kRowsPerWave + m) * kPPitch + half * 8;
+        const bf16_t *rowp = sh.rows + (rb * kRowsPerWave + m_k) * kPPitch + half_k * 8;
 #pragma unroll
         for (int ks = 0; ks < kPKS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8 *>(rowp + ks * 16);
       }
@@ -263,13 +238,13 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         float v[16];
         unpack16(ur[i].a, (bf16_t *)nullptr, v);
         unpack16(ur[i].b, (bf16_t *)nullptr, v + 8);
-        const int c0 = (t0 + sl) * kTileN + wave * kBlockCols + half * 16;
+        const int c0 = (t0 + sl) * kTileN + wave * kBlockCols + half_k * 16;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
           v[c] = acc[c] + v[c];  // z * T: the product kernels' exact expression
           if (kMask && c0 + c >= V) v[c] = -INFINITY;
         }
-        ur[i] = load_u(k_next, rb_next, sl);
+        ur[i] = load_u(k_next, rb_next, sl, m_k, half_k);
         float bm = v[0];
 #pragma unroll
         for (int c = 1; c < 16; ++c) bm = fmaxf(bm, v[c]);
@@ -285,14 +260,14 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         const float om = half_swap(bm), os = half_swap(s);
         const float M = fmaxf(bm, om);
         const float S2 = s * exp2_fast((bm - M) * cl) + os * exp2_fast((om - M) * cl);
-        sh.part[rb * kRowsPerWave + m][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
+        sh.part[rb * kRowsPerWave + m_k][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
       };
       // item 0 (the LDS-held slot): every operand read in flight before
       // its first product
       u16x8 w2f[kPKS];
 #pragma unroll
       for (int ks = 0; ks < kPKS; ++ks)
-        w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane]);
+        w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane_k]);
       __builtin_amdgcn_sched_barrier(0);
       floatx16 acc0, acc1;
 #pragma unroll
@@ -319,8 +294,9 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
     }
     __syncthreads();
 
-    // ---- 3. tile partials (fixed wave order), then this workgroup's flag
-    for (int q = tid; q < R * ntl; q += kBlock) {
+    // ---- 3. tile partials (fixed wave order) into the step's half
+    uint64_t *tiles = p.tiles + (int64_t)(k & 1) * R * nT;
+    for (int q = tid_k; q < R * ntl; q += kBlock) {
       const int row = q / ntl, i = q - row * ntl;
       float M = -INFINITY;
 #pragma unroll
@@ -334,30 +310,29 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         }
       }
       // max z = (max of acc + u) / T exactly (rounding is monotone)
-      st_coherent(p.tile_stats + (int64_t)row * nT + t0 + i,
-                  __builtin_bit_cast(uint64_t, make_float2(M * invT, S)));
+      uint64_t word = __builtin_bit_cast(uint64_t, make_float2(M * invT, S));
+      if (word == kTileEmpty) word = kTileEmpty - 1;  // another NaN: still read as non-finite
+      st_coherent(tiles + (int64_t)row * nT + t0 + i, word);
     }
-    publish(p.flag_tiles + g, k);
 
     // ---- 4. draws of this workgroup's requests
-    if (g < R) {
-      if (!wait_flags<NT>(p.flag_tiles, G, k, p.err, sh)) return;
-      for (int rho = g; rho < R; rho += G) {
-        sample_row<bf16_t, true>(p.sp, k, k < gamma ? p.A_next : nullptr, rho,
-                                 sh.rows + rho * kPPitch, false, sh.sl);
-        __syncthreads();  // LDS of the draw is reused by the next request
-        publish(p.flag_rows + rho, k);
-      }
+    for (int rho = g; rho < R; rho += G) {
+      const PersistIo io{tiles, p.pub, &sh.abort};
+      if (!sample_row<bf16_t, true, kPKS>(p.sp, k, nullptr, rho, sh.rows + rho * kPPitch, false,
+                                          sh.sl, io))
+        return;
+      __syncthreads();  // LDS of the draw is reused by the next request
     }
     if (k == gamma) break;
-
-    // ---- 5. every request drawn before the next step reads its row
-    if (!wait_flags<NT>(p.flag_rows, R, k, p.err, sh)) return;
+    // ---- 5. the next step waits for every draw of this one (step 1 above)
   }
 }
 
-__global__ void persist_clear_kernel(int *flags, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0;
+// Before each launch: every partial word empty, every draw unpublished.
+__global__ void persist_clear_kernel(uint64_t *tiles, int n_words, uint64_t *pub, int R) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += gridDim.x * blockDim.x)
+    tiles[i] = kTileEmpty;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < R; i += gridDim.x * blockDim.x) pub[i] = 0;
 }
 
 // Launch shape of the persistent draft, or false when the shape does not fit
@@ -395,15 +370,15 @@ hipError_t launch_draft_persistent(const DraftLaunch &L, int G, int nt, const Sa
   pp.U = reinterpret_cast<const bf16_t *>(L.U);
   pp.W1 = reinterpret_cast<const bf16_t *>(L.W1);
   pp.W2 = reinterpret_cast<const bf16_t *>(L.W2);
-  pp.x0 = L.x0; pp.tile_stats = L.tile_stats;
-  pp.A_next = reinterpret_cast<bf16_t *>(L.A0);
-  pp.flag_tiles = L.flags;
-  pp.flag_rows = L.flags + kComputeUnits;
+  pp.x0 = L.x0;
+  pp.tiles = reinterpret_cast<uint64_t *>(L.tile_stats);  // [2][R][n_tiles]
+  pp.pub = L.pub;
   pp.sp = sp;
   pp.err = L.err;
-  const int nflags = kComputeUnits + L.R;  // tile flags, then the request flags
-  DSPARK_LAUNCH("persist_clear", stream, persist_clear_kernel, (nflags + 255) / 256, 256, L.flags,
-                nflags);
+  const int n_words = 2 * L.R * n_tiles;
+  DSPARK_LAUNCH("persist_clear", stream, persist_clear_kernel,
+                std::min((n_words + 255) / 256, 4 * kComputeUnits), 256, pp.tiles, n_words, L.pub,
+                L.R);
   const bool mask = L.V % kTileN != 0;
   if (nt == 4) return mask ? launch_persistent_t<4, true>(pp, G, stream)
                            : launch_persistent_t<4, false>(pp, G, stream);

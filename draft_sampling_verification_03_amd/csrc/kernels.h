@@ -42,10 +42,11 @@ struct DraftLaunch {
   const RnnHead *rnn;      // recurrent head instead of the W1 table, or NULL
   // workspace pieces
   int32_t *err;
-  float2 *tile_stats;  // [R][n_tiles]
+  float2 *tile_stats;  // [2][R][n_tiles]: the per-step kernels use the first half, the
+                       // persistent draft both, by the parity of the step
   float *sh;           // [R][gamma]
   void *A0, *A1;       // [R][r] each: transition rows of the current and next step
-  int *flags;          // [kComputeUnits + R]: tile and request flags of the persistent draft
+  uint64_t *pub;       // [R]: draws published by the persistent draft
 };
 
 struct ScheduleLaunch {
@@ -119,8 +120,8 @@ inline int n_tiles_of(int V) { return (V + 127) / 128; }
 constexpr size_t kMaxRowBytes = 512;
 
 inline size_t draft_ws_bytes(int R, int gamma, int V) {
-  return kWsHeader + ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4) +
-         2 * ws_align((size_t)R * kMaxRowBytes) + ws_align(((size_t)kComputeUnits + R) * 4);
+  return kWsHeader + ws_align((size_t)2 * R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * 4) +
+         2 * ws_align((size_t)R * kMaxRowBytes) + ws_align((size_t)R * 8);
 }
 inline size_t schedule_ws_bytes(int R, int gamma) {
   (void)R; (void)gamma;

@@ -47,18 +47,33 @@ struct SampleLds {
   float s_before, s_mt, s_u;
 };
 
+// The persistent draft's side of a draw (sample_row<T, true>), where other
+// workgroups of the same kernel write the row's tile partials and read the
+// draw: the partial words are polled in place until none reads kTileEmpty,
+// then reset to kTileEmpty (the writers of the step two later find them so),
+// and the draw is published as (k << 32) | x_k.  All these accesses are
+// device-coherent.
+struct PersistIo {
+  uint64_t *tiles;  // the step's [R][n_tiles] partial words (bits of float2 (max z, sum))
+  uint64_t *pub;    // [R]
+  int *abort;       // the workgroup's LDS word, set when a wait runs out
+};
+constexpr uint64_t kTileEmpty = ~0ull;  // a NaN pattern (writers store another for it)
+constexpr int kSpinLimit = 1 << 18;     // polls before a wait gives up
+
 // Draw x_k of request rho (k = position, 1-based; p.k is not read); called by
 // all kBlock threads of the workgroup.  arow: W1[x_{k-1}] of rho in LDS (r
 // elements, 16-byte aligned).  With stage_arow the function first copies that
 // row there itself (from A_cur, or from W1[a_tokens[rho]] in place);
 // otherwise the caller has put it there.  A_next (or NULL) receives W1[x_k].
-// The tile partials, and the transition rows read through A_cur or a_tokens,
-// must be visible to the workgroup before the call.  kCoherent: the tile
-// partials are read, and A_next written, with device-coherent accesses (the
-// persistent draft, where other workgroups wrote them in the same kernel).
-template <typename T, bool kCoherent = false>
-__device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A_next, int rho,
-                                           T *arow, bool stage_arow, SampleLds &sl) {
+// Without kPersist the tile partials (p.tile_stats), and the transition rows
+// read through A_cur or a_tokens, must be visible before the call; with it
+// see PersistIo.  KS > 0: r = 16 KS (bf16), fixed at compile time.  Returns
+// false, in every thread, only when a persistent wait ran out (kErrSync).
+template <typename T, bool kPersist = false, int KS = 0>
+__device__ __forceinline__ bool sample_row(const SampleParams &p, int k, void *A_next, int rho,
+                                           T *arow, bool stage_arow, SampleLds &sl,
+                                           const PersistIo &io = PersistIo{}) {
   constexpr int kCpt = kMaxTiles / kBlock;  // tiles per thread, at most
   float *zbuf = sl.zbuf;
   float *red_max = sl.red_max, *red_sum = sl.red_sum;
@@ -83,15 +98,37 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
       Acur = reinterpret_cast<const T *>(p.W1) + (int64_t)min(max(p.a_tokens[rho], 0), V - 1) * r;
     uint4 a = make_uint4(0, 0, 0, 0);
     if (stage_arow && tid < pieces) a = *reinterpret_cast<const uint4 *>(Acur + tid * kPer);
-    const float2 *ts = p.tile_stats + (int64_t)rho * nT;
+    if constexpr (kPersist) {
+      // poll the words not yet written (all in flight at once), then reset them
+      uint64_t *ts = io.tiles + (int64_t)rho * nT;
+      uint64_t v[kCpt];
+      unsigned missing = 0;
 #pragma unroll
-    for (int j = 0; j < kCpt; ++j) {
-      if (kCoherent) {
-        const uint64_t v = t0 + j < t1 ? ld_coherent(ts + t0 + j) : 0ull;
-        pt[j] = t0 + j < t1 ? __builtin_bit_cast(float2, v) : make_float2(-INFINITY, 0.0f);
-      } else {
-        pt[j] = t0 + j < t1 ? ts[t0 + j] : make_float2(-INFINITY, 0.0f);
+      for (int j = 0; j < kCpt; ++j)
+        if (t0 + j < t1) missing |= 1u << j;
+      for (int spins = 0; missing != 0u; ++spins) {
+        if (spins > kSpinLimit) {
+          *io.abort = 1;
+          flag_error(p.err, kErrSync);
+          break;
+        }
+        if (spins > 0) __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j)
+          if (missing & (1u << j)) v[j] = ld_coherent(ts + t0 + j);
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j)
+          if ((missing & (1u << j)) && v[j] != kTileEmpty) missing &= ~(1u << j);
       }
+#pragma unroll
+      for (int j = 0; j < kCpt; ++j) {
+        pt[j] = t0 + j < t1 ? __builtin_bit_cast(float2, v[j]) : make_float2(-INFINITY, 0.0f);
+        if (t0 + j < t1) st_coherent(ts + t0 + j, kTileEmpty);
+      }
+    } else {
+      const float2 *ts = p.tile_stats + (int64_t)rho * nT;
+#pragma unroll
+      for (int j = 0; j < kCpt; ++j) pt[j] = t0 + j < t1 ? ts[t0 + j] : make_float2(-INFINITY, 0.0f);
     }
     // the draw's uniform (a scalar Philox chain) is formed while the loads
     // are in flight: the LDS store keeps it ahead of the first barrier
@@ -106,6 +143,7 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
   lm = wave_max(lm);
   if (lane == 0) red_max[wave] = lm;
   __syncthreads();
+  if (kPersist && *io.abort != 0) return false;
   const float m = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
   float w[kCpt];
   float ls = 0.0f;
@@ -172,8 +210,11 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
 
   // 4. recompute z of that tile, bit-identical to the fused kernel
   const T *Urow = reinterpret_cast<const T *>(p.U) + slot * V;
-  recompute_tile_v<T, true>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar, rho & 31,
-                            zbuf);
+  recompute_tile_v<T, true, KS>(arow, reinterpret_cast<const T *>(p.W2), Urow, V, r, tstar,
+                                rho & 31, zbuf);
+  // persistent: every wave's partial resets have completed before the draw is
+  // published (the step two later writes those words again)
+  if (kPersist) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // 5. scan inside the tile (wave 0, two columns per lane, left to right);
@@ -202,6 +243,8 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
     }
     const float zp = __shfl(pick & 1 ? z1 : z0, pick >> 1);
     const int xk = tstar * kTileN + pick;  // in [0, V): a picked column has positive mass
+    if (kPersist && lane == 0)  // first: the other workgroups wait for it
+      st_coherent(io.pub + rho, ((uint64_t)k << 32) | (uint32_t)min(max(xk, 0), V - 1));
     if (lane == 0) {
       p.x[slot] = finite ? xk : -1;
       p.q_stats[2 * slot] = m;
@@ -216,12 +259,7 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
       T *dst = reinterpret_cast<T *>(A_next) + (int64_t)rho * r + lane * kPer;
       const uint4 w = *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(p.W1) +
                                                        (int64_t)xc * r + lane * kPer);
-      if (kCoherent) {
-        st_coherent(dst, (uint64_t)w.x | ((uint64_t)w.y << 32));
-        st_coherent(reinterpret_cast<char *>(dst) + 8, (uint64_t)w.z | ((uint64_t)w.w << 32));
-      } else {
-        *reinterpret_cast<uint4 *>(dst) = w;
-      }
+      *reinterpret_cast<uint4 *>(dst) = w;
     }
 
   }
@@ -241,6 +279,7 @@ __device__ __forceinline__ void sample_row(const SampleParams &p, int k, void *A
       p.c[slot] = 1.0f / (1.0f + expf(-s / tk));
     }
   }
+  return true;
 }
 
 }  // namespace dspark

@@ -146,8 +146,9 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
  * dspark_draft for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, kernels and results as dspark_draft; the
- * draft's scratch (tile partials R * ceil(V/128) * 8 bytes, the head's dot
- * products, two transition-row buffers) lives in a static device array of
+ * draft's scratch (two halves of tile partials, 2 * R * ceil(V/128) * 8
+ * bytes, the head's dot products, two transition-row buffers, R published
+ * draws) lives in a static device array of
  * DSPARK_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
  * until the process ends.  The call allocates nothing (no hipMalloc, no
  * workspace); its first call on a GPU looks up that GPU's copy of the array.
@@ -159,7 +160,7 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
  * enqueue nothing.  All calls on one GPU share the array: calls whose kernels
  * may overlap on one GPU (other streams, other host threads) race and must be
  * ordered by the caller. */
-#define DSPARK_NOALLOC_SCRATCH_BYTES (8u << 20)
+#define DSPARK_NOALLOC_SCRATCH_BYTES (16u << 20)
 size_t dspark_draft_noalloc_scratch(int R, int gamma, int V);
 dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
                                    const void *U, const void *W1, const void *W2,
