@@ -422,7 +422,43 @@ def main():
         ds.dspark_trace_enable(False)
         kr = ds.trace_summary()
         gru_ms, gru_n = kr.get("gru_step", (float("nan"), 1))
+        # many rounds of decoding with a prefix-dependent synthetic target and the
+        # loop's own acceptance history as confidences (asynchronous top-K: the
+        # history two rounds old sets the capacity); V is small so that the
+        # host-side target forward stays cheap
+        from draft_sampling_verification_03_amd.decode import decode
+        ml = synth.MarkovLoop(R=R, gamma=gamma, V=4096, r=16, dtype=synth.BF16, sps="smooth",
+                              mode=synth.SCHED_ASYNC_TOPK)
+        mt = synth.markov_target(ml)
+        mW1, mW2 = synth.markov_draft_head(ml, mt)
+        msps = synth.markov_sps(ml)
+        n_loop = 48
+        w_loop = time.perf_counter()
+        lo = decode(n_loop, synth.markov_anchors(ml), up(mW1), up(mW2),
+                    lambda t: up(synth.markov_U(ml, mt, t)),
+                    lambda prev: up(synth.markov_target_rows(ml, mt, prev)),
+                    SPS=up(msps), mode=ml.mode, history=(4.0, 1.0), temp=ml.temp, seed=ml.seed)
+        w_loop = time.perf_counter() - w_loop
+        assert lo["device_errors"] == (0, 0, 0), "device error word set in the decode loop"
+        settled = slice(n_loop // 3, None)
+        Bs = R + lo["ell"].sum(axis=1)
+        loop_rows = {
+            "workload": f"Markov-target loop R={R} gamma={gamma} V=4096 r=16 bf16, asynchronous "
+                        f"top-K on the loop's acceptance history, SPS(B) = 60*1024/(1024+B)",
+            "rounds": n_loop, "settled_from_round": n_loop // 3,
+            "tokens_per_request_round_realized": round(float(lo["tau_real"][settled].mean() / R), 4),
+            "tokens_per_request_round_predicted": round(float(lo["tau_pred"][settled].mean() / R), 4),
+            "realized_over_predicted": round(float(lo["tau_real"][settled].sum()
+                                                   / lo["tau_pred"][settled].sum()), 4),
+            "realized_tau_sps": round(float((lo["tau_real"] * msps[Bs])[settled].mean()), 1),
+            "predicted_theta": round(float(lo["theta"][settled].mean()), 1),
+            "mean_ell": round(float(lo["ell"][settled].mean()), 3),
+            "conditional_acceptance": [None if np.isnan(v) else round(float(v), 4)
+                                       for v in lo["cond_accept"]],
+            "wall_ms_per_round_incl_host_target": round(w_loop / n_loop * 1e3, 1),
+        }
         next_rows = {
+            "decode_loop": loop_rows,
             "rnn_head": {"ms_per_round": round(ms_rnn, 4),
                          "positions_per_s": round(R * gamma / (ms_rnn / 1e3), 1),
                          "verify_rows": R * (gamma + 1), "gru_step_us": round(gru_ms / gru_n * 1e3, 3),
@@ -431,7 +467,10 @@ def main():
                              "positions_per_s": round(R * gamma / (ms_train / 1e3), 1)},
         }
         print(f"[bench] next rows: recurrent-head round {ms_rnn:.3f} ms, "
-              f"training reductions {ms_train:.3f} ms", file=sys.stderr, flush=True)
+              f"training reductions {ms_train:.3f} ms; decode loop tokens/request/round "
+              f"{loop_rows['tokens_per_request_round_realized']} realized vs "
+              f"{loop_rows['tokens_per_request_round_predicted']} predicted", file=sys.stderr,
+              flush=True)
 
     # ---- algorithmic work per launch of each kernel (the method's bytes: every
     #      input read once per call; W2 once per draft call, i.e. 1/gamma of it

@@ -227,6 +227,53 @@ def schedule_bruteforce(c, SPS):
     return best, ell
 
 
+def acceptance_counts(ell_rounds, n_acc_rounds, gamma):
+    """Per request and draft position k = 1..gamma, over past rounds: the rounds
+    in which position k was verified (k <= ell and all k - 1 before it were
+    accepted, so verification reached it) and those in which it was accepted
+    (k <= n_acc).  These are the numerator and denominator of the conditional
+    acceptance P(A_k | A_1..A_{k-1}) (Blog, "Conditional acceptance curves").
+    Plain loops: one round, request and position at a time."""
+    R = len(ell_rounds[0]) if len(ell_rounds) else 0
+    verified = [[0] * gamma for _ in range(R)]
+    accepted = [[0] * gamma for _ in range(R)]
+    for ell, n_acc in zip(ell_rounds, n_acc_rounds):
+        for rho in range(R):
+            for k in range(1, gamma + 1):
+                reached = k <= int(ell[rho]) and int(n_acc[rho]) >= k - 1
+                if reached:
+                    verified[rho][k - 1] += 1
+                    if int(n_acc[rho]) >= k:
+                        accepted[rho][k - 1] += 1
+    return verified, accepted
+
+
+def acceptance_estimates(ell_rounds, n_acc_rounds, R, gamma, alpha=4.0, beta=1.0):
+    """[R][gamma] float32 confidences from a loop's own history: the conditional
+    acceptance of each (request, position) with a Beta(alpha, beta) prior,
+    (accepted + alpha) / (verified + alpha + beta), in float64 rounded once.
+    With no past round every entry is alpha / (alpha + beta)."""
+    c = np.full((R, gamma), alpha / (alpha + beta), dtype=np.float64)
+    if len(ell_rounds):
+        verified, accepted = acceptance_counts(ell_rounds, n_acc_rounds, gamma)
+        for rho in range(R):
+            for k in range(gamma):
+                c[rho, k] = (accepted[rho][k] + alpha) / (verified[rho][k] + alpha + beta)
+    return c.astype(np.float32)
+
+
+def conditional_acceptance_curve(ell_rounds, n_acc_rounds, gamma):
+    """P(A_k | A_1..A_{k-1}) for k = 1..gamma over all requests and rounds (nan
+    where position k was never verified)."""
+    verified, accepted = acceptance_counts(ell_rounds, n_acc_rounds, gamma)
+    out = []
+    for k in range(gamma):
+        v = sum(row[k] for row in verified)
+        a = sum(row[k] for row in accepted)
+        out.append(a / v if v else float("nan"))
+    return np.array(out)
+
+
 # --------------------------------------------------------------------- verify
 def verify_request(P_req, U_req, W1, W2, x0, x, ell, seed, rnd, rho, temp=1.0, force_n=-1,
                    want_cdf=False, A_rows=None):

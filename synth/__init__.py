@@ -343,9 +343,14 @@ def markov_anchors(m: MarkovLoop) -> np.ndarray:
 
 
 def markov_sps(m: MarkovLoop) -> np.ndarray:
+    """SPS(B) tables: "tiny" falls steeply (few drafts pay), "knee" at a rate
+    where admitting a candidate pays only when its survival is moderate, and
+    the default is nearly flat (every draft pays)."""
     B = np.arange(m.B_max + 1, dtype=np.float64)
     if m.sps == "tiny":
         return 100.0 / (1.0 + B / 8.0)
+    if m.sps == "knee":
+        return 100.0 / (1.0 + B / 48.0)
     return 60.0 * 1024.0 / (1024.0 + B)
 
 

@@ -52,21 +52,31 @@ def pit_pvalue(m, target, anchors, streams, bins=20, seed=3):
     return pit_pvalue_pairs(m, target, stream_pairs(anchors, streams), bins, seed)
 
 
-def oracle_decode(m, rounds):
-    """The multi-round loop with the oracle: the reference for decode.py."""
+def oracle_decode(m, rounds, history=None):
+    """The multi-round loop with the oracle: the reference for decode.py.  With
+    history = (alpha, beta) the confidences are the loop's own conditional
+    acceptance estimates (rounds before t; the asynchronous mode's history is
+    the estimate of round t - 2, the prior alone before round 2)."""
     target = synth.markov_target(m)
     W1, W2 = synth.markov_draft_head(m, target)
     sps = synth.markov_sps(m)
     anchors = synth.markov_anchors(m).copy()
     streams = [[] for _ in range(m.R)]
-    rec = dict(x=[], ell=[], n_acc=[], y=[])
+    rec = dict(x=[], ell=[], n_acc=[], y=[], c=[], tau_pred=[], tau_real=[])
     for t in range(rounds):
         U = synth.markov_U(m, target, t)
         x = np.stack([oracle.draft_request(U[rho], W1, W2, int(anchors[rho]), m.seed, t, rho,
                                            temp=m.temp)["x"] for rho in range(m.R)])
-        c = synth.markov_confidences(m, t)
-        cp = synth.markov_confidences(m, t - 2) if m.mode == synth.SCHED_ASYNC_TOPK else None
-        ell = oracle.schedule(c, sps, m.mode, c_prev2=cp)["ell"]
+        if history is not None:
+            c = oracle.acceptance_estimates(rec["ell"], rec["n_acc"], m.R, m.gamma, *history)
+            cp = (oracle.acceptance_estimates(rec["ell"][: max(t - 2, 0)], rec["n_acc"][: max(t - 2, 0)],
+                                              m.R, m.gamma, *history)
+                  if m.mode == synth.SCHED_ASYNC_TOPK else None)
+        else:
+            c = synth.markov_confidences(m, t)
+            cp = synth.markov_confidences(m, t - 2) if m.mode == synth.SCHED_ASYNC_TOPK else None
+        sch = oracle.schedule(c, sps, m.mode, c_prev2=cp)
+        ell = sch["ell"]
         n = np.zeros(m.R, dtype=np.int32)
         y = np.zeros((m.R, m.gamma + 1), dtype=np.int32)
         for rho in range(m.R):
@@ -77,8 +87,14 @@ def oracle_decode(m, rounds):
             n[rho], y[rho] = v["n_acc"], v["y"]
             streams[rho].extend(int(tok) for tok in y[rho, : n[rho] + 1])
             anchors[rho] = y[rho, n[rho]]
-        for k, val in (("x", x), ("ell", ell), ("n_acc", n), ("y", y)):
+        for k, val in (("x", x), ("ell", ell), ("n_acc", n), ("y", y), ("c", c)):
             rec[k].append(val)
+        # survival: each request emits 1 + (accepted drafts); the schedule
+        # predicts 1 + sum of a_rk over its admitted depths
+        kk = np.arange(1, m.gamma + 1)[None, :]
+        rec["tau_pred"].append(float(m.R + np.where(kk <= ell[:, None], sch["a"].astype(np.float64),
+                                                     0.0).sum()))
+        rec["tau_real"].append(int((n + 1).sum()))
     return {k: np.asarray(v) for k, v in rec.items()}, streams
 
 
@@ -120,7 +136,72 @@ def test_law_test_rejects_unverified_drafts():
     assert p < 1e-6, f"the draft's law passed as the target's: p = {p}, {n} tokens"
 
 
-def _gpu_loop(m, rounds):
+def test_conditional_acceptance_curve_worked_example():
+    """The conditional acceptance of position 2 is counted over the blocks in
+    which position 1 survived (Blog, "Conditional acceptance curves": of 100
+    blocks, position 1 survives 80 times and position 2 60 times, so
+    P(A_2 | A_1) = 60 / 80 = 0.75, not 0.60)."""
+    from draft_sampling_verification_03_amd.decode import AcceptanceHistory
+    ell = [np.array([2])] * 100
+    n_acc = [np.array([0])] * 20 + [np.array([1])] * 20 + [np.array([2])] * 60
+    assert np.allclose(oracle.conditional_acceptance_curve(ell, n_acc, 2), [0.80, 0.75])
+    h = AcceptanceHistory(1, 2)
+    for e, n in zip(ell, n_acc):
+        h.record(e, n)
+    assert np.allclose(h.curve(), [0.80, 0.75])
+    # with the Beta(4, 1) prior: (80 + 4) / (100 + 5), (60 + 4) / (80 + 5)
+    want = np.array([[84 / 105, 64 / 85]], dtype=np.float32)
+    assert np.array_equal(oracle.acceptance_estimates(ell, n_acc, 1, 2), want)
+    assert np.array_equal(h.confidences(), want)
+
+
+def test_acceptance_estimates_count_only_reached_positions():
+    """A position is counted only when verification reached it: k <= ell and
+    the k - 1 positions before it accepted.  Brute force on a few rounds of
+    three requests, by hand."""
+    from draft_sampling_verification_03_amd.decode import AcceptanceHistory
+    ell = [np.array([3, 2, 0]), np.array([2, 3, 3]), np.array([3, 0, 1])]
+    n_acc = [np.array([1, 2, 0]), np.array([2, 0, 3]), np.array([3, 0, 0])]
+    # request 0: pos 1 reached 3x accepted 3x; pos 2 reached 3x accepted 2x;
+    # pos 3 reached 1x (round 2) accepted 1x (round 0 stopped at pos 2,
+    # round 1 had ell = 2)
+    # request 1: pos 1 reached 2x (rounds 0, 1) accepted 1x; pos 2 reached 1x
+    # accepted 1x; pos 3 never (round 1 rejected position 1)
+    # request 2: pos 1 reached 2x (rounds 1, 2) accepted 1x; pos 2 and 3
+    # reached 1x each (round 1) and accepted
+    verified = [[3, 3, 1], [2, 1, 0], [2, 1, 1]]
+    accepted = [[3, 2, 1], [1, 1, 0], [1, 1, 1]]
+    v, a = oracle.acceptance_counts(ell, n_acc, 3)
+    assert v == verified and a == accepted
+    h = AcceptanceHistory(3, 3, alpha=1.0, beta=1.0)
+    for e, n in zip(ell, n_acc):
+        h.record(e, n)
+    assert np.array_equal(h.tried, verified) and np.array_equal(h.passed, accepted)
+    want = ((np.array(accepted) + 1.0) / (np.array(verified) + 2.0)).astype(np.float32)
+    assert np.array_equal(oracle.acceptance_estimates(ell, n_acc, 3, 3, 1.0, 1.0), want)
+
+
+def test_oracle_loop_history_predicts_realized_tokens():
+    """Prefix survival (Blog, "Prefix survival and accepted length"): a round
+    emits 1 + c_1 + c_1 c_2 + ... tokens per request in expectation when the
+    c_k are the conditional acceptances.  With the loop's own estimates as
+    confidences (asynchronous top-K, history two rounds old), the schedule's
+    predicted tokens sum_r (1 + sum_{k <= ell_r} a_rk) match the realized
+    sum_r (n_acc_r + 1) over many rounds once the estimates have settled."""
+    m = synth.MarkovLoop(R=16, gamma=4, V=64, r=16, mode=synth.SCHED_ASYNC_TOPK, sps="knee")
+    rec, streams = oracle_decode(m, 160, history=(4.0, 1.0))
+    pred, real = rec["tau_pred"][40:].sum(), rec["tau_real"][40:].sum()
+    assert abs(real / pred - 1.0) < 0.05, (real, pred)
+    # the schedule really varies the lengths (every depth is reached), and the
+    # history is the loop's own
+    assert rec["ell"].std() > 0.3 and rec["ell"].max() == m.gamma
+    assert not np.allclose(rec["c"][-1], rec["c"][0])
+    # lossless under the adaptive schedule too
+    p, n = pit_pvalue(m, synth.markov_target(m), synth.markov_anchors(m), streams)
+    assert p > 1e-3, f"stream law rejected: p = {p}, {n} tokens"
+
+
+def _gpu_loop(m, rounds, history=None):
     import torch
     import draft_sampling_verification_03_amd as ds
     from draft_sampling_verification_03_amd.decode import decode
@@ -136,7 +217,7 @@ def _gpu_loop(m, rounds):
                  lambda t: up(synth.markov_U(m, target, t)),
                  lambda prev: up(synth.markov_target_rows(m, target, prev)),
                  SPS=up(synth.markov_sps(m)), mode=m.mode,
-                 conf_of_round=lambda t: up(synth.markov_confidences(m, t)),
+                 conf_of_round=lambda t: up(synth.markov_confidences(m, t)), history=history,
                  temp=m.temp, seed=m.seed)
     assert out["device_errors"] == (0, 0, 0)
     return out
@@ -160,4 +241,32 @@ def test_decode_loop_stream_law_on_gpu():
     g = _gpu_loop(m, 60)
     p, n = pit_pvalue(m, synth.markov_target(m), synth.markov_anchors(m), g["streams"])
     assert n > 8000
+    assert p > 1e-3, f"stream law rejected: p = {p}, {n} tokens"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [synth.SCHED_EARLY_STOP, synth.SCHED_ASYNC_TOPK])
+def test_decode_loop_with_history_matches_oracle(mode):
+    """The loop whose confidences are its own acceptance history: the library's
+    loop and the oracle's emit the same drafts, lengths, acceptances and tokens
+    and schedule with the same confidences, round after round."""
+    m = synth.MarkovLoop(R=8, gamma=4, V=256, r=16, mode=mode, sps="knee")
+    rounds = 16
+    g = _gpu_loop(m, rounds, history=(4.0, 1.0))
+    o, _ = oracle_decode(m, rounds, history=(4.0, 1.0))
+    for t in range(rounds):
+        for k in ("x", "ell", "n_acc", "y", "c", "tau_real"):
+            assert np.array_equal(g[k][t], o[k][t]), f"round {t}: {k} differs"
+        assert abs(g["tau_pred"][t] - o["tau_pred"][t]) <= 1e-5 * o["tau_pred"][t]
+    assert np.allclose(g["cond_accept"],
+                       oracle.conditional_acceptance_curve(o["ell"], o["n_acc"], m.gamma),
+                       equal_nan=True)
+
+
+@pytest.mark.gpu
+def test_decode_loop_with_history_stream_law_on_gpu():
+    m = synth.MarkovLoop(R=64, gamma=4, V=256, r=16, sps="knee", mode=synth.SCHED_ASYNC_TOPK)
+    g = _gpu_loop(m, 80, history=(4.0, 1.0))
+    p, n = pit_pvalue(m, synth.markov_target(m), synth.markov_anchors(m), g["streams"])
+    assert n > 7000
     assert p > 1e-3, f"stream law rejected: p = {p}, {n} tokens"
