@@ -477,10 +477,10 @@ def main():
     #      per draft-step launch, and once per verify call)
     work = {
         "bias_tile_draft": dict(bytes=R * V * s_el + r * V * s_el / gamma + R * r * s_el,
-                                flops=2.0 * R * r * V, bound="mfma"),
+                                flops=2.0 * R * r * V, bound="roofline"),
         # all gamma steps in one launch: U once, W2 once, the transition rows
         "draft_persistent": dict(bytes=R * gamma * V * s_el + r * V * s_el + R * gamma * r * s_el,
-                                 flops=2.0 * R * r * V * gamma, bound="mfma"),
+                                 flops=2.0 * R * r * V * gamma, bound="roofline"),
         "persist_clear": dict(bytes=0, flops=0.0, bound="latency"),
         "draft_sample": dict(bytes=R * nT * 8, flops=0.0, bound="latency"),
         "head_hidden_dot": dict(bytes=R * gamma * cfg.d * s_el, flops=2.0 * R * gamma * cfg.d,
@@ -488,12 +488,18 @@ def main():
         "schedule": dict(bytes=R * gamma * 4 * 2, flops=0.0, bound="latency"),
         "row_chunk_stats": dict(bytes=rows_used * V * s_el, flops=0.0, bound="hbm"),
         "bias_tile_verify": dict(bytes=2 * sum_ell * V * s_el + r * V * s_el,
-                                 flops=2.0 * sum_ell * r * V, bound="hbm"),
+                                 flops=2.0 * sum_ell * r * V, bound="roofline"),
         "verify_finalize": dict(bytes=sum_ell * nT * 8 + R * nT * 8, flops=0.0, bound="latency"),
         "overlap_chunk": dict(bytes=2 * n_ov * V * s_el, flops=0.0, bound="hbm"),
         "overlap_combine": dict(bytes=n_ov * 20, flops=0.0, bound="latency"),
     }
     peak_mfma = PEAK_BF16_TFLOPS if cfg.dtype == synth.BF16 else PEAK_F32_MFMA_TFLOPS
+    for w in work.values():
+        # a product is bound by whichever floor is higher: its bytes at peak HBM
+        # or its flops at peak MFMA (intensity against the ridge of 312 flop/B)
+        if w["bound"] == "roofline":
+            w["bound"] = ("mfma" if w["flops"] / (peak_mfma * 1e12) >= w["bytes"] / (PEAK_HBM_GBPS * 1e9)
+                          else "hbm")
     kernels = {}
     for name, (ms, n) in list(kern.items()) + list(kern_ov.items()):
         w = work.get(name, dict(bytes=0, flops=0.0, bound="latency"))
@@ -526,6 +532,7 @@ def main():
             roof["traffic"] = tr.get("bytes_per_launch")
     roof.update(kernel=dom, avg_us=dk["avg_us"], algorithmic_bytes=dk["bytes_per_launch"],
                 flops_per_launch=dk["flops_per_launch"], hbm_frac=dk["hbm_frac"],
+                mfma_frac=dk.get("mfma_frac"),
                 traffic_over_algorithmic=(round(roof["traffic"] / dk["bytes_per_launch"], 3)
                                           if roof["traffic"] else None))
 
