@@ -250,9 +250,12 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         for (int c = 1; c < 16; ++c) bm = fmaxf(bm, v[c]);
         float s = 0.0f;
         if (!kMask || bm != -INFINITY) {
-          const float nb = -bm * cl;
+          // (v - max) first: exact near the maximum, where the mass is; one
+          // fused multiply-add with -max * log2(e) / T rounded would shift
+          // every term by up to half an ulp of that product (~1e-6 relative
+          // at |max| ~ 40), enough to lift a q(x) near 1 above 1 + 1e-6
 #pragma unroll
-          for (int c = 0; c < 16; ++c) s += exp2_fast(fmaf(v[c], cl, nb));
+          for (int c = 0; c < 16; ++c) s += exp2_fast((v[c] - bm) * cl);
         }
         // the other 16 columns of the row are in lane l ^ 32
         // (both lanes of a row form the same sum: their operands are swapped

@@ -45,9 +45,10 @@ struct RowStatsParams {
 //     two passes, then one workgroup reduction;
 //   - the last row of a request (its bonus position): (max, sum of exp) per
 //     128-column tile as well, kept for the bonus draw.
-// exp(x / T - m) is formed as 2^(x log2(e) / T - x_max log2(e) / T) with one
-// fused multiply-add per element (4% faster than subtracting first), with
-// m = x_max / T exactly (T > 0).
+// exp(x / T - m) is formed as 2^((x - x_max) log2(e) / T), with m = x_max / T
+// exactly (T > 0): x - x_max is exact near the maximum, where the mass is (a
+// single fused multiply-add with x_max log2(e) / T rounded was 4% faster but
+// shifts every term by up to half an ulp of that product).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams p) {
   __shared__ float red[8];
@@ -145,7 +146,6 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
       }
       if (bm != -INFINITY) {
         const float mn = fmaxf(M, bm);
-        const float nb = -mn * cl;
         float sb = 0.0f;
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
           const bool in = p0 + j * kBlock + tid < npc;
           float e = 0.0f;
 #pragma unroll
-          for (int q = 0; q < kPer; ++q) e += exp2_fast(fmaf(x[q], cl, nb));
+          for (int q = 0; q < kPer; ++q) e += exp2_fast((x[q] - mn) * cl);
           sb += in ? e : 0.0f;
         }
         S = fmaf(S, exp2_fast((M - mn) * cl), sb);

@@ -133,6 +133,27 @@ def test_full_size_config(cid):
     print(f"config {cid}: sum ell={int(g['ell'].sum())} n*={g['n_admitted']} {stats}", flush=True)
 
 
+def test_persistent_draft_peaky_logits_ragged_rows():
+    """The single-launch draft (bf16, r = 256, R <= 128) on the stress
+    workload's peaky logits (target sd 8, draft noise sd up to 4) with a
+    partly filled last row block (R = 100): every q(x) stays in (0, 1], and
+    the draws, q(x) and normalizers of sampled requests match the oracle."""
+    cfg = synth.Config(cid=16, name="peaky-r100", R=100, gamma=6, V=151936, r=256,
+                       dtype=synth.BF16, target_sd=8.0, noise="uniform:0.1:4", weight_sd=0.02,
+                       conf="sigmoid:2:1.5", sps="smooth", mode=synth.SCHED_EARLY_STOP)
+    inp = inputs(cfg)
+    stats = new_stats()
+    g = run_round(inp)
+    check_properties(inp, g)
+    check_schedule(inp, g)
+    for rho in (0, 31, 32, 63, 96, 99):
+        for k in range(1, cfg.gamma + 1):
+            check_draft_position(inp, g, rho, k, stats)
+    for rho in (0, 57, 99):
+        check_verify_request(inp, g, rho, stats)
+    print(f"peaky R=100: {stats}", flush=True)
+
+
 @pytest.mark.parametrize("cid", [1, 3])
 def test_tv_overlap_against_oracle(cid):
     inp = inputs(cid)
