@@ -133,6 +133,16 @@ typedef enum {
  *   q_stats [R][gamma][2] (m, S) of z_k, so q_k(v) = exp(z_k(v) - m) / S, fp32
  *   q_x     [R][gamma]    q_k(x_k), fp32
  *   c       [R][gamma]    confidences c_k, written iff h != NULL (may be NULL otherwise)
+ * Execution: with bf16, r = 256, R <= 128 and at most 5 vocabulary tiles of
+ * 128 per compute unit, all gamma steps run in one cooperative launch of one
+ * workgroup per compute unit that keeps W2 on chip for the call; its
+ * workgroups exchange tile partials and draws through the workspace with
+ * device-coherent accesses and bounded waits (a wait that runs out sets
+ * DSPARK_DEVERR_SYNC and the outputs are incomplete).  If the device refuses
+ * the cooperative launch, or DSPARK_PERSISTENT_DRAFT=0 is set in the
+ * environment, gamma launches of the per-step kernels run instead.  Both
+ * follow the same law; they sum the tile partials in different orders, so a
+ * draw whose uniform falls within rounding of a CDF boundary may differ.
  * Workspace: dspark_draft_workspace(R, gamma, V, r, dt) bytes. */
 size_t dspark_draft_workspace(int R, int gamma, int V, int r, dspark_dtype dt);
 dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, float temp,
