@@ -157,16 +157,23 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   }
 
   // ---- U of item (row block rb, tile slot i) at step k: this lane's 16
-  //      columns of its row (two 16-byte pieces; a piece is wholly inside or
-  //      outside [0, V) because V % 8 == 0)
+  //      columns of its row, two 16-byte pieces, each clamped on its own (a
+  //      piece is wholly inside or outside [0, V) because V % 8 == 0, but the
+  //      two pieces of a lane straddle V when V % 16 == 8)
   struct UPiece { u32x4 a, b; };
   auto load_u = [&](int k, int rb, int i, int m, int half) __attribute__((always_inline)) {
     const int rho = min(rb * kRowsPerWave + m, R - 1);
-    const int c0 = min((t0 + i) * kTileN + wave * kBlockCols + half * 16, V - 16);
-    const bf16_t *src = p.U + ((int64_t)rho * gamma + (k - 1)) * V + c0;
+    const int c0 = (t0 + i) * kTileN + wave * kBlockCols + half * 16;
+    const bf16_t *row = p.U + ((int64_t)rho * gamma + (k - 1)) * V;
     UPiece u;
-    u.a = *reinterpret_cast<const u32x4 *>(src);
-    u.b = *reinterpret_cast<const u32x4 *>(src + 8);
+    if constexpr (kMask) {
+      u.a = *reinterpret_cast<const u32x4 *>(row + min(c0, V - 8));
+      u.b = *reinterpret_cast<const u32x4 *>(row + min(c0 + 8, V - 8));
+    } else {  // V % 128 == 0: a lane's 16 columns are all inside or all outside
+      const int cc = min(c0, V - 16);
+      u.a = *reinterpret_cast<const u32x4 *>(row + cc);
+      u.b = *reinterpret_cast<const u32x4 *>(row + cc + 8);
+    }
     return u;
   };
   // the U ring holds one row block of items ahead; item i is tile slot slot_of(i)

@@ -77,6 +77,14 @@ def test_tiny_config_other_rounds(rnd):
     dict(R=4, gamma=4, V=1024, r=128),              # fp32 rank limit
     dict(R=5, gamma=64, V=1024),                    # the longest block
     dict(R=128, gamma=64, V=264),                   # the largest candidate count, 8192
+    # the single-launch draft (bf16, r = 256): a masked last tile, fewer
+    # workgroups than requests (each draws several), one request, a partly
+    # filled last row block, and five tiles per workgroup with a masked one
+    dict(R=3, gamma=4, V=1000, dtype=synth.BF16, r=256, weight_sd=0.05),
+    dict(R=10, gamma=3, V=384, dtype=synth.BF16, r=256, weight_sd=0.05),
+    dict(R=1, gamma=5, V=2056, dtype=synth.BF16, r=256, weight_sd=0.05),
+    dict(R=97, gamma=2, V=4000, dtype=synth.BF16, r=256, weight_sd=0.05),
+    dict(R=4, gamma=2, V=131848, dtype=synth.BF16, r=256, weight_sd=0.02),
 ])
 def test_edge_shapes(over):
     cfg = synth.make_config(1, cid=50 + len(_cache), **over)
