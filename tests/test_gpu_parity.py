@@ -85,6 +85,8 @@ def test_tiny_config_other_rounds(rnd):
     dict(R=1, gamma=5, V=2056, dtype=synth.BF16, r=256, weight_sd=0.05),
     dict(R=97, gamma=2, V=4000, dtype=synth.BF16, r=256, weight_sd=0.05),
     dict(R=4, gamma=2, V=131848, dtype=synth.BF16, r=256, weight_sd=0.02),
+    dict(R=2, gamma=1, V=1024, dtype=synth.BF16, r=256, weight_sd=0.05),
+    dict(R=7, gamma=3, V=2048, dtype=synth.BF16, r=256, weight_sd=0.05, temp=0.6),
 ])
 def test_edge_shapes(over):
     cfg = synth.make_config(1, cid=50 + len(_cache), **over)
@@ -243,16 +245,17 @@ def test_verify_output_law_chi2_on_gpu():
 
 # ----------------------------------------------- next rows: STS and thresholds
 @pytest.mark.gpu
-@pytest.mark.parametrize("dtype", [np.float32, "bf16"])
-def test_confidence_head_position_temperatures(dtype):
+@pytest.mark.parametrize("dtype,r", [(np.float32, 16), ("bf16", 16), ("bf16", 256)])
+def test_confidence_head_position_temperatures(dtype, r):
     """c_k = sigmoid(z_k / T_k) against the oracle's head at the GPU's tokens;
-    a temperature that is not a finite positive number is flagged and taken as 1."""
+    a temperature that is not a finite positive number is flagged and taken as 1.
+    (bf16 with r = 256 runs the single-launch draft.)"""
     rng = np.random.default_rng(21)
-    R, gamma, V, r, d = 16, 5, 512, 16, 64
+    R, gamma, V, d = 16, 5, 512, 64
     store = (lambda a: synth.to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
     U = store(rng.standard_normal((R, gamma, V)).astype(np.float32))
-    W1 = store((0.3 * rng.standard_normal((V, r))).astype(np.float32))
-    W2 = store((0.3 * rng.standard_normal((V, r))).astype(np.float32))
+    W1 = store((0.3 * rng.standard_normal((V, r)) * np.sqrt(16 / r)).astype(np.float32))
+    W2 = store((0.3 * rng.standard_normal((V, r)) * np.sqrt(16 / r)).astype(np.float32))
     h = store(rng.standard_normal((R, gamma, d)).astype(np.float32))
     w = (0.2 * rng.standard_normal(d + r)).astype(np.float32)
     x0 = rng.integers(0, V, R).astype(np.int32)
