@@ -176,8 +176,9 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
     }
     return u;
   };
-  // the U ring holds one row block of items ahead; item i is tile slot slot_of(i)
-  auto slot_of = [](int i) { return i == 0 ? NT - 1 : i - 1; };
+  // the U ring holds one row block of items ahead; item i is tile slot i (the
+  // last slot, held in LDS, comes last)
+  auto slot_of = [](int i) { return i; };
   UPiece ur[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, slot_of(i), m, half);
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
     __syncthreads();
 
     // ---- 2. products and epilogues, row block by row block.  Item i of a
-    //      row block is tile slot slot_of(i): the LDS-held slot first, so that
-    //      its operand reads are in flight together with the rows'
+    //      row block is tile slot i: the register-held slots first (the first
+    //      products wait only for the rows' LDS reads), the LDS-held slot last
     for (int rb = 0; rb < nrb; ++rb) {
       u16x8 bfr[kPKS];
       {
@@ -226,13 +227,13 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
 #pragma unroll
         for (int ks = 0; ks < kPKS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8 *>(rowp + ks * 16);
       }
-      // products of item i >= 1 (W2 from registers)
+      // products of item i < NT - 1 (W2 from registers)
       auto mma = [&](int i) __attribute__((always_inline)) {
         floatx16 acc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < kPKS; ++ks) acc = mfma16<true>(w2r[i > 0 ? i - 1 : 0][ks], bfr[ks], acc);
+        for (int ks = 0; ks < kPKS; ++ks) acc = mfma16<true>(w2r[i < NT - 1 ? i : 0][ks], bfr[ks], acc);
         return acc;
       };
       // the next U of an item: the same tile slot one row block later, or
@@ -272,23 +273,29 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         const float S2 = s * exp2_fast((bm - M) * cl) + os * exp2_fast((om - M) * cl);
         sh.part[rb * kRowsPerWave + m_k][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
       };
-      // item 0 (the LDS-held slot): every operand read in flight before
-      // its first product
+      // item 0 from registers: its products wait only for the rows' reads;
+      // the LDS-held slot's operands are read one item ahead of its products
+      floatx16 acc0 = mma(0), acc1;
       u16x8 w2f[kPKS];
 #pragma unroll
-      for (int ks = 0; ks < kPKS; ++ks)
-        w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane_k]);
-      __builtin_amdgcn_sched_barrier(0);
-      floatx16 acc0, acc1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc0[e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < kPKS; ++ks) acc0 = mfma16<true>(w2f[ks], bfr[ks], acc0);
-#pragma unroll
       for (int i = 0; i < NT; ++i) {
+        if (i + 2 == NT) {
+#pragma unroll
+          for (int ks = 0; ks < kPKS; ++ks)
+            w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane_k]);
+        }
         if (i + 1 < NT) {
-          if (i & 1) acc0 = mma(i + 1);
-          else acc1 = mma(i + 1);
+          floatx16 nx;
+          if (i + 1 < NT - 1) {
+            nx = mma(i + 1);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) nx[e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < kPKS; ++ks) nx = mfma16<true>(w2f[ks], bfr[ks], nx);
+          }
+          if (i & 1) acc0 = nx;
+          else acc1 = nx;
         }
         epilogue(i, (i & 1) ? acc1 : acc0);
         // the epilogue of item i issues while the products of item i + 1 run
