@@ -22,7 +22,7 @@
 //      sequence as the per-step product kernel, so every z = acc + U is
 //      bit-identical to what the sampler recomputes), adds U_k and reduces
 //      each row's 32 columns to (max, sum of exp) in the epilogue, which runs
-//      while the next block's products issue;
+//      while the next tile slot's products issue;
 //   3. the four waves' block partials of a tile combine in a fixed order into
 //      the tile partial (m_t, s_t), stored as one 8-byte word in the half of
 //      the partial buffer that belongs to the step's parity;
@@ -176,12 +176,10 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
     }
     return u;
   };
-  // the U ring holds one row block of items ahead; item i is tile slot i (the
-  // last slot, held in LDS, comes last)
-  auto slot_of = [](int i) { return i; };
+  // the U ring holds one row block of items ahead (item i is tile slot i)
   UPiece ur[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, slot_of(i), m, half);
+  for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, i, m, half);
 
   for (int k = 1; k <= gamma; ++k) {
     // the thread's index, opaque to the compiler once per step: addresses
@@ -242,7 +240,7 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
       const int k_next = last_rb ? min(k + 1, gamma) : k;
       const int rb_next = last_rb ? 0 : rb + 1;
       auto epilogue = [&](int i, const floatx16 &acc) __attribute__((always_inline)) {
-        const int sl = slot_of(i);
+        const int sl = i;
         float v[16];
         unpack16(ur[i].a, (bf16_t *)nullptr, v);
         unpack16(ur[i].b, (bf16_t *)nullptr, v + 8);
