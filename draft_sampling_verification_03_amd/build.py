@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdspark.so")
 SOURCES = ["abi.cpp", "trace.cpp", "draft.hip", "draft_persistent.hip", "schedule.hip", "verify.hip",
-           "train.hip"]
+           "verify_stationary.hip", "train.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("DSPARK_OFFLOAD_ARCH", "gfx950")
 

@@ -254,6 +254,7 @@ static dspark_status verify_impl(int R, int gamma, int V, int r, dspark_dtype dt
   L.bonus_tiles = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
   L.pair_partials = (float2 *)carve(ws, &off, (size_t)R * gamma * n_tiles_of(V) * 8);
   L.row_map = (int4 *)carve(ws, &off, (size_t)R * gamma * 16);
+  L.row_stats = (float4 *)carve(ws, &off, (size_t)R * gamma * 16);
   L.A_rows = carve(ws, &off, (size_t)R * gamma * kMaxRowBytes);
   L.R = R; L.gamma = gamma; L.V = V; L.r = r; L.rows_capacity = rows_capacity;
   L.bf16 = dt == DSPARK_BF16; L.invT = 1.0f / temp; L.ell = ell; L.row_offset = row_offset;
@@ -328,6 +329,7 @@ dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype d
   L.bonus_tiles = (float2 *)carve(ws, &off, (size_t)R * n_tiles_of(V) * 8);
   L.pair_partials = (float2 *)carve(ws, &off, n * n_tiles_of(V) * 8);
   L.row_map = (int4 *)carve(ws, &off, n * 16);
+  L.row_stats = (float4 *)carve(ws, &off, n * 16);
   L.A_rows = carve(ws, &off, n * kMaxRowBytes);
   T.ell = (int32_t *)carve(ws, &off, ((size_t)R + 1) * 4);
   T.row_offset = (int32_t *)carve(ws, &off, ((size_t)R + 1) * 4);

@@ -138,22 +138,31 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   //      slot in LDS, where each lane keeps its own 16-byte pieces
   constexpr int kPRegTiles = NT - 1;
   u16x8 w2r[kPRegTiles][kPKS];
+  {
+    u16x8 w2f[kPKS];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int col = min((t0 + i) * kTileN + wave * kBlockCols + block_col_of_m(m), V - 1);
-    const bf16_t *src = p.W2 + (int64_t)col * kMaxRank + half * 8;
+    for (int i = 0; i < NT; ++i) {
+      const int col = min((t0 + i) * kTileN + wave * kBlockCols + block_col_of_m(m), V - 1);
+      const bf16_t *src = p.W2 + (int64_t)col * kMaxRank + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < kPKS; ++ks) {
-      const u16x8 v = *reinterpret_cast<const u16x8 *>(src + ks * 16);
-      if (i < kPRegTiles) {
-        w2r[i < kPRegTiles ? i : 0][ks] = v;
-        // keep the operand in the accumulation registers (the products read
-        // it there directly); left to itself the allocator moved parts of it
-        // to scratch or copied it into vector registers before every product
-        asm volatile("" : "+a"(w2r[i < kPRegTiles ? i : 0][ks]));
+      for (int ks = 0; ks < kPKS; ++ks) {
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(src + ks * 16);
+        if (i < kPRegTiles) w2r[i < kPRegTiles ? i : 0][ks] = v;
+        else w2f[ks] = v;
       }
-      else sh.w2l[(ks * 4 + wave) * kWave + lane] = __builtin_bit_cast(u32x4, v);
     }
+    // keep the operand in the accumulation registers (the products read it
+    // there directly; left to itself the allocator moved parts of it to
+    // scratch or copied it into vector registers before every product).  The
+    // pins come after every load is in flight: a pin consumes its value, so a
+    // pin after each load made the loads one round trip each.
+#pragma unroll
+    for (int i = 0; i < kPRegTiles; ++i)
+#pragma unroll
+      for (int ks = 0; ks < kPKS; ++ks) asm volatile("" : "+a"(w2r[i][ks]));
+#pragma unroll
+    for (int ks = 0; ks < kPKS; ++ks)
+      sh.w2l[(ks * 4 + wave) * kWave + lane] = __builtin_bit_cast(u32x4, w2f[ks]);
   }
 
   // ---- U of item (row block rb, tile slot i) at step k: this lane's 16

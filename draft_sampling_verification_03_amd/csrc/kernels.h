@@ -78,6 +78,7 @@ struct VerifyLaunch {
   float2 *bonus_tiles;   // [R][n_tiles]
   float2 *pair_partials; // [R * gamma][n_tiles]
   int4 *row_map;         // [R * gamma]
+  float4 *row_stats;     // [R * gamma]: (m_q, log2 S_q, m_p, log2 S_p) of the compact rows
   void *A_rows;          // [R * gamma][r] transition rows of the compact rows
   const void *A_given;   // [gamma][R][r] given transition rows (recurrent head), or NULL
 };
@@ -130,7 +131,7 @@ inline size_t schedule_ws_bytes(int R, int gamma) {
 inline size_t verify_ws_bytes(int R, int gamma, int V, int rows_capacity) {
   return kWsHeader + ws_align((size_t)rows_capacity * 4 * 8) +
          ws_align((size_t)R * n_tiles_of(V) * 8) + ws_align((size_t)R * gamma * n_tiles_of(V) * 8) +
-         ws_align((size_t)R * gamma * 16) + ws_align((size_t)R * gamma * kMaxRowBytes);
+         2 * ws_align((size_t)R * gamma * 16) + ws_align((size_t)R * gamma * kMaxRowBytes);
 }
 inline size_t train_ws_bytes(int R, int gamma, int V) {
   const size_t n = (size_t)R * gamma;

@@ -511,6 +511,19 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
   if (tid == 0) p.n_acc[rho] = n;
 }
 
+bool verify_stationary_shape(int V, int r, bool bf16, int *grid, int *nt);
+hipError_t launch_verify_stationary(const VerifyLaunch &L, int G, int nt, hipStream_t stream);
+
+// DSPARK_STATIONARY_VERIFY=0 in the environment selects the row-stationary
+// verify product for every shape (a switch to compare the two designs).
+static bool getenv_stationary_enabled() {
+  static const bool on = [] {
+    const char *v = getenv("DSPARK_STATIONARY_VERIFY");
+    return v == nullptr || v[0] != '0';
+  }();
+  return on;
+}
+
 template <typename T>
 static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   const int nT = n_tiles_of(L.V);
@@ -534,10 +547,16 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   // compute unit) takes an equal share of the (row group, tile) items it
   // finds there
   const int grid = kComputeUnits;
-  // row groups of 256 rows (8 waves x 1 row block: each W2 block in LDS serves
-  // twice the rows of a 4-wave group; measured faster than 4 waves and than 2
-  // or 3 row blocks per wave)
-  if (L.r == (L.bf16 ? kMaxRank : 128)) {
+  int sgrid = 0, snt = 0;
+  if (getenv_stationary_enabled() && verify_stationary_shape(L.V, L.r, sizeof(T) == 2, &sgrid, &snt)) {
+    // bf16, rank 256: W2 held on chip, every verified row streamed past it
+    // (verify_stationary.hip)
+    const hipError_t e = launch_verify_stationary(L, sgrid, snt, stream);
+    if (e != hipSuccess) return e;
+  } else if (L.r == (L.bf16 ? kMaxRank : 128)) {
+    // row groups of 256 rows (8 waves x 1 row block: each W2 block in LDS
+    // serves twice the rows of a 4-wave group; measured faster than 4 waves
+    // and than 2 or 3 row blocks per wave)
     DSPARK_LAUNCH("bias_tile_verify", stream,
                   (stream_tile_kernel<T, Epi::kVerify, sizeof(T) == 2 ? kMaxRank / 16 : 64, 8, 1>),
                   grid, 8 * kWave, bp);

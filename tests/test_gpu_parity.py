@@ -87,6 +87,9 @@ def test_tiny_config_other_rounds(rnd):
     dict(R=4, gamma=2, V=131848, dtype=synth.BF16, r=256, weight_sd=0.02),
     dict(R=2, gamma=1, V=1024, dtype=synth.BF16, r=256, weight_sd=0.05),
     dict(R=7, gamma=3, V=2048, dtype=synth.BF16, r=256, weight_sd=0.05, temp=0.6),
+    # bf16, r = 256 past five tiles per compute unit (1281 tiles): the
+    # streaming draft and the streaming verify product
+    dict(R=2, gamma=2, V=163968, dtype=synth.BF16, r=256, weight_sd=0.02),
 ])
 def test_edge_shapes(over):
     cfg = synth.make_config(1, cid=50 + len(_cache), **over)
