@@ -55,17 +55,19 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
   constexpr int kPer = Elem<T>::kPerVec;
   constexpr int kBatch = 2;                  // pieces per thread per round (4: 48.9 us, 6: 51.7)
   constexpr int kG = kTileN / kPer;          // threads per tile (bf16: 16, fp32: 32)
-  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int c = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, nT = p.n_tiles;
   int used = p.n_rows;
   if (p.row_offset != nullptr) {
     used = p.row_offset[p.R];
     if (used > p.n_rows) {
-      if (row == 0 && c == 0 && tid == 0) flag_error(p.err, kErrLength);
+      if (blockIdx.y == 0 && c == 0 && tid == 0) flag_error(p.err, kErrLength);
       used = p.n_rows;
     }
   }
-  if (row >= used) return;
+  // rows blockIdx.y, blockIdx.y + gridDim.y, ... below the rows in use (the
+  // host sizes the grid by its bound on them, capped; see the launch)
+  for (int row = blockIdx.y; row < used; row += gridDim.y) {
   const int tpc = (nT + kChunks - 1) / kChunks;
   const int tb = min(c * tpc, nT), te = min(tb + tpc, nT);
   const int vb = tb * kTileN, ve = min(te * kTileN, V);
@@ -205,6 +207,7 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
     const float m = mx * p.invT;
     p.chunks[(int64_t)row * kChunks + c] = make_float2(m, sx);
     if (vb < ve && !(isfinite(m) && isfinite(sx))) flag_error(p.err, kErrNonFinite);
+  }
   }
 }
 
@@ -514,6 +517,10 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
 bool verify_stationary_shape(int V, int r, bool bf16, int *grid, int *nt);
 hipError_t launch_verify_stationary(const VerifyLaunch &L, int G, int nt, hipStream_t stream);
 
+// Below this many possible verified rows (R gamma) the row-stationary product
+// is used: it is one row group, so it reads W2 once.
+constexpr int kStationaryMinRows = 256;
+
 // DSPARK_STATIONARY_VERIFY=0 in the environment selects the row-stationary
 // verify product for every shape (a switch to compare the two designs).
 static bool getenv_stationary_enabled() {
@@ -533,8 +540,12 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   rs.bonus_tiles = L.bonus_tiles; rs.err = L.err;
   rs.gamma = L.gamma; rs.x0 = L.x0; rs.x = L.x; rs.row_map = L.row_map;
   rs.r = L.r; rs.W1 = L.W1; rs.A_rows = L.A_rows; rs.A_given = L.A_given;
-  DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.rows_capacity),
-                kBlock, rs);
+  // at most 1024 rows of workgroups: the rows in use are known only on the
+  // device, and a grid of the host's bound (R (1 + gamma)) dispatched mostly
+  // workgroups that only found they had no row (4% slower at R = 128)
+  constexpr int kRowGrid = 1024;
+  DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>,
+                dim3(kChunks, L.rows_capacity < kRowGrid ? L.rows_capacity : kRowGrid), kBlock, rs);
 
   BiasTileParams bp{};
   bp.R = L.R; bp.gamma = L.gamma; bp.V = L.V; bp.r = L.r; bp.n_tiles = nT; bp.invT = L.invT;
@@ -548,9 +559,12 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   // finds there
   const int grid = kComputeUnits;
   int sgrid = 0, snt = 0;
-  if (getenv_stationary_enabled() && verify_stationary_shape(L.V, L.r, sizeof(T) == 2, &sgrid, &snt)) {
-    // bf16, rank 256: W2 held on chip, every verified row streamed past it
-    // (verify_stationary.hip)
+  if (getenv_stationary_enabled() && L.R * L.gamma > kStationaryMinRows &&
+      verify_stationary_shape(L.V, L.r, sizeof(T) == 2, &sgrid, &snt)) {
+    // bf16, rank 256, more than one 256-row group possible: W2 held on chip,
+    // every verified row streamed past it (verify_stationary.hip).  With at
+    // most 256 verified rows the row-stationary kernel reads W2 once anyway
+    // and has no prologue to hide (R = 32, gamma = 7: 51.5 against 58 us).
     const hipError_t e = launch_verify_stationary(L, sgrid, snt, stream);
     if (e != hipSuccess) return e;
   } else if (L.r == (L.bf16 ? kMaxRank : 128)) {
@@ -593,7 +607,10 @@ struct OverlapParams {
 template <typename T>
 __global__ __launch_bounds__(kBlock) void overlap_chunk_kernel(OverlapParams p) {
   __shared__ float red[8];
-  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, V = p.V, nT = p.n_tiles;
+  const int c = blockIdx.x, tid = threadIdx.x, V = p.V, nT = p.n_tiles;
+  // rows blockIdx.y, blockIdx.y + gridDim.y, ... (the grid's second
+  // dimension is capped)
+  for (int row = blockIdx.y; row < p.n_rows; row += gridDim.y) {
   float mp, rp, mq, rq;
   if (p.p_stats != nullptr) {
     mp = p.p_stats[2 * (int64_t)row]; rp = 1.0f / p.p_stats[2 * (int64_t)row + 1];
@@ -635,6 +652,7 @@ __global__ __launch_bounds__(kBlock) void overlap_chunk_kernel(OverlapParams p) 
   }
   const float s = block_sum(acc, red);
   if (tid == 0) p.partial[(int64_t)row * kChunks + c] = s;
+  }
 }
 
 __global__ void overlap_combine_kernel(int n_rows, const float *partial, float *c_star) {
@@ -649,22 +667,21 @@ __global__ void overlap_combine_kernel(int n_rows, const float *partial, float *
 template <typename T>
 static hipError_t launch_overlap_t(const OverlapLaunch &L, hipStream_t stream) {
   const int nT = n_tiles_of(L.V);
+  // the grid's second dimension is at most 65535; past it the kernels loop
+  const int gy = L.n_rows < 65535 ? L.n_rows : 65535;
   if (L.p_stats == nullptr) {
     RowStatsParams rs{};
     rs.n_rows = L.n_rows; rs.V = L.V; rs.n_tiles = nT; rs.invT = L.invT; rs.err = L.err;
     rs.X = L.P; rs.chunks = L.p_chunks;
-    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.n_rows),
-                  kBlock, rs);
+    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, gy), kBlock, rs);
     rs.X = L.Q; rs.chunks = L.q_chunks;
-    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, L.n_rows),
-                  kBlock, rs);
+    DSPARK_LAUNCH("row_chunk_stats", stream, row_chunk_stats_kernel<T>, dim3(kChunks, gy), kBlock, rs);
   }
   OverlapParams op{};
   op.n_rows = L.n_rows; op.V = L.V; op.n_tiles = nT; op.invT = L.invT; op.P = L.P; op.Q = L.Q;
   op.p_stats = L.p_stats; op.q_stats = L.q_stats; op.p_chunks = L.p_chunks;
   op.q_chunks = L.q_chunks; op.partial = L.partial;
-  DSPARK_LAUNCH("overlap_chunk", stream, overlap_chunk_kernel<T>, dim3(kChunks, L.n_rows), kBlock,
-                op);
+  DSPARK_LAUNCH("overlap_chunk", stream, overlap_chunk_kernel<T>, dim3(kChunks, gy), kBlock, op);
   DSPARK_LAUNCH("overlap_combine", stream, overlap_combine_kernel, (L.n_rows + 255) / 256, 256,
                 L.n_rows, L.partial, L.c_star);
   return hipGetLastError();

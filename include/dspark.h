@@ -238,10 +238,10 @@ dspark_status dspark_schedule(int R, int gamma, dspark_sched_mode mode, float th
  *   n_acc  [R]           accepted drafts n, int32
  *   y      [R][gamma+1]  x_1..x_n, then the final token, then -1, int32
  *   c_star [R][gamma]    c*_k for k <= ell, NaN beyond, fp32
- * Execution: with bf16, r = 256 and at most 5 vocabulary tiles of 128 per
- * compute unit, the c* and residual tile partials come from one workgroup
- * per compute unit that keeps its tiles of W2 on chip while every verified
- * row streams past; otherwise (or with DSPARK_STATIONARY_VERIFY=0 in the
+ * Execution: with bf16, r = 256, R * gamma > 256 and at most 5 vocabulary
+ * tiles of 128 per compute unit, the c* and residual tile partials come from
+ * one workgroup per compute unit that keeps its tiles of W2 on chip while
+ * every verified row streams past; otherwise (or with DSPARK_STATIONARY_VERIFY=0 in the
  * environment) from a kernel that keeps rows on chip and streams W2.  Both
  * compute the same products; they add the partials in different orders, so
  * c* may differ in the last bits and a residual draw whose uniform falls

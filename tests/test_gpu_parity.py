@@ -146,6 +146,32 @@ def test_full_size_config(cid):
     print(f"config {cid}: sum ell={int(g['ell'].sum())} n*={g['n_admitted']} {stats}", flush=True)
 
 
+@pytest.mark.parametrize("over,reqs", [
+    # one masked tile per workgroup (157 tiles), every request checked
+    (dict(R=40, gamma=7, V=20000), None),
+    # five tiles per workgroup with a masked one, sampled requests
+    (dict(R=33, gamma=8, V=131848), (0, 16, 32)),
+])
+def test_stationary_verify_shapes(over, reqs):
+    """The W2-stationary verify product (bf16, r = 256, R gamma > 256) with
+    every position admitted: 9 row blocks of 32, the last one partly filled,
+    and masked vocabulary tails; draws, c* and the final tokens against the
+    oracle."""
+    cfg = synth.make_config(1, cid=80 + over["R"], dtype=synth.BF16, r=256, weight_sd=0.05, **over)
+    inp = inputs(cfg)
+    stats = new_stats()
+    g = run_round(inp, mode=0)
+    assert (g["ell"] == cfg.gamma).all()
+    check_properties(inp, g)
+    check_schedule(inp, g)
+    reqs = range(cfg.R) if reqs is None else reqs
+    for rho in reqs:
+        for k in range(1, cfg.gamma + 1):
+            check_draft_position(inp, g, rho, k, stats)
+        check_verify_request(inp, g, rho, stats)
+    print(f"stationary verify {over}: {stats}", flush=True)
+
+
 def test_persistent_draft_peaky_logits_ragged_rows():
     """The single-launch draft (bf16, r = 256, R <= 128) on the stress
     workload's peaky logits (target sd 8, draft noise sd up to 4) with a
