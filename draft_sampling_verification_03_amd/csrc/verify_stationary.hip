@@ -15,7 +15,9 @@
 // of each row to the two partials in the epilogue.  A row's U_k and P
 // segments arrive as 1280-byte runs (the workgroup's five tiles), prefetched
 // one row block ahead in a register ring, instead of 64-byte pieces of 512
-// rows at a time.
+// rows at a time.  A small pass before it gathers each verified row's q and
+// p statistics into one record, so that the product needs a single load per
+// row besides its U_k and P.
 #include "bias_tile.h"
 #include "kernels.h"
 #include "trace.h"
