@@ -69,17 +69,20 @@ struct PersistLds {
   int tok[kPRows];                                   // x_{k-1} of every request
   u32x4 w2l[kPKS * 4 * kWave];                       // W2 of the last tile slot, per lane
   float2 part[kPRows][NT][4];                        // (max of v, sum) per row, tile, wave
+  bf16_t own[2][kPPitch];                            // chunked: A_k of this workgroup's request
+                                                     // in a chunk, by chunk parity
   SampleLds sl;
   int abort;
 };
 
-// The draws x_step of every request into sh.tok, once published (thread t
-// polls requests t, t + kBlock, ...).  Returns false (and flags the error)
-// if a poll ran out.
+// The draws x_step of requests [r0, r1) into sh.tok[row - r0], once
+// published (thread t polls requests r0 + t, r0 + t + kBlock, ...).  Returns
+// false (and flags the error) if a poll ran out.
 template <int NT>
-__device__ __forceinline__ bool wait_tokens(const PersistParams &p, PersistLds<NT> &sh, int step) {
+__device__ __forceinline__ bool wait_tokens(const PersistParams &p, PersistLds<NT> &sh, int step,
+                                            int r0, int r1) {
   bool ok = true;
-  for (int row = threadIdx.x; row < p.R; row += kBlock) {
+  for (int row = r0 + threadIdx.x; row < r1; row += kBlock) {
     uint64_t v = ld_coherent(p.pub + row);
     for (int spins = 0; (int64_t)(v >> 32) < step; ++spins) {
       if (spins > kSpinLimit) {
@@ -89,7 +92,7 @@ __device__ __forceinline__ bool wait_tokens(const PersistParams &p, PersistLds<N
       __builtin_amdgcn_s_sleep(1);
       v = ld_coherent(p.pub + row);
     }
-    sh.tok[row] = (int)min((uint32_t)v, (uint32_t)(p.V - 1));  // in range when published
+    sh.tok[row - r0] = (int)min((uint32_t)v, (uint32_t)(p.V - 1));  // in range when published
   }
   if (!ok) {
     sh.abort = 1;
@@ -99,18 +102,20 @@ __device__ __forceinline__ bool wait_tokens(const PersistParams &p, PersistLds<N
   return sh.abort == 0;
 }
 
-// The anchors x_0 (validated) into sh.tok (step 1's transition rows are
-// W1[x_0]); thread t takes requests t, t + kBlock, ...
+// The anchors x_0 (validated) of requests [r0, r1) into sh.tok[row - r0]
+// (step 1's transition rows are W1[x_0]); thread t takes requests r0 + t,
+// r0 + t + kBlock, ...
 template <int NT>
-__device__ __forceinline__ void anchor_tokens(const PersistParams &p, PersistLds<NT> &sh) {
+__device__ __forceinline__ void anchor_tokens(const PersistParams &p, PersistLds<NT> &sh, int r0,
+                                              int r1) {
   bool bad = false;
-  for (int row = threadIdx.x; row < p.R; row += kBlock) {
+  for (int row = r0 + threadIdx.x; row < r1; row += kBlock) {
     int tok = p.x0[row];
     if (tok < 0 || tok >= p.V) {
       bad = true;
       tok = tok < 0 ? 0 : p.V - 1;
     }
-    sh.tok[row] = tok;
+    sh.tok[row - r0] = tok;
   }
   if (bad) flag_error(p.err, kErrToken);
   __syncthreads();
@@ -118,7 +123,7 @@ __device__ __forceinline__ void anchor_tokens(const PersistParams &p, PersistLds
 
 // NT: vocabulary tiles per workgroup (at most); kMask: V is not a multiple of
 // the tile width, so the last tile has columns past V.
-template <int NT, bool kMask>
+template <int NT, bool kMask, bool kChunked>
 __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistParams p) {
   __shared__ __align__(16) PersistLds<NT> sh;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -190,165 +195,208 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
 #pragma unroll
   for (int i = 0; i < NT; ++i) ur[i] = load_u(1, 0, i, m, half);
 
-  for (int k = 1; k <= gamma; ++k) {
-    // the thread's index, opaque to the compiler once per step: addresses
-    // derived from it are formed again every step instead of being held
-    // across the whole loop (where they went to scratch, and every reload
-    // waited for all loads in flight, the U prefetch included)
-    int tid_k = tid;
-    asm volatile("" : "+v"(tid_k));
-    const int lane_k = tid_k & (kWave - 1), m_k = lane_k & 31, half_k = lane_k >> 5;
-    // ---- 1. transition rows of step k into LDS: W1[x_{k-1}], x_0 the
-    //      anchors, then the draws the samplers published (rows >= R are zero)
-    if (k == 1) anchor_tokens<NT>(p, sh);
-    else if (!wait_tokens<NT>(p, sh, k - 1)) return;
-    {
-      // thread t: 16-byte piece t % 32 of rows t / 32 + 8 j: every load in
-      // flight before the first LDS store, and no branch between them (a row
-      // past R reads row R - 1 and stores zeros)
-      constexpr int kPieces = kMaxRank * 2 / 16;  // 16-byte pieces per row
-      constexpr int kIt = kPRows * kPieces / kBlock;
-      const int off = (tid_k % kPieces) * 8, row0 = tid_k / kPieces;
-      u32x4 v[kIt];
-#pragma unroll
-      for (int j = 0; j < kIt; ++j) {
-        const int row = min(row0 + j * (kBlock / kPieces), R - 1);
-        v[j] = *reinterpret_cast<const u32x4 *>(p.W1 + (int64_t)sh.tok[row] * kMaxRank + off);
-      }
-#pragma unroll
-      for (int j = 0; j < kIt; ++j) {
-        const int row = row0 + j * (kBlock / kPieces);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(sh.rows + row * kPPitch + off) = row < R ? v[j] : z;
-      }
-    }
-    __syncthreads();
-
-    // ---- 2. products and epilogues, row block by row block.  Item i of a
-    //      row block is tile slot i: the register-held slots first (the first
-    //      products wait only for the rows' LDS reads), the LDS-held slot last
-    for (int rb = 0; rb < nrb; ++rb) {
-      u16x8 bfr[kPKS];
-      {
-        const bf16_t *rowp = sh.rows + (rb * kRowsPerWave + m_k) * kPPitch + half_k * 8;
-#pragma unroll
-        for (int ks = 0; ks < kPKS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8 *>(rowp + ks * 16);
-      }
-      // products of item i < NT - 1 (W2 from registers)
-      auto mma = [&](int i) __attribute__((always_inline)) {
-        floatx16 acc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < kPKS; ++ks) acc = mfma16<true>(w2r[i < NT - 1 ? i : 0][ks], bfr[ks], acc);
-        return acc;
-      };
-      // the next U of an item: the same tile slot one row block later, or
-      // the first row block of the next step (the last step reloads its own)
-      const bool last_rb = rb + 1 == nrb;
-      const int k_next = last_rb ? min(k + 1, gamma) : k;
-      const int rb_next = last_rb ? 0 : rb + 1;
-      auto epilogue = [&](int i, const floatx16 &acc) __attribute__((always_inline)) {
-        const int sl = i;
-        float v[16];
-        unpack16(ur[i].a, (bf16_t *)nullptr, v);
-        unpack16(ur[i].b, (bf16_t *)nullptr, v + 8);
-        const int c0 = (t0 + sl) * kTileN + wave * kBlockCols + half_k * 16;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          v[c] = acc[c] + v[c];  // z * T: the product kernels' exact expression
-          if (kMask && c0 + c >= V) v[c] = -INFINITY;
-        }
-        ur[i] = load_u(k_next, rb_next, sl, m_k, half_k);
-        float bm = v[0];
-#pragma unroll
-        for (int c = 1; c < 16; ++c) bm = fmaxf(bm, v[c]);
-        float s = 0.0f;
-        if (!kMask || bm != -INFINITY) {
-          // (v - max) first: exact near the maximum, where the mass is; one
-          // fused multiply-add with -max * log2(e) / T rounded would shift
-          // every term by up to half an ulp of that product (~1e-6 relative
-          // at |max| ~ 40), enough to lift a q(x) near 1 above 1 + 1e-6
-#pragma unroll
-          for (int c = 0; c < 16; ++c) s += exp2_fast((v[c] - bm) * cl);
-        }
-        // the other 16 columns of the row are in lane l ^ 32
-        // (both lanes of a row form the same sum: their operands are swapped
-        // and addition is commutative, so both store the same value)
-        const float om = half_swap(bm), os = half_swap(s);
-        const float M = fmaxf(bm, om);
-        const float S2 = s * exp2_fast((bm - M) * cl) + os * exp2_fast((om - M) * cl);
-        sh.part[rb * kRowsPerWave + m_k][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
-      };
-      // item 0 from registers: its products wait only for the rows' reads;
-      // the LDS-held slot's operands are read one item ahead of its products
-      floatx16 acc0 = mma(0), acc1;
-      u16x8 w2f[kPKS];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (i + 2 == NT) {
-#pragma unroll
-          for (int ks = 0; ks < kPKS; ++ks)
-            w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane_k]);
-        }
-        if (i + 1 < NT) {
-          floatx16 nx;
-          if (i + 1 < NT - 1) {
-            nx = mma(i + 1);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) nx[e] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < kPKS; ++ks) nx = mfma16<true>(w2f[ks], bfr[ks], nx);
-          }
-          if (i & 1) acc0 = nx;
-          else acc1 = nx;
-        }
-        epilogue(i, (i & 1) ? acc1 : acc0);
-        // the epilogue of item i issues while the products of item i + 1 run
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector ALU
-        }
-        // nothing moves across items: hoisting the next items' loads would
-        // run out of registers
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __syncthreads();
-
-    // ---- 3. tile partials (fixed wave order) into the step's half
+  // this workgroup's requests are rho = g, g + G, ...; the first one at or
+  // after row r0
+  auto first_own = [&](int r0) __attribute__((always_inline)) {
+    return kChunked ? r0 + ((g - r0) % G + G) % G : g;
+  };
+  // ---- 4. draws of this workgroup's requests among rows [r0, r1) at step k;
+  //      false when a wait ran out
+  auto draws = [&](int k, int c, int r0, int r1) __attribute__((always_inline)) {
     uint64_t *tiles = p.tiles + (int64_t)(k & 1) * R * nT;
-    for (int q = tid_k; q < R * ntl; q += kBlock) {
-      const int row = q / ntl, i = q - row * ntl;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.part[row][i][w].x);
-      float S = 0.0f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float2 pw = sh.part[row][i][w];
-          if (pw.x != -INFINITY) S += pw.y * exp2_fast((pw.x - M) * cl);
-        }
-      }
-      // max z = (max of acc + u) / T exactly (rounding is monotone)
-      uint64_t word = __builtin_bit_cast(uint64_t, make_float2(M * invT, S));
-      if (word == kTileEmpty) word = kTileEmpty - 1;  // another NaN: still read as non-finite
-      st_coherent(tiles + (int64_t)row * nT + t0 + i, word);
-    }
-
-    // ---- 4. draws of this workgroup's requests
-    for (int rho = g; rho < R; rho += G) {
+    for (int rho = first_own(r0); rho < r1; rho += G) {
       const PersistIo io{tiles, p.pub, &sh.abort};
-      if (!sample_row<bf16_t, true, kPKS>(p.sp, k, nullptr, rho, sh.rows + rho * kPPitch, false,
-                                          sh.sl, io))
-        return;
+      bf16_t *arow = kChunked ? sh.own[c & 1] : sh.rows + rho * kPPitch;
+      // (a thread index made opaque in every draw: 1.7% faster at R = 128,
+      // and the chunked kernel held no address in scratch across the loop)
+      if (!sample_row<bf16_t, true, kPKS, true>(p.sp, k, nullptr, rho, arow, false, sh.sl, io))
+        return false;
       __syncthreads();  // LDS of the draw is reused by the next request
     }
-    if (k == gamma) break;
-    // ---- 5. the next step waits for every draw of this one (step 1 above)
+    return true;
+  };
+  // requests in chunks of kPRows (one chunk unless kChunked): the draws of a
+  // chunk run after the next chunk's products, so every workgroup's partials
+  // of the chunk are long written when its samplers poll them, and the draws
+  // of step k - 1 are out before step k reaches the chunk
+  const int n_chunks = kChunked ? (R + kPRows - 1) / kPRows : 1;
+
+  for (int k = 1; k <= gamma; ++k) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int r0 = kChunked ? c * kPRows : 0, r1 = kChunked ? min(R, r0 + kPRows) : R;
+      const int rb0 = kChunked ? r0 / kRowsPerWave : 0;
+      const int rb1 = kChunked ? (r1 + kRowsPerWave - 1) / kRowsPerWave : nrb;
+      // the thread's index, opaque to the compiler once per step (and chunk):
+      // addresses derived from it are formed again every step instead of
+      // being held across the whole loop (where they went to scratch, and
+      // every reload waited for all loads in flight, the U prefetch included)
+      int tid_k = tid;
+      asm volatile("" : "+v"(tid_k));
+      const int lane_k = tid_k & (kWave - 1), m_k = lane_k & 31, half_k = lane_k >> 5;
+      // ---- 1. transition rows of the chunk at step k into LDS: W1[x_{k-1}],
+      //      x_0 the anchors, then the draws the samplers published (rows
+      //      past R are zero)
+      if (k == 1) anchor_tokens<NT>(p, sh, r0, r1);
+      else if (!wait_tokens<NT>(p, sh, k - 1, r0, r1)) return;
+      {
+        // thread t: 16-byte piece t % 32 of rows t / 32 + 8 j: every load in
+        // flight before the first LDS store, and no branch between them (a
+        // row past R reads row R - 1 and stores zeros)
+        constexpr int kPieces = kMaxRank * 2 / 16;  // 16-byte pieces per row
+        constexpr int kIt = kPRows * kPieces / kBlock;
+        const int off = (tid_k % kPieces) * 8, row0 = tid_k / kPieces;
+        u32x4 v[kIt];
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) {
+          const int row = min(row0 + j * (kBlock / kPieces), r1 - r0 - 1);
+          v[j] = *reinterpret_cast<const u32x4 *>(p.W1 + (int64_t)sh.tok[row] * kMaxRank + off);
+        }
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) {
+          const int row = row0 + j * (kBlock / kPieces);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4 *>(sh.rows + row * kPPitch + off) = row < r1 - r0 ? v[j] : z;
+        }
+      }
+      __syncthreads();
+      if constexpr (kChunked) {
+        // this workgroup's request of the chunk (at most one: G >= kPRows)
+        // keeps its row until its draw, after the next chunk's rows replace
+        // these
+        const int mine = first_own(r0);
+        constexpr int kPieces = kMaxRank * 2 / 16;
+        if (mine < r1 && tid_k < kPieces)
+          *reinterpret_cast<u32x4 *>(sh.own[c & 1] + tid_k * 8) =
+              *reinterpret_cast<const u32x4 *>(sh.rows + (mine - r0) * kPPitch + tid_k * 8);
+      }
+
+      // ---- 2. products and epilogues, row block by row block.  Item i of a
+      //      row block is tile slot i: the register-held slots first (the first
+      //      products wait only for the rows' LDS reads), the LDS-held slot last
+      for (int rb = rb0; rb < rb1; ++rb) {
+        const int rbl = rb - rb0;  // row block within the chunk (LDS rows and partials)
+        u16x8 bfr[kPKS];
+        {
+          const bf16_t *rowp = sh.rows + (rbl * kRowsPerWave + m_k) * kPPitch + half_k * 8;
+  #pragma unroll
+          for (int ks = 0; ks < kPKS; ++ks) bfr[ks] = *reinterpret_cast<const u16x8 *>(rowp + ks * 16);
+        }
+        // products of item i < NT - 1 (W2 from registers)
+        auto mma = [&](int i) __attribute__((always_inline)) {
+          floatx16 acc;
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  #pragma unroll
+          for (int ks = 0; ks < kPKS; ++ks) acc = mfma16<true>(w2r[i < NT - 1 ? i : 0][ks], bfr[ks], acc);
+          return acc;
+        };
+        // the next U of an item: the same tile slot one row block later, or
+        // the first row block of the next step (the last step reloads its own)
+        const bool last_rb = rb + 1 == nrb;
+        const int k_next = last_rb ? min(k + 1, gamma) : k;
+        const int rb_next = last_rb ? 0 : rb + 1;
+        auto epilogue = [&](int i, const floatx16 &acc) __attribute__((always_inline)) {
+          const int sl = i;
+          float v[16];
+          unpack16(ur[i].a, (bf16_t *)nullptr, v);
+          unpack16(ur[i].b, (bf16_t *)nullptr, v + 8);
+          const int c0 = (t0 + sl) * kTileN + wave * kBlockCols + half_k * 16;
+  #pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            v[c] = acc[c] + v[c];  // z * T: the product kernels' exact expression
+            if (kMask && c0 + c >= V) v[c] = -INFINITY;
+          }
+          ur[i] = load_u(k_next, rb_next, sl, m_k, half_k);
+          float bm = v[0];
+  #pragma unroll
+          for (int c = 1; c < 16; ++c) bm = fmaxf(bm, v[c]);
+          float s = 0.0f;
+          if (!kMask || bm != -INFINITY) {
+            // (v - max) first: exact near the maximum, where the mass is; one
+            // fused multiply-add with -max * log2(e) / T rounded would shift
+            // every term by up to half an ulp of that product (~1e-6 relative
+            // at |max| ~ 40), enough to lift a q(x) near 1 above 1 + 1e-6
+  #pragma unroll
+            for (int c = 0; c < 16; ++c) s += exp2_fast((v[c] - bm) * cl);
+          }
+          // the other 16 columns of the row are in lane l ^ 32
+          // (both lanes of a row form the same sum: their operands are swapped
+          // and addition is commutative, so both store the same value)
+          const float om = half_swap(bm), os = half_swap(s);
+          const float M = fmaxf(bm, om);
+          const float S2 = s * exp2_fast((bm - M) * cl) + os * exp2_fast((om - M) * cl);
+          sh.part[rbl * kRowsPerWave + m_k][sl][wave] = make_float2(M, M != -INFINITY ? S2 : 0.0f);
+        };
+        // item 0 from registers: its products wait only for the rows' reads;
+        // the LDS-held slot's operands are read one item ahead of its products
+        floatx16 acc0 = mma(0), acc1;
+        u16x8 w2f[kPKS];
+  #pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          if (i + 2 == NT) {
+  #pragma unroll
+            for (int ks = 0; ks < kPKS; ++ks)
+              w2f[ks] = __builtin_bit_cast(u16x8, sh.w2l[(ks * 4 + wave) * kWave + lane_k]);
+          }
+          if (i + 1 < NT) {
+            floatx16 nx;
+            if (i + 1 < NT - 1) {
+              nx = mma(i + 1);
+            } else {
+  #pragma unroll
+              for (int e = 0; e < 16; ++e) nx[e] = 0.0f;
+  #pragma unroll
+              for (int ks = 0; ks < kPKS; ++ks) nx = mfma16<true>(w2f[ks], bfr[ks], nx);
+            }
+            if (i & 1) acc0 = nx;
+            else acc1 = nx;
+          }
+          epilogue(i, (i & 1) ? acc1 : acc0);
+          // the epilogue of item i issues while the products of item i + 1 run
+  #pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then six vector ALU
+          }
+          // nothing moves across items: hoisting the next items' loads would
+          // run out of registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+
+      __syncthreads();
+
+      // ---- 3. tile partials (fixed wave order) into the step's half
+      uint64_t *tiles = p.tiles + (int64_t)(k & 1) * R * nT;
+      for (int q = tid_k; q < (r1 - r0) * ntl; q += kBlock) {
+        const int rl = q / ntl, i = q - rl * ntl;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.part[rl][i][w].x);
+        float S = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float2 pw = sh.part[rl][i][w];
+            if (pw.x != -INFINITY) S += pw.y * exp2_fast((pw.x - M) * cl);
+          }
+        }
+        // max z = (max of acc + u) / T exactly (rounding is monotone)
+        uint64_t word = __builtin_bit_cast(uint64_t, make_float2(M * invT, S));
+        if (word == kTileEmpty) word = kTileEmpty - 1;  // another NaN: still read as non-finite
+        st_coherent(tiles + (int64_t)(r0 + rl) * nT + t0 + i, word);
+      }
+
+      // ---- 4. draws: this chunk's (one chunk), else the previous chunk's
+      if (!kChunked) {
+        if (!draws(k, c, r0, r1)) return;
+      } else if (c > 0) {
+        if (!draws(k, c - 1, r0 - kPRows, r0)) return;
+      }
+    }
+    if (kChunked && !draws(k, n_chunks - 1, (n_chunks - 1) * kPRows, R)) return;
+    // ---- 5. the next step waits for the draws of this one (step 1 above)
   }
 }
 
@@ -361,26 +409,29 @@ __global__ void persist_clear_kernel(uint64_t *tiles, int n_words, uint64_t *pub
 
 // Launch shape of the persistent draft, or false when the shape does not fit
 // it (then the per-step kernels run).  One workgroup per compute unit; each
-// holds at most 5 tiles (640 columns) of W2.
+// holds at most 5 tiles (640 columns) of W2.  Past kPRows requests the rows
+// go in chunks of kPRows (at most kMaxChunks), which needs a grid of at least
+// kPRows workgroups: each then draws at most one request of a chunk.
+constexpr int kMaxChunks = 4;
 bool persistent_draft_shape(int R, int V, int r, bool bf16, int *grid, int *nt) {
-  if (!bf16 || r != kMaxRank || R > kPRows || V < kTileN) return false;
+  if (!bf16 || r != kMaxRank || R > kMaxChunks * kPRows || V < kTileN) return false;
   const int n_tiles = (V + kTileN - 1) / kTileN;
   const int G = n_tiles < kComputeUnits ? n_tiles : kComputeUnits;
   const int per = (n_tiles + G - 1) / G;
-  if (per > 5) return false;
+  if (per > 5 || (R > kPRows && G < kPRows)) return false;
   *grid = G;
   *nt = per <= 4 ? 4 : 5;
   return true;
 }
 
-template <int NT, bool kMask>
+template <int NT, bool kMask, bool kChunked>
 static hipError_t launch_persistent_t(PersistParams &pp, int G, hipStream_t stream) {
   void *args[] = {&pp};
   hipEvent_t start = nullptr, stop = nullptr;
   if (trace_on()) trace_events("draft_persistent", &start, &stop);
   if (start) (void)hipEventRecord(start, stream);
   hipError_t e = hipLaunchCooperativeKernel(
-      reinterpret_cast<const void *>(&draft_persistent_kernel<NT, kMask>), dim3(G), dim3(kBlock),
+      reinterpret_cast<const void *>(&draft_persistent_kernel<NT, kMask, kChunked>), dim3(G), dim3(kBlock),
       args, 0, stream);
   if (stop) (void)hipEventRecord(stop, stream);
   return e;
@@ -404,10 +455,16 @@ hipError_t launch_draft_persistent(const DraftLaunch &L, int G, int nt, const Sa
                 std::min((n_words + 255) / 256, 4 * kComputeUnits), 256, pp.tiles, n_words, L.pub,
                 L.R);
   const bool mask = L.V % kTileN != 0;
-  if (nt == 4) return mask ? launch_persistent_t<4, true>(pp, G, stream)
-                           : launch_persistent_t<4, false>(pp, G, stream);
-  return mask ? launch_persistent_t<5, true>(pp, G, stream)
-              : launch_persistent_t<5, false>(pp, G, stream);
+  if (L.R > kPRows) {
+    if (nt == 4) return mask ? launch_persistent_t<4, true, true>(pp, G, stream)
+                             : launch_persistent_t<4, false, true>(pp, G, stream);
+    return mask ? launch_persistent_t<5, true, true>(pp, G, stream)
+                : launch_persistent_t<5, false, true>(pp, G, stream);
+  }
+  if (nt == 4) return mask ? launch_persistent_t<4, true, false>(pp, G, stream)
+                           : launch_persistent_t<4, false, false>(pp, G, stream);
+  return mask ? launch_persistent_t<5, true, false>(pp, G, stream)
+              : launch_persistent_t<5, false, false>(pp, G, stream);
 }
 
 }  // namespace dspark

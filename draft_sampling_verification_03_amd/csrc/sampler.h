@@ -68,9 +68,13 @@ constexpr int kSpinLimit = 1 << 18;     // polls before a wait gives up
 // otherwise the caller has put it there.  A_next (or NULL) receives W1[x_k].
 // Without kPersist the tile partials (p.tile_stats), and the transition rows
 // read through A_cur or a_tokens, must be visible before the call; with it
-// see PersistIo.  KS > 0: r = 16 KS (bf16), fixed at compile time.  Returns
-// false, in every thread, only when a persistent wait ran out (kErrSync).
-template <typename T, bool kPersist = false, int KS = 0>
+// see PersistIo.  KS > 0: r = 16 KS (bf16), fixed at compile time.
+// kFreshTid: the thread index is made opaque to the compiler at each call,
+// so that no address derived from it is held across a caller's loop (held
+// ones went to scratch, and a reload waits for every load in flight).
+// Returns false, in every thread, only when a persistent wait ran out
+// (kErrSync).
+template <typename T, bool kPersist = false, int KS = 0, bool kFreshTid = false>
 __device__ __forceinline__ bool sample_row(const SampleParams &p, int k, void *A_next, int rho,
                                            T *arow, bool stage_arow, SampleLds &sl,
                                            const PersistIo &io = PersistIo{}) {
@@ -80,7 +84,10 @@ __device__ __forceinline__ bool sample_row(const SampleParams &p, int k, void *A
   int *red_found = sl.red_found, *red_last = sl.red_last;
   float &s_before = sl.s_before, &s_mt = sl.s_mt, &s_u = sl.s_u;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  int tid_raw = threadIdx.x;
+  if constexpr (kFreshTid) asm volatile("" : "+v"(tid_raw));
+  const int tid = tid_raw, lane = tid & (kWave - 1);
+  const int wave = kFreshTid ? __builtin_amdgcn_readfirstlane(tid / kWave) : tid / kWave;
   const int V = p.V, r = p.r, nT = p.n_tiles;
   const int64_t slot = (int64_t)rho * p.gamma + (k - 1);
   constexpr int kPer = 16 / (int)sizeof(T);

@@ -133,9 +133,11 @@ typedef enum {
  *   q_stats [R][gamma][2] (m, S) of z_k, so q_k(v) = exp(z_k(v) - m) / S, fp32
  *   q_x     [R][gamma]    q_k(x_k), fp32
  *   c       [R][gamma]    confidences c_k, written iff h != NULL (may be NULL otherwise)
- * Execution: with bf16, r = 256, R <= 128 and at most 5 vocabulary tiles of
- * 128 per compute unit, all gamma steps run in one cooperative launch of one
- * workgroup per compute unit that keeps W2 on chip for the call; its
+ * Execution: with bf16, r = 256, R <= 512 and at most 5 vocabulary tiles of
+ * 128 per compute unit (past R = 128 also at least 128 tiles: V >= 16384),
+ * all gamma steps run in one cooperative launch of one workgroup per compute
+ * unit that keeps W2 on chip for the call (past R = 128 the requests go in
+ * chunks of 128, the draws of one chunk beside the next chunk's products); its
  * workgroups exchange tile partials and draws through the workspace with
  * device-coherent accesses and bounded waits (a wait that runs out sets
  * DSPARK_DEVERR_SYNC and the outputs are incomplete).  If the device refuses
