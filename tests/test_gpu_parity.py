@@ -172,6 +172,26 @@ def test_stationary_verify_shapes(over, reqs):
     print(f"stationary verify {over}: {stats}", flush=True)
 
 
+@pytest.mark.parametrize("over", [
+    # two chunks, the last partly filled (72 rows); 157 workgroups, a masked tile
+    dict(R=200, gamma=3, V=20000),
+    # two chunks, the last of one request; 129 workgroups of one tile each
+    dict(R=129, gamma=2, V=16512),
+    # past 128 requests with fewer than 128 tiles: the per-step kernels
+    dict(R=150, gamma=2, V=4096),
+])
+def test_chunked_persistent_draft(over):
+    """The single-launch draft past 128 requests (bf16, r = 256): requests in
+    chunks of 128, each chunk's draws after the next chunk's products; every
+    draw, q(x), normalizer and the verification against the oracle."""
+    cfg = synth.make_config(1, cid=90 + over["R"], dtype=synth.BF16, r=256, weight_sd=0.05, **over)
+    inp = inputs(cfg)
+    stats = new_stats()
+    g = run_round(inp, mode=2)
+    full_check(inp, g, stats)
+    print(f"chunked draft {over}: sum ell={int(g['ell'].sum())} {stats}", flush=True)
+
+
 def test_persistent_draft_peaky_logits_ragged_rows():
     """The single-launch draft (bf16, r = 256, R <= 128) on the stress
     workload's peaky logits (target sd 8, draft noise sd up to 4) with a
