@@ -213,7 +213,7 @@ static hipError_t launch_draft_t(const DraftLaunch &L, hipStream_t stream) {
     sp.sh = L.sh; sp.w_e = L.w_conf + L.d; sp.b_conf = L.b_conf; sp.c = L.c;
     sp.conf_temp = L.conf_temp;
   }
-  // bf16, rank 256, up to 128 requests: every step in one persistent launch
+  // bf16, rank 256, up to 512 requests: every step in one persistent launch
   // that keeps W2 on chip (draft_persistent.hip)
   int pgrid = 0, pnt = 0;
   if (L.rnn == nullptr && getenv_persistent_enabled() &&

@@ -10,7 +10,9 @@
 // whole 128-column vocabulary tiles and keeps their W2 columns for the whole
 // call: wave w holds the 32-column block w of every tile, the first NT - 1
 // tiles' operands in its registers (64 per tile), the last one in LDS.  Per
-// step only U_k and the transition rows move.
+// step only U_k and the transition rows move.  Past 128 requests the steps
+// below run per chunk of 128 requests, and the draws of a chunk come after
+// the next chunk's products (see the step loop).
 //
 // One step k:
 //   1. the transition rows A_k = W1[x_{k-1}] of every request (x_0 = anchor)
