@@ -65,6 +65,9 @@ def weighted_totals(per, gamma, alpha=ALPHA):
     (dict(R=5, gamma=7, V=2056, r=32, dtype=synth.BF16), 1.0),
     (dict(R=2, gamma=1, V=136, r=16, dtype=synth.BF16), 1.3),
     (dict(R=4, gamma=3, V=1000, r=256, dtype=synth.BF16, weight_sd=0.05), 1.0),  # single launch
+    # the single launch past 128 requests (two chunks) and the W2-stationary
+    # verify product (R gamma > 256)
+    (dict(R=160, gamma=2, V=20000, r=256, dtype=synth.BF16, weight_sd=0.05), 1.0),
 ])
 def test_train_losses_match_oracle_small(shape, temp):
     cfg = synth.make_config(1, **shape)
