@@ -62,7 +62,8 @@ def _same(a, b):
 
 def test_noalloc_draft_matches_workspace_draft_on_consecutive_calls():
     stream = torch.cuda.current_stream()
-    cases = [(128, 4, 151936, 256, True, True), (7, 3, 2056, 32, True, False),
+    # the single-launch draft in two chunks of requests, then smaller calls
+    cases = [(256, 4, 151936, 256, True, True), (7, 3, 2056, 32, True, False),
              (5, 2, 1000, 16, False, True)]
     for i, (R, gamma, V, r, bf16, head) in enumerate(cases):
         print(f"[noalloc] call {i}: R={R} gamma={gamma} V={V} r={r} bf16={bf16} head={head}",
