@@ -204,11 +204,11 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   };
   // ---- 4. draws of this workgroup's requests among rows [r0, r1) at step k;
   //      false when a wait ran out
-  auto draws = [&](int k, int c, int r0, int r1) __attribute__((always_inline)) {
+  auto draws = [&](int k, int ch, int r0, int r1) __attribute__((always_inline)) {
     uint64_t *tiles = p.tiles + (int64_t)(k & 1) * R * nT;
     for (int rho = first_own(r0); rho < r1; rho += G) {
       const PersistIo io{tiles, p.pub, &sh.abort};
-      bf16_t *arow = kChunked ? sh.own[c & 1] : sh.rows + rho * kPPitch;
+      bf16_t *arow = kChunked ? sh.own[ch & 1] : sh.rows + rho * kPPitch;
       // (a thread index made opaque in every draw: 1.7% faster at R = 128,
       // and the chunked kernel held no address in scratch across the loop)
       if (!sample_row<bf16_t, true, kPKS, true>(p.sp, k, nullptr, rho, arow, false, sh.sl, io))
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
   const int n_chunks = kChunked ? (R + kPRows - 1) / kPRows : 1;
 
   for (int k = 1; k <= gamma; ++k) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int r0 = kChunked ? c * kPRows : 0, r1 = kChunked ? min(R, r0 + kPRows) : R;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const int r0 = kChunked ? ch * kPRows : 0, r1 = kChunked ? min(R, r0 + kPRows) : R;
       const int rb0 = kChunked ? r0 / kRowsPerWave : 0;
       const int rb1 = kChunked ? (r1 + kRowsPerWave - 1) / kRowsPerWave : nrb;
       // the thread's index, opaque to the compiler once per step (and chunk):
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
         const int mine = first_own(r0);
         constexpr int kPieces = kMaxRank * 2 / 16;
         if (mine < r1 && tid_k < kPieces)
-          *reinterpret_cast<u32x4 *>(sh.own[c & 1] + tid_k * 8) =
+          *reinterpret_cast<u32x4 *>(sh.own[ch & 1] + tid_k * 8) =
               *reinterpret_cast<const u32x4 *>(sh.rows + (mine - r0) * kPPitch + tid_k * 8);
       }
 
@@ -392,9 +392,9 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
 
       // ---- 4. draws: this chunk's (one chunk), else the previous chunk's
       if (!kChunked) {
-        if (!draws(k, c, r0, r1)) return;
-      } else if (c > 0) {
-        if (!draws(k, c - 1, r0 - kPRows, r0)) return;
+        if (!draws(k, ch, r0, r1)) return;
+      } else if (ch > 0) {
+        if (!draws(k, ch - 1, r0 - kPRows, r0)) return;
       }
     }
     if (kChunked && !draws(k, n_chunks - 1, (n_chunks - 1) * kPRows, R)) return;
