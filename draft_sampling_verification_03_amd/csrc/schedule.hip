@@ -240,13 +240,30 @@ __device__ __forceinline__ int transposed_base() {
   const int lane = (int)(threadIdx.x & (kWave - 1)), wave = (int)threadIdx.x / kWave;
   return ((lane & 3) << LE) | (wave << (LE + 2)) | ((lane >> 2) << (LE + 6));
 }
+// LDS word of key position p in an exchange.  The low five bits of the word
+// (its bank pair) take, besides the lane bits each layout already has there,
+// the lane bits it lacks: the blocked layout's bits 5 .. 4 + log2(E) go to
+// the register bits 0 .. log2(E) - 1, the transposed layout's lane bits at
+// log2(E) + 6 .. go to the register bits and to the wave bits at
+// log2(E) + 2 .. 4.  Each register e of the 32 lanes of a half wave then
+// writes or reads 32 different bank pairs in both layouts (without it 16
+// lanes shared one at E = 8: the cross-wave levels of an 8192-key sort took
+// ~11 µs each).  A bijection on [0, 1024 E): only bits 0 .. 4 change, by a
+// function of bits 5 and up.
+template <int E>
+__device__ __forceinline__ int exchange_word(int p) {
+  constexpr int LE = E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : 3;
+  const int lo = ((p >> 5) ^ (p >> (LE + 6))) & (E - 1);
+  const int hi = ((p >> (2 * LE + 6)) & ((1 << (3 - LE)) - 1)) << (LE + 2);
+  return p ^ lo ^ hi;
+}
 template <int E>
 __device__ __forceinline__ void exchange(uint64_t (&k)[E], uint64_t *buf, int from, int to) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) buf[from + e] = k[e];
+  for (int e = 0; e < E; ++e) buf[exchange_word<E>(from + e)] = k[e];
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < E; ++e) k[e] = buf[to + e];
+  for (int e = 0; e < E; ++e) k[e] = buf[exchange_word<E>(to + e)];
 }
 template <int E>
 __device__ __forceinline__ void local_stage(uint64_t (&k)[E], int base, int size, int s) {
