@@ -1,17 +1,19 @@
 // Exact speculative-sampling verification of the flattened ragged batch
 // (Blog, "One-token exactness", "Why only the longest accepted prefix
 // survives", "Variable-length verification without wasting kernels"; KB
-// sections 7-8).  Three launches:
+// sections 7-8).  The launches:
 //
 //  1. row_chunk_stats_kernel: one HBM pass over the sum(1 + ell) target rows,
 //     (max, sum exp) per quarter row; the last row of every request (its bonus
 //     position) also keeps per-tile partials for sampling.
-//  2. tile_kernel<Verify>: recompute z_k of every verified draft with the
-//     draft's arithmetic, stream U_k and P_k once, emit per-tile
-//     (sum min(p, q), sum (p - q)_+).
-//  3. verify_finalize_kernel: one workgroup per request: c*_k, the accept
-//     tests in order, the first rejection, and the residual or bonus draw by
-//     a two-level inverse CDF.
+//  2. the product: recompute z_k of every verified draft with the draft's
+//     arithmetic, stream U_k and P_k once, emit per-tile
+//     (sum min(p, q), sum (p - q)_+) -- verify_stationary_kernel (W2 held on
+//     chip, after verify_row_stats_kernel; verify_stationary.hip) or
+//     stream_tile_kernel<verify> (bias_tile.h).
+//  3. verify_finalize_kernel: per request, one workgroup for the accept tests
+//     in order, the first rejection and the residual or bonus draw by a
+//     two-level inverse CDF, and one for c*_k.
 #include "bias_tile.h"
 #include "kernels.h"
 #include "trace.h"
@@ -290,77 +292,41 @@ __device__ int pick_in_tile(const float *ebuf, float before, float scale, float 
   return pick;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams p) {
-  __shared__ float wbuf[kMaxTiles];
-  __shared__ float zbuf[kTileN];
-  __shared__ float ebuf[kTileN];
-  __shared__ __align__(16) T arow[kMaxRank + 16];
-  __shared__ float fred[8];
-  __shared__ int ired[8];
-  __shared__ float s_before;
-  __shared__ float2 s_ps[kMaxGamma + 1];  // (m_p, S_p) of the request's target rows
-  __shared__ int s_x[kMaxGamma];          // its draft tokens
-  __shared__ float s_ufin[kMaxGamma + 1];  // final-token uniform of each position
+// The request's slice of the ragged batch, checked against the batch bounds.
+// An invalid slice runs as an empty one (every address stays in bounds).
+struct RequestSlice {
+  bool ok;
+  int ell, base;
+  int64_t d_off;  // compact index of (rho, k = 1)
+};
+__device__ __forceinline__ RequestSlice request_slice(const FinalizeParams &p, int rho, int ell_in,
+                                                      int base_in, int next, int rows_used) {
+  RequestSlice q;
+  q.ok = ell_in >= 0 && ell_in <= p.gamma && base_in >= 0 && next == base_in + 1 + ell_in &&
+         base_in + ell_in < p.rows_capacity && rows_used <= p.rows_capacity && base_in >= rho &&
+         (int64_t)base_in - rho + ell_in <= (int64_t)p.R * p.gamma;
+  q.ell = q.ok ? ell_in : 0;
+  q.base = q.ok ? base_in : 0;
+  q.d_off = q.ok ? (int64_t)q.base - rho : 0;
+  return q;
+}
 
-  constexpr int kTpt = kMaxTiles / kBlock;  // tiles per thread, at most
+// c*_k = sum over tiles of sum_v min(p, q) in tile order (NaN past ell), by a
+// workgroup of its own: the accept tests and the final draw do not read it.
+// Wave w takes k = w + 1, w + 5, ... two at a time, every tile load in flight
+// (clamped past n_tiles, masked in the sum).
+__device__ __forceinline__ void finalize_cstar(const FinalizeParams &p, int rho) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int rho = blockIdx.x, gamma = p.gamma, V = p.V, nT = p.n_tiles;
-  int32_t *yrow = p.y + (int64_t)rho * (gamma + 1);
+  const int gamma = p.gamma, nT = p.n_tiles;
+  const RequestSlice q = request_slice(p, rho, p.ell[rho], p.row_offset[rho], p.row_offset[rho + 1],
+                                       p.row_offset[p.R]);
+  const int ell = q.ell;
   float *crow = p.c_star + (int64_t)rho * gamma;
-
-  // ---- loads that need only rho, all in flight together: the request's
-  //      slice of the ragged batch (every thread validates the same values),
-  //      the draft token and q(x_k) of position k = tid + 1, and the bonus
-  //      row's tile partials
-  const int ell_in = p.ell[rho];
-  const int base_in = p.row_offset[rho];
-  const int next = p.row_offset[rho + 1], rows_used = p.row_offset[p.R];
-  const int32_t *xr = p.x + (int64_t)rho * gamma;
-  // (unconditional loads at clamped positions: a load under a condition
-  // would be waited for inside its branch)
-  const int xk_raw = xr[min(tid, gamma - 1)];
-  const float qk = p.q_x[(int64_t)rho * gamma + min(tid, gamma - 1)];
-  const int x0 = p.x0[rho];
-  float2 bt[kTpt];
-#pragma unroll
-  for (int i = 0; i < kTpt; ++i)
-    bt[i] = p.bonus_tiles[(int64_t)rho * nT + min(tid + i * kBlock, nT - 1)];
-  const bool ok = ell_in >= 0 && ell_in <= gamma && base_in >= 0 && next == base_in + 1 + ell_in &&
-                  base_in + ell_in < p.rows_capacity && rows_used <= p.rows_capacity &&
-                  base_in >= rho && (int64_t)base_in - rho + ell_in <= (int64_t)p.R * gamma;
-  // an invalid slice runs as an empty one (every address stays in bounds, so
-  // the loads above need not wait for the check) and is reported at the end
-  const int ell = ok ? ell_in : 0, base = ok ? base_in : 0;
-  const int64_t d_off = ok ? (int64_t)base - rho : 0;  // compact index of (rho, k = 1)
-
-  // ---- target-row inputs of position k = tid + 1 <= ell + 1 (the row after
-  //      the drafts is the bonus row): chunk statistics, and p(x_k)
-  const bool own_row = tid <= ell;
-  const int prow = base + (own_row ? tid : 0);
-  float2 cs[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) cs[c] = p.p_chunks[(int64_t)prow * kChunks + c];
-  const bool test = tid < ell;
-  const int xk = xk_raw < 0 ? 0 : (xk_raw >= V ? V - 1 : xk_raw);
-  const float tx = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)prow * V,
-                               test ? xk : 0);
-
-  // ---- the Philox uniforms (long integer chains) while the loads are in
-  //      flight: the accept test of position k = tid + 1, and the final draw
-  //      at each position it could land on (the LDS store keeps it here)
-  const float u_acc = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamAccept);
-  if (tid <= gamma)
-    s_ufin[tid] = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamFinal);
-
-  // ---- c*_k = sum over tiles of sum_v min(p, q) in tile order: wave w takes
-  //      k = w + 1, w + 5, ... two at a time, every tile load in flight
-  //      (clamped past n_tiles, masked in the sum)
   constexpr int kTpl = kMaxTiles / kWave;  // tiles per lane, at most
   for (int ka = 1 + wave; ka <= ell; ka += 2 * (kBlock / kWave)) {
     const int kb = ka + kBlock / kWave;
-    const float2 *pa = p.pair_partials + (d_off + ka - 1) * nT;
-    const float2 *pb = p.pair_partials + (d_off + min(kb, ell) - 1) * nT;
+    const float2 *pa = p.pair_partials + (q.d_off + ka - 1) * nT;
+    const float2 *pb = p.pair_partials + (q.d_off + min(kb, ell) - 1) * nT;
     float va[kTpl], vb[kTpl];
 #pragma unroll
     for (int i = 0; i < kTpl; ++i) {
@@ -383,6 +349,75 @@ __global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams 
     }
   }
   for (int k = ell + 1 + tid; k <= gamma; k += kBlock) crow[k - 1] = NAN;
+}
+
+// Workgroups [0, R): the accept tests, the first rejection and the final
+// token of request rho = blockIdx.x; workgroups [R, 2R): c* of request
+// blockIdx.x - R.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void verify_finalize_kernel(FinalizeParams p) {
+  if (blockIdx.x >= (unsigned)p.R) {  // uniform
+    finalize_cstar(p, blockIdx.x - p.R);
+    return;
+  }
+  __shared__ float wbuf[kMaxTiles];
+  __shared__ float zbuf[kTileN];
+  __shared__ float ebuf[kTileN];
+  __shared__ __align__(16) T arow[kMaxRank + 16];
+  __shared__ float fred[8];
+  __shared__ int ired[8];
+  __shared__ float s_before;
+  __shared__ float2 s_ps[kMaxGamma + 1];  // (m_p, S_p) of the request's target rows
+  __shared__ int s_x[kMaxGamma];          // its draft tokens
+  __shared__ float s_ufin[kMaxGamma + 1];  // final-token uniform of each position
+
+  constexpr int kTpt = kMaxTiles / kBlock;  // tiles per thread, at most
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rho = blockIdx.x, gamma = p.gamma, V = p.V, nT = p.n_tiles;
+  int32_t *yrow = p.y + (int64_t)rho * (gamma + 1);
+
+  // ---- loads that need only rho, all in flight together: the request's
+  //      slice of the ragged batch (every thread validates the same values),
+  //      the draft token and q(x_k) of position k = tid + 1, and the bonus
+  //      row's tile partials
+  const int ell_in = p.ell[rho];
+  const int base_in = p.row_offset[rho];
+  const int next = p.row_offset[rho + 1], rows_used = p.row_offset[p.R];
+  const int32_t *xr = p.x + (int64_t)rho * gamma;
+  // (unconditional loads at clamped positions: a load under a condition
+  // would be waited for inside its branch)
+  const int xk_raw = xr[min(tid, gamma - 1)];
+  const float qk = p.q_x[(int64_t)rho * gamma + min(tid, gamma - 1)];
+  const int x0 = p.x0[rho];
+  float2 bt[kTpt];
+#pragma unroll
+  for (int i = 0; i < kTpt; ++i)
+    bt[i] = p.bonus_tiles[(int64_t)rho * nT + min(tid + i * kBlock, nT - 1)];
+  // an invalid slice runs as an empty one (every address stays in bounds, so
+  // the loads above need not wait for the check) and is reported at the end
+  const RequestSlice sl = request_slice(p, rho, ell_in, base_in, next, rows_used);
+  const bool ok = sl.ok;
+  const int ell = sl.ell, base = sl.base;
+  const int64_t d_off = sl.d_off;
+
+  // ---- target-row inputs of position k = tid + 1 <= ell + 1 (the row after
+  //      the drafts is the bonus row): chunk statistics, and p(x_k)
+  const bool own_row = tid <= ell;
+  const int prow = base + (own_row ? tid : 0);
+  float2 cs[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) cs[c] = p.p_chunks[(int64_t)prow * kChunks + c];
+  const bool test = tid < ell;
+  const int xk = xk_raw < 0 ? 0 : (xk_raw >= V ? V - 1 : xk_raw);
+  const float tx = Elem<T>::at(reinterpret_cast<const T *>(p.P) + (int64_t)prow * V,
+                               test ? xk : 0);
+
+  // ---- the Philox uniforms (long integer chains) while the loads are in
+  //      flight: the accept test of position k = tid + 1, and the final draw
+  //      at each position it could land on (the LDS store keeps it here)
+  const float u_acc = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamAccept);
+  if (tid <= gamma)
+    s_ufin[tid] = uniform01(p.seed, p.round, (uint64_t)(tid + 1), (uint64_t)rho, kStreamFinal);
 
   // ---- accept tests: u * q(x_k) < p(x_k), first rejection
   float2 ps_own = make_float2(0.0f, 0.0f);
@@ -586,7 +621,7 @@ static hipError_t launch_verify_t(const VerifyLaunch &L, hipStream_t stream) {
   fp.q_stats = L.q_stats; fp.q_x = L.q_x; fp.seed = L.seed; fp.round = L.round;
   fp.p_chunks = L.p_chunks; fp.bonus_tiles = L.bonus_tiles; fp.pair_partials = L.pair_partials;
   fp.n_acc = L.n_acc; fp.y = L.y; fp.c_star = L.c_star; fp.err = L.err;
-  DSPARK_LAUNCH("verify_finalize", stream, verify_finalize_kernel<T>, L.R, kBlock, fp);
+  DSPARK_LAUNCH("verify_finalize", stream, verify_finalize_kernel<T>, 2 * L.R, kBlock, fp);
   return hipGetLastError();
 }
 
