@@ -72,7 +72,9 @@ __global__ __launch_bounds__(kBlock) void row_chunk_stats_kernel(RowStatsParams 
   for (int row = blockIdx.y; row < used; row += gridDim.y) {
   const int tpc = (nT + kChunks - 1) / kChunks;
   const int tb = min(c * tpc, nT), te = min(tb + tpc, nT);
-  const int vb = tb * kTileN, ve = min(te * kTileN, V);
+  // an empty chunk (c tpc >= nT) starts at V, so that its clamped loads read
+  // the row's last piece and never the bytes past it
+  const int vb = min(tb * kTileN, V), ve = min(te * kTileN, V);
   const int npc = (ve - vb + kPer - 1) / kPer;  // pieces in the chunk (V % kPer == 0)
   const T *X = reinterpret_cast<const T *>(p.X) + (int64_t)row * V + vb;
   const float cl = p.invT * kLog2e;
@@ -639,54 +641,71 @@ struct OverlapParams {
   float *partial;                     // [n_rows][kChunks]
 };
 
+// sum over one quarter of a row pair of min(p, q), one workgroup per quarter:
+// rounds of kBatch 16-byte pieces of P and of Q per thread, two rounds in
+// flight (non-temporal loads; indices clamped, so no branch stands between
+// the loads: past the chunk they read its last piece again and the results
+// are not used), the row's statistics loaded behind the first two rounds.
+// min(p, q) = 2^min(log2 p, log2 q): one exponential per element.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void overlap_chunk_kernel(OverlapParams p) {
   __shared__ float red[8];
+  constexpr int kPer = Elem<T>::kPerVec;
+  constexpr int kBatch = 2;
+  constexpr int kRound = kBatch * kBlock;
   const int c = blockIdx.x, tid = threadIdx.x, V = p.V, nT = p.n_tiles;
+  const int tpc = (nT + kChunks - 1) / kChunks;
+  // an empty chunk starts at V (its clamped loads read the row's last piece)
+  const int vb = min(min(c * tpc, nT) * kTileN, V), ve = min(min(c * tpc + tpc, nT) * kTileN, V);
+  const int npc = (ve - vb + kPer - 1) / kPer;  // pieces in the chunk (V % kPer == 0)
+  const float invT = p.invT;
   // rows blockIdx.y, blockIdx.y + gridDim.y, ... (the grid's second
   // dimension is capped)
   for (int row = blockIdx.y; row < p.n_rows; row += gridDim.y) {
-  float mp, rp, mq, rq;
-  if (p.p_stats != nullptr) {
-    mp = p.p_stats[2 * (int64_t)row]; rp = 1.0f / p.p_stats[2 * (int64_t)row + 1];
-    mq = p.q_stats[2 * (int64_t)row]; rq = 1.0f / p.q_stats[2 * (int64_t)row + 1];
-  } else {
-    const float2 a = combine_chunk_stats(p.p_chunks + (int64_t)row * kChunks);
-    const float2 b = combine_chunk_stats(p.q_chunks + (int64_t)row * kChunks);
-    mp = a.x; rp = 1.0f / a.y; mq = b.x; rq = 1.0f / b.y;
-  }
-  const int tpc = (nT + kChunks - 1) / kChunks;
-  const int vb = min(c * tpc, nT) * kTileN, ve = min(min(c * tpc + tpc, nT) * kTileN, V);
-  const T *Pr = reinterpret_cast<const T *>(p.P) + (int64_t)row * V;
-  const T *Qr = reinterpret_cast<const T *>(p.Q) + (int64_t)row * V;
-  constexpr int kPer = Elem<T>::kPerVec;
-  constexpr int kUnroll = 2;
-  float acc = 0.0f;
-  for (int v0 = vb + tid * kPer; v0 < ve; v0 += kBlock * kPer * kUnroll) {
-    float a[kUnroll][kPer], b[kUnroll][kPer];
-    bool ok[kUnroll];
+    const T *Pr = reinterpret_cast<const T *>(p.P) + (int64_t)row * V + vb;
+    const T *Qr = reinterpret_cast<const T *>(p.Q) + (int64_t)row * V + vb;
+    auto issue = [&](u32x4 (&a)[kBatch], u32x4 (&b)[kBatch], int p0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int v = v0 + u * kBlock * kPer;
-      ok[u] = v < ve;
-      if (ok[u]) {
-        Elem<T>::vec(Pr, v, a[u]);
-        Elem<T>::vec(Qr, v, b[u]);
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t off = (int64_t)min(p0 + j * kBlock + tid, npc - 1) * kPer;
+        a[j] = ld_stream4(Pr + off);
+        b[j] = ld_stream4(Qr + off);
       }
+    };
+    u32x4 ca[kBatch], cb[kBatch], na[kBatch], nb[kBatch];
+    issue(ca, cb, 0);
+    issue(na, nb, kRound);
+    float mp, lp, mq, lq;  // (m, log2 S) of p and of q
+    if (p.p_stats != nullptr) {
+      mp = p.p_stats[2 * (int64_t)row]; lp = log2_fast(p.p_stats[2 * (int64_t)row + 1]);
+      mq = p.q_stats[2 * (int64_t)row]; lq = log2_fast(p.q_stats[2 * (int64_t)row + 1]);
+    } else {
+      const float2 a = combine_chunk_stats(p.p_chunks + (int64_t)row * kChunks);
+      const float2 b = combine_chunk_stats(p.q_chunks + (int64_t)row * kChunks);
+      mp = a.x; lp = log2_fast(a.y); mq = b.x; lq = log2_fast(b.y);
     }
+    float acc = 0.0f;
+    auto reduce = [&](const u32x4 (&a)[kBatch], const u32x4 (&b)[kBatch], int p0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (!ok[u]) continue;
+      for (int j = 0; j < kBatch; ++j) {
+        float x[kPer], y[kPer];
+        unpack16(a[j], (T *)nullptr, x);
+        unpack16(b[j], (T *)nullptr, y);
+        float sj = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const float pv = fexp(a[u][q] * p.invT - mp) * rp;
-        const float qv = fexp(b[u][q] * p.invT - mq) * rq;
-        acc += fminf(pv, qv);
+        for (int q = 0; q < kPer; ++q)
+          sj += exp2_fast(fminf(log2_prob(x[q], invT, mp, lp), log2_prob(y[q], invT, mq, lq)));
+        acc += p0 + j * kBlock + tid < npc ? sj : 0.0f;
       }
+    };
+    for (int p0 = 0; p0 < npc; p0 += 2 * kRound) {
+      reduce(ca, cb, p0);
+      issue(ca, cb, p0 + 2 * kRound);
+      if (p0 + kRound < npc) reduce(na, nb, p0 + kRound);
+      issue(na, nb, p0 + 3 * kRound);
     }
-  }
-  const float s = block_sum(acc, red);
-  if (tid == 0) p.partial[(int64_t)row * kChunks + c] = s;
+    const float s = block_sum(acc, red);
+    if (tid == 0) p.partial[(int64_t)row * kChunks + c] = s;
   }
 }
 
