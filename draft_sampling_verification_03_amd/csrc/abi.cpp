@@ -112,7 +112,7 @@ dspark_status dspark_draft(int R, int gamma, int V, int r, dspark_dtype dt, floa
     if (!w_conf || !c) return DSPARK_ERR_NULL;
     if (d < 8 || d > 65536 || d % 8 != 0) return DSPARK_ERR_SHAPE;
     if (!isfinite(b_conf)) return DSPARK_ERR_VALUE;
-    if (!aligned16(h)) return DSPARK_ERR_ALIGN;
+    if (!aligned16(h) || !aligned16(w_conf)) return DSPARK_ERR_ALIGN;
   }
   if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || !aligned16(ws)) return DSPARK_ERR_ALIGN;
   if (ws_bytes < draft_ws_bytes(R, gamma, V)) return DSPARK_ERR_WORKSPACE;
@@ -146,7 +146,7 @@ dspark_status dspark_draft_noalloc(int R, int gamma, int V, int r, dspark_dtype 
     if (!w_conf || !c) return DSPARK_ERR_NULL;
     if (d < 8 || d > 65536 || d % 8 != 0) return DSPARK_ERR_SHAPE;
     if (!isfinite(b_conf)) return DSPARK_ERR_VALUE;
-    if (!aligned16(h)) return DSPARK_ERR_ALIGN;
+    if (!aligned16(h) || !aligned16(w_conf)) return DSPARK_ERR_ALIGN;
   }
   if (!aligned16(U) || !aligned16(W1) || !aligned16(W2) || ((uintptr_t)dev_error & 3u) != 0)
     return DSPARK_ERR_ALIGN;

@@ -34,7 +34,10 @@ __global__ __launch_bounds__(kBlock) void draft_sample_kernel(SampleParams p) {
   sample_row<T>(p, p.k, p.A_next, blockIdx.x, arow, true, sl);
 }
 
-// sh[rho][k] = sum_j w[j] h[rho][k][j]: one wave per (rho, k), 16-byte loads.
+// sh[rho][k] = sum_j w[j] h[rho][k][j]: one wave per (rho, k).  Lane l takes
+// the 16-byte pieces l, l + 64, ... of the row in that order, kIt of them in
+// flight at a time (non-temporal loads of h, read once; indices clamped, so
+// no branch stands between the loads), with their kPer weights each.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, int d,
                                                                  const T *h, const float *w,
@@ -42,14 +45,35 @@ __global__ __launch_bounds__(kBlock) void head_hidden_dot_kernel(int n_slots, in
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t slot = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (slot >= n_slots) return;
-  constexpr int kPer = Elem<T>::kPerVec;
+  constexpr int kPer = Elem<T>::kPerVec;  // elements per 16-byte piece
+  constexpr int kIt = 8;
   const T *row = h + slot * d;
+  const int np = d / kPer;  // d % 8 == 0
   float acc = 0.0f;
-  for (int j = lane * kPer; j < d; j += kWave * kPer) {
-    float hv[kPer];
-    Elem<T>::vec(row, j, hv);
+  for (int p0 = 0; p0 < np; p0 += kIt * kWave) {
+    u32x4 v[kIt];
+    float4 wv[kIt][kPer / 4];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) acc = fmaf(w[j + q], hv[q], acc);
+    for (int i = 0; i < kIt; ++i) {
+      const int pc = min(p0 + i * kWave + lane, np - 1);
+      v[i] = ld_stream4(row + (int64_t)pc * kPer);
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) wv[i][q] = reinterpret_cast<const float4 *>(w + pc * kPer)[q];
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      if (p0 + i * kWave + lane < np) {
+        float hv[kPer];
+        unpack16(v[i], (T *)nullptr, hv);
+#pragma unroll
+        for (int q = 0; q < kPer / 4; ++q) {
+          acc = fmaf(wv[i][q].x, hv[4 * q], acc);
+          acc = fmaf(wv[i][q].y, hv[4 * q + 1], acc);
+          acc = fmaf(wv[i][q].z, hv[4 * q + 2], acc);
+          acc = fmaf(wv[i][q].w, hv[4 * q + 3], acc);
+        }
+      }
+    }
   }
   acc = wave_sum(acc);
   if (lane == 0) sh[slot] = acc;

@@ -68,7 +68,7 @@ def draft_args(**over):
     (dict(temp=float("inf")), VALUE), (dict(temp=float("nan")), VALUE),
     (dict(ws_bytes=16), WS), (dict(U=P + 4), ALIGN), (dict(W1=P + 8), ALIGN),
     (dict(h=P, d=16, w_conf=None, c=P), NULL), (dict(h=P, d=12, w_conf=P, c=P), SHAPE),
-    (dict(h=P + 2, d=16, w_conf=P, c=P), ALIGN),
+    (dict(h=P + 2, d=16, w_conf=P, c=P), ALIGN), (dict(h=P, d=16, w_conf=P + 4, c=P), ALIGN),
 ])
 def test_draft_validation(over, expect):
     assert A.dspark_draft(**draft_args(**over)) == expect
