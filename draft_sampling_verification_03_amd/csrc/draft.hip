@@ -1,7 +1,10 @@
 // Markov-head drafting (Blog, "Markov sequential head"; Bangkok 4.1; KB
-// section 2): gamma serial steps, each = one fused bias-tile launch (partials
-// of z_k per vocabulary tile) + one sampling launch (one workgroup per request,
-// the two-level inverse CDF of sampler.h).
+// section 2): gamma serial steps.  For bf16, rank 256 and up to 512 requests
+// all of them run in one cooperative launch that keeps W2 on chip
+// (draft_persistent.hip); otherwise (and when that launch is refused) each
+// step is one fused bias-tile launch (partials of z_k per vocabulary tile) +
+// one sampling launch (one workgroup per request, the two-level inverse CDF
+// of sampler.h), and the recurrent head adds its state update per step.
 //
 // The transition rows W1[x_{k-1}] of step k > 1 sit in a contiguous [R][r]
 // buffer (A_k) written by the sampler of step k-1, so the tile kernel loads

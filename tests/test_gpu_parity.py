@@ -235,6 +235,38 @@ def test_tv_overlap_against_oracle(cid):
         assert abs(c1[i] - o) <= tol and abs(c2[i] - o) <= tol
 
 
+@pytest.mark.parametrize("V,bf16", [
+    (8, False),      # one tile narrower than itself: three of the four row chunks empty
+    (264, True),     # three tiles: the last chunk empty, its start past V
+    (1144, True),    # nine tiles, V not a multiple of 128: an empty last chunk
+    (1144, False),
+    (20000, True),   # chunks of 40 tiles, a masked last tile
+])
+def test_tv_overlap_small_vocabularies(V, bf16):
+    """dspark_tv_overlap where some row chunks hold no tile (their loads are
+    clamped to the row's last piece and their sums are empty) against the
+    oracle, with the statistics computed on the device and supplied."""
+    rng = np.random.default_rng(V + 7 * bf16)
+    n = 6
+    P = rng.normal(0.0, 3.0, (n, V)).astype(np.float32)
+    Q = (P + rng.normal(0.0, 1.5, (n, V))).astype(np.float32)
+    P[1] = Q[1]                      # p = q: overlap 1
+    if bf16:
+        P, Q = synth.to_bf16_bits(P), synth.to_bf16_bits(Q)
+    dP, dQ = dev(P), dev(Q)
+    tol = 2e-3 if bf16 else 1e-5
+
+    def stats(t):
+        z = t.double()
+        m = z.max(dim=1).values
+        return torch.stack([m, torch.exp(z - m[:, None]).sum(dim=1)], dim=1).float().contiguous()
+
+    for c in (ds.tv_overlap(dP, dQ).cpu().numpy(),
+              ds.tv_overlap(dP, dQ, p_stats=stats(dP), q_stats=stats(dQ)).cpu().numpy()):
+        for i in range(n):
+            assert abs(c[i] - oracle.overlap(P[i], Q[i])) <= tol, (V, bf16, i)
+
+
 def test_determinism_bitwise():
     inp = inputs(3)
     outs = [run_round(inp) for _ in range(3)]
