@@ -235,6 +235,33 @@ def test_tv_overlap_against_oracle(cid):
         assert abs(c1[i] - o) <= tol and abs(c2[i] - o) <= tol
 
 
+def test_tv_overlap_full_launch_sampled_rows():
+    """The standalone overlap in the launch the benchmark times: all 2048
+    (target row, draft row) pairs of the R = 128, gamma = 16, V = 151936
+    workload in one call, statistics supplied and computed on the device;
+    sampled rows (first, last, chunk-straddling middle ones) against the
+    oracle, and every value in [0, 1]."""
+    inp = inputs(3)
+    cfg = inp.cfg
+    R, gamma, V = cfg.R, cfg.gamma, cfg.V
+    n = R * gamma
+    P = inp.T.reshape(R * (gamma + 1), V)[:n]
+    Q = inp.U.reshape(n, V)
+    dP, dQ = inp.dT[:n], inp.dU.reshape(n, V)  # the same bytes, already on the device
+
+    def stats(t):
+        z = t.float()
+        m = z.max(dim=1).values
+        return torch.stack([m, torch.exp(z - m[:, None]).sum(dim=1)], dim=1).contiguous()
+
+    c = ds.tv_overlap(dP, dQ, p_stats=stats(dP), q_stats=stats(dQ)).cpu().numpy()
+    assert c.shape == (n,) and np.isfinite(c).all()
+    assert ((c >= -1e-6) & (c <= 1 + 1e-5)).all()
+    tol = prob_tol(cfg)
+    for i in (0, 1, 255, 256, 1023, 1024, 1537, n - 1):
+        assert abs(c[i] - oracle.overlap(P[i], Q[i])) <= tol, i
+
+
 @pytest.mark.parametrize("V,bf16", [
     (8, False),      # one tile narrower than itself: three of the four row chunks empty
     (264, True),     # three tiles: the last chunk empty, its start past V
