@@ -341,6 +341,7 @@ dspark_status dspark_train_losses(int R, int gamma, int V, int r, dspark_dtype d
   L.W2 = W2; L.x0 = x0; L.x = y; L.q_stats = D.q_stats; L.q_x = D.q_x;
   T.R = R; T.gamma = gamma; T.c = c; T.a_ce = a_ce; T.a_tv = a_tv; T.a_conf = a_conf;
   T.per_pos = per_pos; T.totals = totals;
+  T.req_sums = (double *)carve(ws, &off, (size_t)R * 3 * 8);
   return from_hip(launch_train(T, stream));
 }
 

@@ -104,6 +104,7 @@ struct TrainLaunch {
   double a_ce, a_tv, a_conf;
   float *per_pos;  // [3][R][gamma] or NULL
   double *totals;  // [4]
+  double *req_sums;  // [R][3]: each request's weighted (CE, L1, BCE) means
 };
 
 hipError_t launch_draft(const DraftLaunch &L, hipStream_t stream);
@@ -137,7 +138,7 @@ inline size_t train_ws_bytes(int R, int gamma, int V) {
   const size_t n = (size_t)R * gamma;
   return draft_ws_bytes(R, gamma, V) + verify_ws_bytes(R, gamma, V, R * (gamma + 1)) +
          4 * ws_align(n * 4) + ws_align(n * 8) + 3 * ws_align(((size_t)R + 1) * 4) +
-         ws_align((size_t)R * (gamma + 1) * 4);
+         ws_align((size_t)R * (gamma + 1) * 4) + ws_align((size_t)R * 3 * 8);
 }
 inline size_t overlap_ws_bytes(int n_rows, int V) {
   (void)V;

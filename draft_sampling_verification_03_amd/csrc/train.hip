@@ -12,8 +12,10 @@
 //     and step k + 1 conditions on W1[y_k];
 //  2. verification with every position admitted (ell = gamma, request rho's
 //     rows at rho (gamma + 1)): its sum min(p, q) is c*_k;
-//  3. loss_reduce_kernel: one workgroup folds the R x gamma positions in a
-//     fixed order (fp64 sums, so the totals do not depend on the schedule).
+//  3. loss_request_kernel (one wave per request: the positions' losses and
+//     the request's weighted means) and loss_fold_kernel (one workgroup
+//     folds the request means in a fixed order; fp64 sums, so the totals do
+//     not depend on the schedule).
 #include "kernels.h"
 #include "common.h"
 #include "trace.h"
@@ -33,10 +35,9 @@ struct LossParams {
   const float *c;       // [R][gamma] confidences
   double a_ce, a_tv, a_conf;
   float *per_pos;       // [3][R][gamma] or NULL
+  double *req_sums;     // [R][3]
   double *totals;       // [4]
 };
-
-constexpr int kLossWaves = 16;
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -44,43 +45,54 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// wave w takes requests w, w + 16, ...; lane k - 1 takes position k
-__global__ __launch_bounds__(kLossWaves * kWave) void loss_reduce_kernel(LossParams p) {
-  __shared__ double part[kLossWaves][3];
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+// One wave per request (lane k - 1 takes position k): the position's
+// (CE, L1, BCE) and the request's position-weighted means.
+__global__ __launch_bounds__(kBlock) void loss_request_kernel(LossParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rho = blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (rho >= p.R) return;
   const int gamma = p.gamma, k = lane + 1;
   const double wk = k <= gamma ? exp(-(double)(k - 1) / gamma) : 0.0;
   const double wsum = wave_sum_f64(wk);
-  double acc[3] = {0.0, 0.0, 0.0};
-  for (int rho = wave; rho < p.R; rho += kLossWaves) {
-    double v[3] = {0.0, 0.0, 0.0};
-    if (k <= gamma) {
-      const int64_t s = (int64_t)rho * gamma + lane;
-      const double cs = p.c_star[s], ck = p.c[s];
-      v[0] = -(double)p.logq[s];
-      v[1] = 2.0 * (1.0 - cs);
-      v[2] = -(cs * log(ck) + (1.0 - cs) * log(1.0 - ck));
-      if (p.per_pos != nullptr) {
-        const int64_t n = (int64_t)p.R * gamma;
-        p.per_pos[s] = (float)v[0];
-        p.per_pos[n + s] = (float)v[1];
-        p.per_pos[2 * n + s] = (float)v[2];
-      }
+  double v[3] = {0.0, 0.0, 0.0};
+  if (k <= gamma) {
+    const int64_t s = (int64_t)rho * gamma + lane;
+    const double cs = p.c_star[s], ck = p.c[s];
+    v[0] = -(double)p.logq[s];
+    v[1] = 2.0 * (1.0 - cs);
+    v[2] = -(cs * log(ck) + (1.0 - cs) * log(1.0 - ck));
+    if (p.per_pos != nullptr) {
+      const int64_t n = (int64_t)p.R * gamma;
+      p.per_pos[s] = (float)v[0];
+      p.per_pos[n + s] = (float)v[1];
+      p.per_pos[2 * n + s] = (float)v[2];
     }
-#pragma unroll
-    for (int i = 0; i < 3; ++i) acc[i] += wave_sum_f64(wk * v[i]) / wsum;
   }
-  if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) part[wave][i] = acc[i];
+  for (int i = 0; i < 3; ++i) {
+    const double m = wave_sum_f64(wk * v[i]) / wsum;
+    if (lane == 0) p.req_sums[(int64_t)rho * 3 + i] = m;
   }
+}
+
+// The request means folded in a fixed order: thread t sums requests t,
+// t + kBlock, ... in turn, then thread 0 the threads' sums in thread order.
+__global__ __launch_bounds__(kBlock) void loss_fold_kernel(LossParams p) {
+  __shared__ double part[kBlock][3];
+  const int t = threadIdx.x;
+  double acc[3] = {0.0, 0.0, 0.0};
+  for (int rho = t; rho < p.R; rho += kBlock)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) acc[i] += p.req_sums[(int64_t)rho * 3 + i];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) part[t][i] = acc[i];
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double t[3] = {0.0, 0.0, 0.0};
-    for (int w = 0; w < kLossWaves; ++w)
-      for (int i = 0; i < 3; ++i) t[i] += part[w][i];
-    for (int i = 0; i < 3; ++i) p.totals[i] = t[i] / p.R;
-    p.totals[3] = p.a_ce * (t[0] / p.R) + p.a_tv * (t[1] / p.R) + p.a_conf * (t[2] / p.R);
+  if (t == 0) {
+    double tot[3] = {0.0, 0.0, 0.0};
+    for (int w = 0; w < kBlock; ++w)
+      for (int i = 0; i < 3; ++i) tot[i] += part[w][i];
+    for (int i = 0; i < 3; ++i) p.totals[i] = tot[i] / p.R;
+    p.totals[3] = p.a_ce * (tot[0] / p.R) + p.a_tv * (tot[1] / p.R) + p.a_conf * (tot[2] / p.R);
   }
 }
 
@@ -94,8 +106,10 @@ hipError_t launch_train(const TrainLaunch &L, hipStream_t stream) {
   LossParams lp{};
   lp.R = L.R; lp.gamma = L.gamma; lp.logq = L.draft.logq_x; lp.c_star = L.verify.c_star;
   lp.c = L.c; lp.a_ce = L.a_ce; lp.a_tv = L.a_tv; lp.a_conf = L.a_conf;
-  lp.per_pos = L.per_pos; lp.totals = L.totals;
-  DSPARK_LAUNCH("loss_reduce", stream, loss_reduce_kernel, 1, kLossWaves * kWave, lp);
+  lp.per_pos = L.per_pos; lp.totals = L.totals; lp.req_sums = L.req_sums;
+  DSPARK_LAUNCH("loss_request", stream, loss_request_kernel, (L.R + kBlock / kWave - 1) / (kBlock / kWave),
+                kBlock, lp);
+  DSPARK_LAUNCH("loss_fold", stream, loss_fold_kernel, 1, kBlock, lp);
   return hipGetLastError();
 }
 
