@@ -367,8 +367,6 @@ __global__ __launch_bounds__(kBlock, 1) void draft_persistent_kernel(PersistPara
       }
       __syncthreads();
 
-      __syncthreads();
-
       // ---- 3. tile partials (fixed wave order) into the step's half
       uint64_t *tiles = p.tiles + (int64_t)(k & 1) * R * nT;
       for (int q = tid_k; q < (r1 - r0) * ntl; q += kBlock) {
