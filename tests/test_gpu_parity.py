@@ -90,6 +90,9 @@ def test_tiny_config_other_rounds(rnd):
     # bf16, r = 256 past five tiles per compute unit (1281 tiles): the
     # streaming draft and the streaming verify product
     dict(R=2, gamma=2, V=163968, dtype=synth.BF16, r=256, weight_sd=0.02),
+    # bf16, r = 256 past 512 requests: the per-step kernels (8-wave row
+    # groups), and the W2-stationary verify over 1040 possible rows
+    dict(R=520, gamma=2, V=2048, dtype=synth.BF16, r=256, weight_sd=0.05),
 ])
 def test_edge_shapes(over):
     cfg = synth.make_config(1, cid=50 + len(_cache), **over)
