@@ -154,6 +154,8 @@ def test_full_size_config(cid):
     (dict(R=40, gamma=7, V=20000), None),
     # five tiles per workgroup with a masked one, sampled requests
     (dict(R=33, gamma=8, V=131848), (0, 16, 32)),
+    # a temperature other than 1 (both the draft's and the verify's z / T)
+    (dict(R=36, gamma=8, V=20000, temp=0.7), None),
 ])
 def test_stationary_verify_shapes(over, reqs):
     """The W2-stationary verify product (bf16, r = 256, R gamma > 256) with
