@@ -102,7 +102,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the hot path has no collective and this build runs on a single MI355X",
+              "the hot path has no collective; it runs on a single MI355X",
               file=sys.stderr, flush=True)
         sys.exit(2)
     if args.steps < 1:
